@@ -1,0 +1,264 @@
+"""Pins of the oracle's whole forward pass (CPU only).
+
+* the float64 brute force (full-sequence, explicit causal mask) on the tiny
+  decoder in both architectures and with 8-bit weights, and on one-layer
+  slices of the real shapes with a small vocabulary;
+* closed forms: zero layers, zero-output layers;
+* the step list and steps-per-layer counts the pages print;
+* runtime invariants: bulk == token by token, reset, KV positions;
+* planted mistakes in the oracle, each of which one of these pins catches.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from brute_f64 import forward_all, rel_l2
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "step_lists.txt")
+
+
+def run_token_by_token(cfg, W, toks):
+    m = oracle.Model(cfg, W, max_ctx=max(cfg["max_ctx"], len(toks)))
+    out = np.stack([m.forward([t]) for t in toks])
+    m.close()
+    return out
+
+
+def tiny(**kw):
+    cfg = synth.config("tiny", **kw)
+    return cfg, synth.make_weights(cfg)
+
+
+@pytest.mark.parametrize("arch,wdtype", [("qwen3", "f32"), ("llama", "f32"),
+                                         ("qwen3", "f16"), ("llama", "q8")])
+def test_tiny_matches_f64_brute_force_every_step(arch, wdtype):
+    cfg, W = tiny(arch=arch, wdtype=wdtype)
+    toks = synth.make_prompt(cfg, 40)
+    cfg["max_ctx"] = 48
+    got = run_token_by_token(cfg, W, toks)
+    ref = forward_all(cfg, W, toks)
+    worst = max(rel_l2(got[s], ref[s]) for s in range(len(toks)))
+    assert worst < 2e-6, worst
+
+
+@pytest.mark.parametrize("name,vocab,n", [("qwen3_0p6b", 512, 6),
+                                          ("llama_8b", 384, 3),
+                                          ("qwen3_8b", 256, 3)])
+def test_one_layer_real_shape_matches_brute_force(name, vocab, n):
+    cfg = synth.config(name, n_layers=1, vocab=vocab, max_ctx=8)
+    W = synth.make_weights(cfg)
+    toks = synth.make_prompt(cfg, n)
+    got = run_token_by_token(cfg, W, toks)
+    ref = forward_all(cfg, W, toks)
+    for s in range(n):
+        assert rel_l2(got[s], ref[s]) < 2e-6
+
+
+def test_one_layer_q8_real_shape_matches_brute_force():
+    cfg = synth.config("llama_8b_q8", n_layers=1, vocab=256, max_ctx=4,
+                       d_model=1024, ffn_dim=2048, n_heads=8, n_kv_heads=2)
+    W = synth.make_weights(cfg)
+    toks = synth.make_prompt(cfg, 3)
+    got = run_token_by_token(cfg, W, toks)
+    ref = forward_all(cfg, W, toks)
+    for s in range(3):
+        assert rel_l2(got[s], ref[s]) < 2e-6
+
+
+def test_zero_layers_closed_form_tied():
+    # x = e_t, y = x * r with unit norm weight, logit_t = r * |e_t|^2.
+    cfg, W = tiny(n_layers=0)
+    W["output_norm.weight"] = np.ones_like(W["output_norm.weight"])
+    m = oracle.Model(cfg, W)
+    E = W["token_embd.weight"].astype(np.float64)
+    for t in (0, 5, 255):
+        m.reset()
+        lg = m.forward([t])
+        r = 1.0 / np.sqrt(np.mean(E[t] ** 2) + cfg["rms_eps"])
+        assert lg[t] == pytest.approx(r * np.sum(E[t] ** 2), rel=1e-6)
+        assert np.allclose(lg, E @ (E[t] * r), rtol=1e-5, atol=1e-6)
+
+
+def test_zero_output_layers_reduce_to_zero_layers_bitwise():
+    cfg, W = tiny()
+    for i in range(cfg["n_layers"]):
+        for s in ("attn_output", "ffn_down"):
+            W[f"blk.{i}.{s}.weight"] = np.zeros_like(W[f"blk.{i}.{s}.weight"])
+    toks = synth.make_prompt(cfg, 6)
+    a = run_token_by_token(cfg, W, toks)
+    cfg0 = dict(cfg, n_layers=0)
+    b = run_token_by_token(cfg0, W, toks)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def golden_lists():
+    ops, steps = {}, {}
+    for line in open(GOLDEN):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        key, rest = line.split(":", 1)
+        if key == "steps_per_layer":
+            arch, n = rest.split()
+            steps[arch] = int(n)
+        else:
+            ops[key] = rest.split()
+    return ops, steps
+
+
+@pytest.mark.parametrize("arch", ["qwen3", "llama"])
+def test_step_list_matches_the_printed_definition(arch):
+    gold, steps = golden_lists()
+    cfg, W = tiny(arch=arch)
+    m = oracle.Model(cfg, W)
+    m.forward(synth.make_prompt(cfg, 2))
+    sections = m.trace().split("|")
+    assert len(sections) - 2 == cfg["n_layers"]
+    assert sections[0].split(",") == gold[f"{arch} prologue"]
+    for blk in sections[1:-1]:
+        assert blk.split(",") == gold[f"{arch} block"]
+        assert len(blk.split(",")) == steps[arch]
+    assert sections[-1].split(",") == gold[f"{arch} epilogue"]
+
+
+def test_norm_heads_before_rope_matters():
+    # The qwen3 definition puts norm_heads before rope; the other order is
+    # a different model (page "Local inference and architectures", "The
+    # format"). The planted swap must move the logits.
+    cfg, W = tiny()
+    toks = synth.make_prompt(cfg, 8)
+    good = run_token_by_token(cfg, W, toks)
+    oracle.set_mutation("norm_after_rope")
+    try:
+        bad = run_token_by_token(cfg, W, toks)
+    finally:
+        oracle.set_mutation("none")
+    # at position 0 RoPE is the identity, so only later steps can differ
+    assert np.array_equal(good[0], bad[0])
+    assert max(rel_l2(bad[s], good[s]) for s in range(1, 8)) > 1e-4
+
+
+def test_bulk_equals_token_by_token_bitwise():
+    cfg, W = tiny()
+    toks = synth.make_prompt(cfg, 20)
+    a = oracle.Model(cfg, W)
+    la = a.forward(toks[:13])
+    lb_model = oracle.Model(cfg, W)
+    for t in toks[:12]:
+        lb_model.forward([t], logits=False)
+    lb = lb_model.forward([toks[12]])
+    assert np.array_equal(la.view(np.uint32), lb.view(np.uint32))
+    for layer in range(cfg["n_layers"]):
+        for which in (0, 1):
+            assert np.array_equal(a.kv_read(layer, which, 0, 13),
+                                  lb_model.kv_read(layer, which, 0, 13))
+    # and continuing after a bulk call uses absolute positions
+    assert np.array_equal(a.forward(toks[13:20]), lb_model.forward(toks[13:20]))
+
+
+def test_reset_rerun_is_bitwise_identical_and_thread_count_free():
+    cfg, W = tiny()
+    toks = synth.make_prompt(cfg, 10)
+    m = oracle.Model(cfg, W)
+    a = m.forward(toks)
+    m.reset()
+    assert m.kv_len == 0
+    b = m.forward(toks)
+    assert np.array_equal(a, b)
+    n0 = oracle.threads()
+    oracle.set_threads(1)
+    try:
+        m.reset()
+        c = m.forward(toks)
+    finally:
+        oracle.set_threads(n0)
+    assert np.array_equal(a, c)
+
+
+def test_kv_rows_and_positions():
+    cfg, W = tiny(arch="llama")
+    toks = synth.make_prompt(cfg, 5)
+    m = oracle.Model(cfg, W)
+    m.forward(toks)
+    assert m.kv_len == 5
+    # layer 0, position 0: k = W_k rmsnorm(embed(t0)), RoPE at 0 is identity
+    x = oracle.embed(W["token_embd.weight"], int(toks[0]))
+    h = oracle.rmsnorm(x, W["blk.0.attn_norm.weight"], cfg["rms_eps"])
+    k = oracle.matvec(W["blk.0.attn_k.weight"], h)
+    v = oracle.matvec(W["blk.0.attn_v.weight"], h)
+    hd = cfg["head_dim"]
+    assert np.array_equal(m.kv_read(0, 0, 0, 1).reshape(-1), k)
+    assert np.array_equal(m.kv_read(0, 1, 0, 1).reshape(-1), v)
+    # layer 0, position 3: that token's k rotated by RoPE at position 3
+    c, s = oracle.rope_table(8, hd, cfg["rope_theta"])
+    x3 = oracle.embed(W["token_embd.weight"], int(toks[3]))
+    h3 = oracle.rmsnorm(x3, W["blk.0.attn_norm.weight"], cfg["rms_eps"])
+    k3 = oracle.rope(oracle.matvec(W["blk.0.attn_k.weight"], h3), hd, c[3], s[3])
+    assert np.array_equal(m.kv_read(0, 0, 3, 1).reshape(-1), k3)
+    with pytest.raises(RuntimeError):
+        m.forward(np.zeros(cfg["max_ctx"], np.int32))
+    assert m.kv_len == 5
+    with pytest.raises(RuntimeError):
+        m.forward([cfg["vocab"]])
+
+
+# ---- planted mistakes -----------------------------------------------------
+
+def _brute_tiny_fails(arch):
+    cfg, W = tiny(arch=arch)
+    toks = synth.make_prompt(cfg, 12)
+    got = run_token_by_token(cfg, W, toks)
+    ref = forward_all(cfg, W, toks)
+    worst = max(rel_l2(got[s], ref[s]) for s in range(len(toks)))
+    return not worst <= 1e-4  # NaN counts as caught
+
+
+def _rmsnorm_closed_form_fails():
+    x = np.full(64, 1e-3, np.float32)
+    got = oracle.rmsnorm(x, np.ones(64, np.float32), 1e-6)
+    ref = 1e-3 / np.sqrt(1e-6 + 1e-6)
+    return abs(float(got[0]) - ref) > 1e-5
+
+
+def _one_hot_fails():
+    W = (0.02 * np.random.default_rng(1).standard_normal((8, 8))).astype(np.float32)
+    h = np.zeros(8, np.float32)
+    h[3] = 1.0
+    return not np.array_equal(oracle.matvec(W, h), W[:, 3])
+
+
+def _kv_row_fails():
+    # K cached at position 0 of layer 0 is the unrotated k of token 0 (RoPE
+    # at position 0 is the identity). A constant position offset leaves the
+    # logits unchanged (scores depend only on m - n) but not the cache.
+    cfg, W = tiny(arch="llama")
+    toks = synth.make_prompt(cfg, 2)
+    m = oracle.Model(cfg, W)
+    m.forward(toks)
+    x = oracle.embed(W["token_embd.weight"], int(toks[0]))
+    h = oracle.rmsnorm(x, W["blk.0.attn_norm.weight"], cfg["rms_eps"])
+    k = oracle.matvec(W["blk.0.attn_k.weight"], h)
+    return not np.array_equal(m.kv_read(0, 0, 0, 1).reshape(-1), k)
+
+
+@pytest.mark.parametrize("mutation", [m for m in oracle.MUTATIONS if m != "none"])
+def test_each_planted_mistake_is_caught(mutation):
+    oracle.set_mutation(mutation)
+    try:
+        caught = (_rmsnorm_closed_form_fails() or _one_hot_fails()
+                  or _kv_row_fails()
+                  or _brute_tiny_fails("qwen3") or _brute_tiny_fails("llama"))
+    finally:
+        oracle.set_mutation("none")
+    assert caught, mutation
+
+
+def test_pins_pass_without_mistakes():
+    assert not _rmsnorm_closed_form_fails()
+    assert not _one_hot_fails()
+    assert not _kv_row_fails()
+    assert not _brute_tiny_fails("qwen3")
+    assert not _brute_tiny_fails("llama")
