@@ -1,0 +1,101 @@
+// kernels.h — launchers of the gfx950 kernels, used by the runtime (host
+// C++). Internal to the library; the public surface is include/decfwd.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace dfk {
+
+enum WType { W_F32 = 0, W_F16 = 1, W_Q8 = 2 };
+
+// A device matrix [rows][cols] (y = W h). f32 / f16: `data` holds the
+// values row-major. Q8: `data` holds the int8 values row-major and `scales`
+// the f16 scale of every 32-value block, [rows][cols / 32].
+struct Weight {
+    int dtype = W_F16;
+    const void* data = nullptr;
+    const uint16_t* scales = nullptr;
+    int64_t rows = 0, cols = 0;
+};
+
+// Epilogues of the decode matvec.
+//   MV_STORE : out[n]  = r * (W (x . w))[n]
+//   MV_RESID : out[n] += r * (W (x . w))[n]            (residual add)
+//   MV_SWIGLU: out[f]  = silu(r (W (x . w))[f]) * r (W (x . w))[f + up_rows]
+// where (x . w) is x times the norm weight and r = 1/sqrt(mean(x^2) + eps)
+// when a norm weight is given, else x and r = 1.
+enum MatvecMode { MV_STORE = 0, MV_RESID = 1, MV_SWIGLU = 2 };
+
+// Device-side decode state: the position and the token of the step being
+// computed, so that a captured step needs no per-step arguments.
+struct DevState {
+    int pos;        // position of the token being decoded
+    int tok;        // its id
+    int step;       // index of the next generated token
+    int argmax_count;
+    float part_val[256];
+    int part_idx[256];
+};
+
+// Decode attention: rows per tile, most work-groups per KV head (the
+// partition of tiles over work-groups depends only on the position), and
+// query heads per KV head (1, 2, 4 or 8).
+constexpr int ATTN_T = 64;
+constexpr int ATTN_MAX_SPLIT = 128;
+constexpr int ATTN_MAX_GROUP = 8;
+
+// Work-groups per KV head that decode attention uses at position p.
+inline int attn_splits(int p)
+{
+    const int tiles = (p + 1 + ATTN_T - 1) / ATTN_T;
+    const int tpw = (tiles + ATTN_MAX_SPLIT - 1) / ATTN_MAX_SPLIT;
+    return (tiles + tpw - 1) / tpw;
+}
+
+hipError_t launch_matvec(const Weight& W, int mode, const float* x,
+                         const float* norm_w, float eps, int64_t n_out,
+                         int64_t up_rows, float* out, hipStream_t s);
+
+hipError_t launch_embed(const Weight& E, const int* tokens_dev,
+                        const int* state_tok, int n_rows, float* x,
+                        hipStream_t s);
+
+struct AttnDecodeArgs {
+    const float* qkv;          // [n_heads*hd | n_kv*hd | n_kv*hd]
+    const float* q_norm;       // [hd] or null (llama)
+    const float* k_norm;
+    float eps;
+    const float* cos_t;        // [max_ctx][hd/2]
+    const float* sin_t;
+    float* kc;                 // this layer's K cache [n_kv][max_ctx][hd]
+    float* vc;
+    int max_ctx, n_heads, n_kv, head_dim;
+    const int* state_pos;      // device int: position p
+    float* part;               // [n_kv][ATTN_MAX_SPLIT][group][hd + 2]
+    float* out;                // [n_heads][hd]
+    int grid_splits;           // work-groups launched per KV head (>= in use)
+};
+hipError_t launch_attn_decode(const AttnDecodeArgs& a, hipStream_t s);
+// Merge of the split partials into `out` (no-op when one split covers p).
+hipError_t launch_attn_combine(const AttnDecodeArgs& a, hipStream_t s);
+
+// argmax over n values, lowest index on ties, NaN never wins. Writes the id
+// to *out_dev. When `advance` is set it also stores the id as the next token
+// of the state, appends it to gen_out[state->step] and advances pos / step.
+hipError_t launch_argmax(const float* v, int n, DevState* st, int* out_dev,
+                         int advance, int* gen_out, hipStream_t s);
+
+hipError_t launch_set_state(DevState* st, int pos, int tok, int step,
+                            hipStream_t s);
+
+// Upload helpers.
+hipError_t launch_to_f32(const void* src, int src_dtype, int64_t n, float* dst,
+                         hipStream_t s);
+// Split host-format 8-bit blocks (34 bytes: f16 scale, 32 int8) of a
+// [rows][cols] matrix into a value plane and a scale plane.
+hipError_t launch_q8_split(const uint8_t* blocks, int64_t rows, int64_t cols,
+                           int8_t* values, uint16_t* scales, hipStream_t s);
+
+}  // namespace dfk

@@ -1,0 +1,1077 @@
+// runtime.hip — host side of the library: the C ABI of include/decfwd.h.
+//
+// Load follows page "Execution contract", section "Load phase": validate
+// the config and the tensor table, upload the weights, precompute the RoPE
+// cos/sin cache. Memory follows section "Memory lifecycle": weights live as
+// long as the model; one KV cache sized to max context, appended on every
+// step and cleared by reset; activations come from a frame allocator with
+// exact-size buckets that is reset at the start of every forward. Errors are
+// structured codes with a message naming the tensor / field / bytes (section
+// "Error semantics"); a failed call never aborts and never falls back.
+#include "kernels.h"
+
+#include "../../include/decfwd.h"
+
+#include <atomic>
+#include <chrono>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <utility>
+#include <vector>
+
+using namespace dfk;
+
+namespace {
+
+thread_local std::string g_load_error;
+
+std::string fmt(const char* f, ...)
+{
+    char buf[1024];
+    va_list ap;
+    va_start(ap, f);
+    vsnprintf(buf, sizeof buf, f, ap);
+    va_end(ap);
+    return buf;
+}
+
+struct Fail {
+    df_status code;
+    std::string msg;
+};
+
+// ---------------------------------------------------------------------------
+// Frame allocator (page "Execution contract", "Memory lifecycle",
+// "Activations"): buffers bucketed by (exact byte size, usage); reset()
+// makes every buffer of the previous forward available again. Within a
+// bucket buffers are handed out in a fixed order from a cursor, so a forward
+// that makes the same requests gets the same addresses every time.
+// ---------------------------------------------------------------------------
+enum Usage { USAGE_DEVICE = 0 };
+
+class FramePool {
+public:
+    void* alloc(size_t bytes, int usage, Fail* err)
+    {
+        auto key = std::make_pair(bytes, usage);
+        auto& bucket = pool_[key];
+        size_t& cur = cursor_[key];
+        if (cur == bucket.size()) {
+            void* p = nullptr;
+            if (hipMalloc(&p, bytes ? bytes : 1) != hipSuccess) {
+                (void)hipGetLastError();
+                *err = {DF_ERR_OUT_OF_MEMORY,
+                        fmt("frame allocator: hipMalloc of %zu bytes failed", bytes)};
+                return nullptr;
+            }
+            bucket.push_back(p);
+            total_ += bytes;
+        }
+        return bucket[cur++];
+    }
+    void reset()
+    {
+        for (auto& kv : cursor_) kv.second = 0;
+    }
+    void release()
+    {
+        for (auto& kv : pool_)
+            for (void* p : kv.second) (void)hipFree(p);
+        pool_.clear();
+        cursor_.clear();
+        total_ = 0;
+    }
+    size_t bytes() const { return total_; }
+
+private:
+    std::map<std::pair<size_t, int>, std::vector<void*>> pool_;
+    std::map<std::pair<size_t, int>, size_t> cursor_;
+    size_t total_ = 0;
+};
+
+struct Layer {
+    Weight wqkv, wo, wgu, wd;  // [q;k;v], o, [gate;up], down
+    float* attn_norm = nullptr;
+    float* ffn_norm = nullptr;
+    float* q_norm = nullptr;
+    float* k_norm = nullptr;
+};
+
+}  // namespace
+
+struct df_model {
+    df_config cfg{};
+    int device = 0;
+    hipStream_t stream = nullptr;
+    bool own_stream = false;
+    std::string err;
+    std::atomic<int> busy{0};
+    int32_t kv_len = 0;
+
+    std::vector<void*> allocs;  // every long-lived device allocation
+    int64_t weight_bytes = 0, kv_bytes = 0;
+
+    Weight embd, out;
+    float* out_norm = nullptr;
+    std::vector<Layer> layers;
+    float* kc = nullptr;  // [L][n_kv][max_ctx][hd]
+    float* vc = nullptr;
+    float* cos_t = nullptr;  // [max_ctx][hd/2]
+    float* sin_t = nullptr;
+    DevState* state = nullptr;
+    float* attn_part = nullptr;
+    int* argmax_out = nullptr;
+    int* gen_tokens = nullptr;  // [max_ctx]
+
+    FramePool pool;
+
+    // Captured decode step (+ argmax) for df_generate, replayed once per
+    // token; valid while its buffers are the ones the pool hands out.
+    hipGraphExec_t gen_exec = nullptr;
+    std::vector<void*> gen_key;
+
+    // df_profile: event pairs around the launches of one kernel class.
+    int prof_kernel = -1;
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> prof_events;
+    size_t prof_used = 0;
+    int64_t prof_launches = 0;
+    double prof_ms = 0;
+
+    double load_ms = 0;
+    hipEvent_t ev0 = nullptr, ev1 = nullptr;
+    int ev_kind = 0;  // 0 none, 1 step, 2 prefill
+    double last_prefill_ms = 0, last_step_ms = 0;
+    int64_t n_forward = 0;
+};
+
+namespace {
+
+void* dev_alloc(df_model* m, size_t bytes, const char* what, Fail* err)
+{
+    void* p = nullptr;
+    if (hipMalloc(&p, bytes ? bytes : 1) != hipSuccess) {
+        (void)hipGetLastError();
+        *err = {DF_ERR_OUT_OF_MEMORY,
+                fmt("hipMalloc of %zu bytes for %s failed", bytes, what)};
+        return nullptr;
+    }
+    m->allocs.push_back(p);
+    return p;
+}
+
+void release(df_model* m)
+{
+    if (!m) return;
+    if (m->stream) (void)hipStreamSynchronize(m->stream);
+    for (void* p : m->allocs) (void)hipFree(p);
+    m->allocs.clear();
+    for (auto& ev : m->prof_events) {
+        (void)hipEventDestroy(ev.first);
+        (void)hipEventDestroy(ev.second);
+    }
+    m->prof_events.clear();
+    if (m->gen_exec) (void)hipGraphExecDestroy(m->gen_exec);
+    m->gen_exec = nullptr;
+    m->pool.release();
+    if (m->ev0) (void)hipEventDestroy(m->ev0);
+    if (m->ev1) (void)hipEventDestroy(m->ev1);
+    if (m->own_stream && m->stream) (void)hipStreamDestroy(m->stream);
+    m->stream = nullptr;
+}
+
+// ---------------------------------------------------------------------------
+// Validation (page "Execution contract", "Load phase", step 3: config schema
+// and tensor completeness). Host only: runs before any HIP call.
+// ---------------------------------------------------------------------------
+bool cfg_fail(Fail* e, const char* field, const std::string& reason)
+{
+    *e = {DF_ERR_INVALID_CONFIG, fmt("invalid config: %s %s", field, reason.c_str())};
+    return false;
+}
+
+bool validate_config(const df_config* c, Fail* e)
+{
+    if (!c) { *e = {DF_ERR_INVALID_ARGUMENT, "config is NULL"}; return false; }
+    if (c->arch != DF_ARCH_LLAMA && c->arch != DF_ARCH_QWEN3)
+        return cfg_fail(e, "arch", fmt("= %d: expected 0 (llama) or 1 (qwen3)", c->arch));
+    if (c->n_layers < 0 || c->n_layers > 4096)
+        return cfg_fail(e, "n_layers", fmt("= %d: expected 0..4096", c->n_layers));
+    if (c->d_model <= 0 || c->d_model % 32 || c->d_model > 16384)
+        return cfg_fail(e, "d_model", fmt("= %d: expected a multiple of 32 in 32..16384", c->d_model));
+    if (c->head_dim != 16 && c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128)
+        return cfg_fail(e, "head_dim", fmt("= %d: expected 16, 32, 64 or 128", c->head_dim));
+    if (c->n_kv_heads <= 0 || c->n_heads <= 0 || c->n_heads % c->n_kv_heads)
+        return cfg_fail(e, "n_heads", fmt("= %d with n_kv_heads = %d: n_kv_heads must divide n_heads",
+                                          c->n_heads, c->n_kv_heads));
+    {
+        const int G = c->n_heads / c->n_kv_heads;
+        if (G != 1 && G != 2 && G != 4 && G != 8)
+            return cfg_fail(e, "n_heads", fmt("/ n_kv_heads = %d: expected 1, 2, 4 or 8 query heads "
+                                              "per KV head", G));
+    }
+    if (int64_t(c->n_heads) * c->head_dim > 16384 || (c->n_heads * c->head_dim) % 32)
+        return cfg_fail(e, "n_heads", fmt("* head_dim = %lld: expected a multiple of 32 up to 16384",
+                                          (long long)c->n_heads * c->head_dim));
+    if (c->ffn_dim <= 0 || c->ffn_dim % 32 || c->ffn_dim > 16384)
+        return cfg_fail(e, "ffn_dim", fmt("= %d: expected a multiple of 32 in 32..16384", c->ffn_dim));
+    if (c->vocab <= 0)
+        return cfg_fail(e, "vocab", fmt("= %d: expected >= 1", c->vocab));
+    if (c->max_ctx <= 0 || c->max_ctx > (1 << 20))
+        return cfg_fail(e, "max_ctx", fmt("= %d: expected 1..1048576", c->max_ctx));
+    if (!(c->rope_theta > 0) || !std::isfinite(c->rope_theta))
+        return cfg_fail(e, "rope_theta", fmt("= %g: expected a finite value > 0", c->rope_theta));
+    if (!(c->rms_eps >= 0) || !std::isfinite(c->rms_eps))
+        return cfg_fail(e, "rms_eps", fmt("= %g: expected a finite value >= 0", c->rms_eps));
+    return true;
+}
+
+const char* dtype_name(int d)
+{
+    return d == DF_F32 ? "f32" : d == DF_F16 ? "f16" : d == DF_Q8_32 ? "q8_32" : "unknown";
+}
+
+uint64_t expected_bytes(int dtype, int64_t rows, int64_t cols)
+{
+    if (dtype == DF_F32) return uint64_t(rows * cols) * 4;
+    if (dtype == DF_F16) return uint64_t(rows * cols) * 2;
+    return uint64_t(rows) * uint64_t(cols / 32) * 34;
+}
+
+enum Kind { K_EMBED, K_NORM, K_MATMUL };
+
+struct Need {
+    std::string name;
+    Kind kind;
+    int64_t rows, cols;
+    bool required;
+    std::string required_by;
+};
+
+std::vector<Need> required_tensors(const df_config* c)
+{
+    const int64_t d = c->d_model, hd = c->head_dim, F = c->ffn_dim, V = c->vocab;
+    const int64_t qd = int64_t(c->n_heads) * hd, kvd = int64_t(c->n_kv_heads) * hd;
+    std::vector<Need> v;
+    v.push_back({"token_embd.weight", K_EMBED, V, d, true, "embed"});
+    for (int i = 0; i < c->n_layers; ++i) {
+        const std::string b = "blk." + std::to_string(i) + ".";
+        const std::string L = "layer " + std::to_string(i);
+        v.push_back({b + "attn_norm.weight", K_NORM, 1, d, true, L + " rms_norm (attention)"});
+        v.push_back({b + "attn_q.weight", K_MATMUL, qd, d, true, L + " q matmul"});
+        v.push_back({b + "attn_k.weight", K_MATMUL, kvd, d, true, L + " k matmul"});
+        v.push_back({b + "attn_v.weight", K_MATMUL, kvd, d, true, L + " v matmul"});
+        if (c->arch == DF_ARCH_QWEN3) {
+            v.push_back({b + "attn_q_norm.weight", K_NORM, 1, hd, true, L + " norm_heads q"});
+            v.push_back({b + "attn_k_norm.weight", K_NORM, 1, hd, true, L + " norm_heads k"});
+        }
+        v.push_back({b + "attn_output.weight", K_MATMUL, d, qd, true, L + " o matmul"});
+        v.push_back({b + "ffn_norm.weight", K_NORM, 1, d, true, L + " rms_norm (ffn)"});
+        v.push_back({b + "ffn_gate.weight", K_MATMUL, F, d, true, L + " gate matmul"});
+        v.push_back({b + "ffn_up.weight", K_MATMUL, F, d, true, L + " up matmul"});
+        v.push_back({b + "ffn_down.weight", K_MATMUL, d, F, true, L + " down matmul"});
+    }
+    v.push_back({"output_norm.weight", K_NORM, 1, d, true, "final rms_norm"});
+    v.push_back({"output.weight", K_MATMUL, V, d, false, "logits matmul"});
+    return v;
+}
+
+bool validate_tensors(const df_config* c, const df_tensor* t, size_t n,
+                      std::map<std::string, const df_tensor*>* found, Fail* e)
+{
+    if (n && !t) { *e = {DF_ERR_INVALID_ARGUMENT, "tensor table is NULL"}; return false; }
+    const auto need = required_tensors(c);
+    std::map<std::string, const Need*> by_name;
+    for (const auto& nd : need) by_name[nd.name] = &nd;
+    for (size_t i = 0; i < n; ++i) {
+        if (!t[i].name) {
+            *e = {DF_ERR_INVALID_ARGUMENT, fmt("tensor %zu has no name", i)};
+            return false;
+        }
+        const std::string name = t[i].name;
+        auto it = by_name.find(name);
+        if (it == by_name.end()) {
+            *e = {DF_ERR_INVALID_ARGUMENT,
+                  fmt("tensor '%s' is not part of the %s step list with %d layers", name.c_str(),
+                      c->arch == DF_ARCH_QWEN3 ? "qwen3" : "llama", c->n_layers)};
+            return false;
+        }
+        if (found->count(name)) {
+            *e = {DF_ERR_INVALID_ARGUMENT, fmt("tensor '%s' given twice", name.c_str())};
+            return false;
+        }
+        const Need& nd = *it->second;
+        const df_tensor& x = t[i];
+        if (x.dtype != DF_F32 && x.dtype != DF_F16 && x.dtype != DF_Q8_32) {
+            *e = {DF_ERR_UNSUPPORTED_OP, fmt("tensor '%s': dtype code %d is not f32, f16 or q8_32",
+                                             name.c_str(), x.dtype)};
+            return false;
+        }
+        if (nd.kind != K_MATMUL && x.dtype == DF_Q8_32) {
+            *e = {DF_ERR_UNSUPPORTED_OP,
+                  fmt("tensor '%s' (%s): q8_32 is supported for matmul weights only; "
+                      "embeddings and norm weights are f32 or f16",
+                      name.c_str(), nd.required_by.c_str())};
+            return false;
+        }
+        if (x.rows != nd.rows || x.cols != nd.cols) {
+            *e = {DF_ERR_SHAPE_MISMATCH,
+                  fmt("tensor '%s' (%s): expected shape [%lld, %lld], got [%lld, %lld]",
+                      name.c_str(), nd.required_by.c_str(), (long long)nd.rows,
+                      (long long)nd.cols, (long long)x.rows, (long long)x.cols)};
+            return false;
+        }
+        if (x.dtype == DF_Q8_32 && x.cols % 32) {
+            *e = {DF_ERR_SHAPE_MISMATCH, fmt("tensor '%s': q8_32 needs cols divisible by 32, got %lld",
+                                             name.c_str(), (long long)x.cols)};
+            return false;
+        }
+        const uint64_t want = expected_bytes(x.dtype, x.rows, x.cols);
+        if (x.nbytes != want) {
+            *e = {DF_ERR_WEIGHT_FORMAT_MISMATCH,
+                  fmt("tensor '%s': declared %s [%lld, %lld] needs %llu bytes, got %llu",
+                      name.c_str(), dtype_name(x.dtype), (long long)x.rows, (long long)x.cols,
+                      (unsigned long long)want, (unsigned long long)x.nbytes)};
+            return false;
+        }
+        if (!x.data) {
+            *e = {DF_ERR_INVALID_ARGUMENT, fmt("tensor '%s': data is NULL", name.c_str())};
+            return false;
+        }
+        (*found)[name] = &x;
+    }
+    for (const auto& nd : need) {
+        if (nd.required && !found->count(nd.name)) {
+            *e = {DF_ERR_MISSING_TENSOR, fmt("missing tensor '%s', required by %s",
+                                             nd.name.c_str(), nd.required_by.c_str())};
+            return false;
+        }
+    }
+    // Fused launches need matching dtypes: q/k/v, gate/up, and one dtype for
+    // every block matmul so that all layers run the same kernels.
+    int block_dtype = -1;
+    for (const auto& nd : need) {
+        if (nd.kind != K_MATMUL || nd.name == "output.weight") continue;
+        const int dt = (*found)[nd.name]->dtype;
+        if (block_dtype < 0) block_dtype = dt;
+        if (dt != block_dtype) {
+            *e = {DF_ERR_WEIGHT_FORMAT_MISMATCH,
+                  fmt("tensor '%s' is %s but the other block matmul weights are %s; "
+                      "one dtype is required for all of them",
+                      nd.name.c_str(), dtype_name(dt), dtype_name(block_dtype))};
+            return false;
+        }
+    }
+    return true;
+}
+
+// ---------------------------------------------------------------------------
+// Upload.
+// ---------------------------------------------------------------------------
+bool check(hipError_t r, const char* what, Fail* e, df_status code = DF_ERR_BACKEND_INIT)
+{
+    if (r == hipSuccess) return true;
+    (void)hipGetLastError();
+    *e = {code, fmt("%s: %s", what, hipGetErrorString(r))};
+    return false;
+}
+
+hipMemcpyKind kind_of(const df_tensor* t)
+{
+    return t->on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice;
+}
+
+// Concatenate matmul weights along rows into one device matrix.
+bool upload_matrix(df_model* m, const std::vector<const df_tensor*>& parts,
+                   Weight* w, const char* what, Fail* e)
+{
+    const int dt = parts[0]->dtype;
+    const int64_t cols = parts[0]->cols;
+    int64_t rows = 0;
+    for (auto* p : parts) rows += p->rows;
+    w->rows = rows;
+    w->cols = cols;
+    if (dt == DF_F32 || dt == DF_F16) {
+        const size_t es = dt == DF_F32 ? 4 : 2;
+        char* dst = static_cast<char*>(dev_alloc(m, size_t(rows * cols) * es, what, e));
+        if (!dst) return false;
+        size_t off = 0;
+        for (auto* p : parts) {
+            if (!check(hipMemcpyAsync(dst + off, p->data, p->nbytes, kind_of(p), m->stream),
+                       what, e))
+                return false;
+            off += p->nbytes;
+        }
+        w->dtype = dt == DF_F32 ? W_F32 : W_F16;
+        w->data = dst;
+        w->scales = nullptr;
+        m->weight_bytes += int64_t(rows * cols * es);
+        return true;
+    }
+    // 8-bit blocks: value plane [rows][cols] and scale plane [rows][cols/32].
+    int8_t* vals = static_cast<int8_t*>(dev_alloc(m, size_t(rows * cols), what, e));
+    if (!vals) return false;
+    uint16_t* sc = static_cast<uint16_t*>(dev_alloc(m, size_t(rows * (cols / 32)) * 2, what, e));
+    if (!sc) return false;
+    int64_t row0 = 0;
+    for (auto* p : parts) {
+        const uint8_t* src = static_cast<const uint8_t*>(p->data);
+        void* staging = nullptr;
+        if (!p->on_device) {
+            if (!check(hipMalloc(&staging, p->nbytes), "staging for 8-bit repack", e,
+                       DF_ERR_OUT_OF_MEMORY))
+                return false;
+            if (!check(hipMemcpyAsync(staging, p->data, p->nbytes, hipMemcpyHostToDevice,
+                                      m->stream), what, e)) {
+                (void)hipFree(staging);
+                return false;
+            }
+            src = static_cast<const uint8_t*>(staging);
+        }
+        hipError_t r = launch_q8_split(src, p->rows, cols, vals + row0 * cols,
+                                       sc + row0 * (cols / 32), m->stream);
+        if (staging) {
+            (void)hipStreamSynchronize(m->stream);
+            (void)hipFree(staging);
+        }
+        if (!check(r, "8-bit repack", e)) return false;
+        row0 += p->rows;
+    }
+    w->dtype = W_Q8;
+    w->data = vals;
+    w->scales = sc;
+    m->weight_bytes += int64_t(rows * cols + rows * (cols / 32) * 2);
+    return true;
+}
+
+bool upload_norm(df_model* m, const df_tensor* t, float** out, Fail* e)
+{
+    const int64_t n = t->rows * t->cols;
+    float* dst = static_cast<float*>(dev_alloc(m, size_t(n) * 4, t->name, e));
+    if (!dst) return false;
+    const void* src = t->data;
+    void* staging = nullptr;
+    if (!t->on_device) {
+        if (!check(hipMalloc(&staging, t->nbytes), "staging", e, DF_ERR_OUT_OF_MEMORY)) return false;
+        if (!check(hipMemcpyAsync(staging, t->data, t->nbytes, hipMemcpyHostToDevice, m->stream),
+                   t->name, e)) {
+            (void)hipFree(staging);
+            return false;
+        }
+        src = staging;
+    }
+    hipError_t r = launch_to_f32(src, t->dtype == DF_F32 ? W_F32 : W_F16, n, dst, m->stream);
+    if (staging) {
+        (void)hipStreamSynchronize(m->stream);
+        (void)hipFree(staging);
+    }
+    if (!check(r, t->name, e)) return false;
+    *out = dst;
+    m->weight_bytes += n * 4;
+    return true;
+}
+
+bool upload_embedding(df_model* m, const df_tensor* t, Weight* w, Fail* e)
+{
+    std::vector<const df_tensor*> parts{t};
+    return upload_matrix(m, parts, w, t->name, e);
+}
+
+bool build_model(df_model* m, const std::map<std::string, const df_tensor*>& T, Fail* e)
+{
+    const df_config& c = m->cfg;
+    auto get = [&](const std::string& n) { return T.at(n); };
+    if (!upload_embedding(m, get("token_embd.weight"), &m->embd, e)) return false;
+    m->layers.resize(size_t(c.n_layers));
+    for (int i = 0; i < c.n_layers; ++i) {
+        const std::string b = "blk." + std::to_string(i) + ".";
+        Layer& L = m->layers[size_t(i)];
+        if (!upload_norm(m, get(b + "attn_norm.weight"), &L.attn_norm, e)) return false;
+        if (!upload_matrix(m, {get(b + "attn_q.weight"), get(b + "attn_k.weight"),
+                               get(b + "attn_v.weight")}, &L.wqkv, "q/k/v weights", e))
+            return false;
+        if (c.arch == DF_ARCH_QWEN3) {
+            if (!upload_norm(m, get(b + "attn_q_norm.weight"), &L.q_norm, e)) return false;
+            if (!upload_norm(m, get(b + "attn_k_norm.weight"), &L.k_norm, e)) return false;
+        }
+        if (!upload_matrix(m, {get(b + "attn_output.weight")}, &L.wo, "o weight", e)) return false;
+        if (!upload_norm(m, get(b + "ffn_norm.weight"), &L.ffn_norm, e)) return false;
+        if (!upload_matrix(m, {get(b + "ffn_gate.weight"), get(b + "ffn_up.weight")}, &L.wgu,
+                           "gate/up weights", e))
+            return false;
+        if (!upload_matrix(m, {get(b + "ffn_down.weight")}, &L.wd, "down weight", e)) return false;
+    }
+    if (!upload_norm(m, get("output_norm.weight"), &m->out_norm, e)) return false;
+    // "output.weight | token_embd.weight" (page "Local inference and
+    // architectures", "Rules": this tensor, or that one if it is absent).
+    auto it = T.find("output.weight");
+    if (it != T.end()) {
+        if (!upload_matrix(m, {it->second}, &m->out, "output weight", e)) return false;
+    } else {
+        m->out = m->embd;
+    }
+
+    // KV cache sized to max context (section "Memory lifecycle", "KV cache").
+    const int64_t hd = c.head_dim;
+    const size_t kv_elems = size_t(c.n_layers) * size_t(c.n_kv_heads) * size_t(c.max_ctx) * size_t(hd);
+    m->kc = static_cast<float*>(dev_alloc(m, kv_elems * 4, "K cache", e));
+    if (!m->kc) return false;
+    m->vc = static_cast<float*>(dev_alloc(m, kv_elems * 4, "V cache", e));
+    if (!m->vc) return false;
+    m->kv_bytes = int64_t(kv_elems) * 8;
+
+    // cos/sin position cache, computed in f64 and rounded to f32 (section
+    // "Memory lifecycle", "Position caches").
+    const int64_t half = hd / 2;
+    std::vector<float> cs(size_t(c.max_ctx * half)), sn(size_t(c.max_ctx * half));
+    for (int64_t p = 0; p < c.max_ctx; ++p)
+        for (int64_t i = 0; i < half; ++i) {
+            const double ang = double(p) * std::pow(c.rope_theta, -2.0 * double(i) / double(hd));
+            cs[size_t(p * half + i)] = float(std::cos(ang));
+            sn[size_t(p * half + i)] = float(std::sin(ang));
+        }
+    m->cos_t = static_cast<float*>(dev_alloc(m, cs.size() * 4, "rope cos", e));
+    if (!m->cos_t) return false;
+    m->sin_t = static_cast<float*>(dev_alloc(m, sn.size() * 4, "rope sin", e));
+    if (!m->sin_t) return false;
+    if (!check(hipMemcpyAsync(m->cos_t, cs.data(), cs.size() * 4, hipMemcpyHostToDevice, m->stream),
+               "rope cos upload", e))
+        return false;
+    if (!check(hipMemcpyAsync(m->sin_t, sn.data(), sn.size() * 4, hipMemcpyHostToDevice, m->stream),
+               "rope sin upload", e))
+        return false;
+
+    // Decode state, attention partials and counters.
+    m->state = static_cast<DevState*>(dev_alloc(m, sizeof(DevState), "decode state", e));
+    if (!m->state) return false;
+    const int G = c.n_heads / c.n_kv_heads;
+    m->attn_part = static_cast<float*>(dev_alloc(
+        m, size_t(c.n_kv_heads) * ATTN_MAX_SPLIT * G * (hd + 2) * 4, "attention partials", e));
+    if (!m->attn_part) return false;
+    m->argmax_out = static_cast<int*>(dev_alloc(m, 4, "argmax result", e));
+    if (!m->argmax_out) return false;
+    m->gen_tokens = static_cast<int*>(dev_alloc(m, size_t(c.max_ctx) * 4, "generated tokens", e));
+    if (!m->gen_tokens) return false;
+    if (!check(hipMemsetAsync(m->state, 0, sizeof(DevState), m->stream), "state init", e)) return false;
+    if (!check(hipStreamSynchronize(m->stream), "upload", e)) return false;
+    return true;
+}
+
+// ---------------------------------------------------------------------------
+// The decode step: one token at position kv_len (state->pos), through the
+// step list. Per layer: [rms_norm + q/k/v matmul] -> [norm_heads + rope + KV
+// append + attention] -> [o matmul + add] -> [rms_norm + gate/up matmul +
+// silu + mul] -> [down matmul + add]; then [rms_norm + logits matmul].
+// ---------------------------------------------------------------------------
+struct StepBufs {
+    float *x, *qkv, *att, *mid;
+};
+
+bool step_buffers(df_model* m, StepBufs* b, Fail* e)
+{
+    const df_config& c = m->cfg;
+    const size_t qd = size_t(c.n_heads) * c.head_dim, kvd = size_t(c.n_kv_heads) * c.head_dim;
+    b->x = static_cast<float*>(m->pool.alloc(size_t(c.d_model) * 4, USAGE_DEVICE, e));
+    b->qkv = static_cast<float*>(m->pool.alloc((qd + 2 * kvd) * 4, USAGE_DEVICE, e));
+    b->att = static_cast<float*>(m->pool.alloc(qd * 4, USAGE_DEVICE, e));
+    b->mid = static_cast<float*>(m->pool.alloc(size_t(c.ffn_dim) * 4, USAGE_DEVICE, e));
+    return b->x && b->qkv && b->att && b->mid;
+}
+
+// Event pair around one launch when its class is being profiled.
+struct ProfScope {
+    df_model* m;
+    hipEvent_t end = nullptr;
+    ProfScope(df_model* mm, int kernel) : m(mm)
+    {
+        if (m->prof_kernel != kernel) return;
+        if (m->prof_used == m->prof_events.size()) {
+            hipEvent_t a = nullptr, b = nullptr;
+            if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
+                (void)hipGetLastError();
+                return;
+            }
+            m->prof_events.emplace_back(a, b);
+        }
+        auto& ev = m->prof_events[m->prof_used++];
+        (void)hipEventRecord(ev.first, m->stream);
+        end = ev.second;
+    }
+    ~ProfScope()
+    {
+        if (end) (void)hipEventRecord(end, m->stream);
+    }
+};
+
+hipError_t launch_step(df_model* m, const StepBufs& b, int grid_splits, float* logits)
+{
+    const df_config& c = m->cfg;
+    const float eps = float(c.rms_eps);
+    const int hd = c.head_dim;
+    const int64_t qd = int64_t(c.n_heads) * hd, kvd = int64_t(c.n_kv_heads) * hd;
+    const size_t kv_layer = size_t(c.n_kv_heads) * size_t(c.max_ctx) * size_t(hd);
+    hipError_t r;
+    {
+        ProfScope ps(m, DF_K_EMBED);
+        r = launch_embed(m->embd, nullptr, &m->state->tok, 1, b.x, m->stream);
+    }
+    if (r != hipSuccess) return r;
+    for (int l = 0; l < c.n_layers; ++l) {
+        const Layer& L = m->layers[size_t(l)];
+        {
+            ProfScope ps(m, DF_K_QKV);
+            r = launch_matvec(L.wqkv, MV_STORE, b.x, L.attn_norm, eps, qd + 2 * kvd, 0, b.qkv, m->stream);
+        }
+        if (r != hipSuccess) return r;
+        AttnDecodeArgs a{};
+        a.qkv = b.qkv;
+        a.q_norm = L.q_norm;
+        a.k_norm = L.k_norm;
+        a.eps = eps;
+        a.cos_t = m->cos_t;
+        a.sin_t = m->sin_t;
+        a.kc = m->kc + size_t(l) * kv_layer;
+        a.vc = m->vc + size_t(l) * kv_layer;
+        a.max_ctx = c.max_ctx;
+        a.n_heads = c.n_heads;
+        a.n_kv = c.n_kv_heads;
+        a.head_dim = hd;
+        a.state_pos = &m->state->pos;
+        a.part = m->attn_part;
+        a.out = b.att;
+        a.grid_splits = grid_splits;
+        {
+            ProfScope ps(m, DF_K_ATTN);
+            r = launch_attn_decode(a, m->stream);
+            if (r == hipSuccess) r = launch_attn_combine(a, m->stream);
+        }
+        if (r != hipSuccess) return r;
+        {
+            ProfScope ps(m, DF_K_O);
+            r = launch_matvec(L.wo, MV_RESID, b.att, nullptr, eps, c.d_model, 0, b.x, m->stream);
+        }
+        if (r != hipSuccess) return r;
+        {
+            ProfScope ps(m, DF_K_GATE_UP);
+            r = launch_matvec(L.wgu, MV_SWIGLU, b.x, L.ffn_norm, eps, c.ffn_dim, c.ffn_dim, b.mid,
+                              m->stream);
+        }
+        if (r != hipSuccess) return r;
+        {
+            ProfScope ps(m, DF_K_DOWN);
+            r = launch_matvec(L.wd, MV_RESID, b.mid, nullptr, eps, c.d_model, 0, b.x, m->stream);
+        }
+        if (r != hipSuccess) return r;
+    }
+    if (logits) {
+        ProfScope ps(m, DF_K_LOGITS);
+        r = launch_matvec(m->out, MV_STORE, b.x, m->out_norm, eps, c.vocab, 0, logits, m->stream);
+    }
+    return r;
+}
+
+struct BusyGuard {
+    df_model* m;
+    bool ok;
+    explicit BusyGuard(df_model* mm) : m(mm)
+    {
+        int expect = 0;
+        ok = m->busy.compare_exchange_strong(expect, 1);
+    }
+    ~BusyGuard()
+    {
+        if (ok) m->busy.store(0);
+    }
+};
+
+df_status set_err(df_model* m, df_status code, const std::string& msg)
+{
+    m->err = msg;
+    return code;
+}
+
+void collect_event_time(df_model* m)
+{
+    if (!m->ev_kind) return;
+    if (hipEventSynchronize(m->ev1) == hipSuccess) {
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, m->ev0, m->ev1) == hipSuccess) {
+            if (m->ev_kind == 1) m->last_step_ms = ms;
+            else m->last_prefill_ms = ms;
+        }
+    }
+    (void)hipGetLastError();
+    m->ev_kind = 0;
+}
+
+df_status decode_one(df_model* m, int32_t tok, float* logits)
+{
+    Fail e{DF_OK, ""};
+    const int pos = m->kv_len;
+    m->pool.reset();
+    StepBufs b{};
+    if (!step_buffers(m, &b, &e)) return set_err(m, e.code, e.msg);
+    hipError_t r = launch_set_state(m->state, pos, tok, 0, m->stream);
+    if (r == hipSuccess) r = launch_step(m, b, attn_splits(pos), logits);
+    if (r != hipSuccess) {
+        (void)hipGetLastError();
+        return set_err(m, DF_ERR_DEVICE, fmt("decode launch failed: %s", hipGetErrorString(r)));
+    }
+    m->kv_len = pos + 1;
+    return DF_OK;
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+extern "C" {
+
+df_status df_load(const df_config* cfg, const df_tensor* tensors, size_t n_tensors,
+                  const df_options* opt, df_model** out)
+{
+    const auto t_start = std::chrono::steady_clock::now();
+    g_load_error.clear();
+    if (!out) {
+        g_load_error = "df_load: out is NULL";
+        return DF_ERR_INVALID_ARGUMENT;
+    }
+    *out = nullptr;
+    Fail e{DF_OK, ""};
+    std::map<std::string, const df_tensor*> found;
+    if (!validate_config(cfg, &e) || !validate_tensors(cfg, tensors, n_tensors, &found, &e)) {
+        g_load_error = e.msg;
+        return e.code;
+    }
+
+    // Backend init: the first device call.
+    int ndev = 0;
+    hipError_t r = hipGetDeviceCount(&ndev);
+    if (r != hipSuccess || ndev <= 0) {
+        (void)hipGetLastError();
+        g_load_error = fmt("backend init: no HIP device (%s)",
+                           r != hipSuccess ? hipGetErrorString(r) : "0 devices");
+        return DF_ERR_BACKEND_INIT;
+    }
+    const int dev = opt ? opt->device : 0;
+    if (dev < 0 || dev >= ndev) {
+        g_load_error = fmt("backend init: device %d out of range (0..%d)", dev, ndev - 1);
+        return DF_ERR_BACKEND_INIT;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        g_load_error = "backend init: hipGetDeviceProperties failed";
+        return DF_ERR_BACKEND_INIT;
+    }
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+        g_load_error = fmt("backend init: device %d is %s; this library is built for gfx950",
+                           dev, prop.gcnArchName);
+        return DF_ERR_BACKEND_INIT;
+    }
+    if (hipSetDevice(dev) != hipSuccess) {
+        (void)hipGetLastError();
+        g_load_error = fmt("backend init: hipSetDevice(%d) failed", dev);
+        return DF_ERR_BACKEND_INIT;
+    }
+
+    df_model* m = new (std::nothrow) df_model();
+    if (!m) {
+        g_load_error = "host allocation of the model failed";
+        return DF_ERR_OUT_OF_MEMORY;
+    }
+    m->cfg = *cfg;
+    m->device = dev;
+    if (opt && opt->stream) {
+        m->stream = static_cast<hipStream_t>(opt->stream);
+    } else {
+        if (hipStreamCreateWithFlags(&m->stream, hipStreamNonBlocking) != hipSuccess) {
+            (void)hipGetLastError();
+            delete m;
+            g_load_error = "backend init: hipStreamCreate failed";
+            return DF_ERR_BACKEND_INIT;
+        }
+        m->own_stream = true;
+    }
+    if (hipEventCreate(&m->ev0) != hipSuccess || hipEventCreate(&m->ev1) != hipSuccess) {
+        (void)hipGetLastError();
+        release(m);
+        delete m;
+        g_load_error = "backend init: hipEventCreate failed";
+        return DF_ERR_BACKEND_INIT;
+    }
+    if (!build_model(m, found, &e)) {
+        release(m);
+        delete m;
+        g_load_error = e.msg;
+        return e.code;
+    }
+    m->load_ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t_start).count();
+    *out = m;
+    return DF_OK;
+}
+
+df_status df_forward(df_model* m, const int32_t* tokens, int32_t n, float* logits_dev)
+{
+    if (!m) return DF_ERR_INVALID_ARGUMENT;
+    BusyGuard guard(m);
+    if (!guard.ok) return DF_ERR_BUSY;
+    if (!tokens || n <= 0)
+        return set_err(m, DF_ERR_INVALID_ARGUMENT, fmt("df_forward: tokens %s, n = %d",
+                                                       tokens ? "given" : "NULL", n));
+    if (int64_t(m->kv_len) + n > m->cfg.max_ctx)
+        return set_err(m, DF_ERR_CONTEXT_FULL,
+                       fmt("df_forward: %d positions in the cache + %d new > max_ctx %d",
+                           m->kv_len, n, m->cfg.max_ctx));
+    for (int32_t i = 0; i < n; ++i)
+        if (tokens[i] < 0 || tokens[i] >= m->cfg.vocab)
+            return set_err(m, DF_ERR_INVALID_ARGUMENT,
+                           fmt("df_forward: token %d at index %d outside [0, %d)", tokens[i], i,
+                               m->cfg.vocab));
+    if (hipSetDevice(m->device) != hipSuccess) {
+        (void)hipGetLastError();
+        return set_err(m, DF_ERR_DEVICE, "hipSetDevice failed");
+    }
+    collect_event_time(m);
+    (void)hipEventRecord(m->ev0, m->stream);
+    df_status st = DF_OK;
+    for (int32_t i = 0; i < n && st == DF_OK; ++i)
+        st = decode_one(m, tokens[i], i == n - 1 ? logits_dev : nullptr);
+    (void)hipEventRecord(m->ev1, m->stream);
+    m->ev_kind = n == 1 ? 1 : 2;
+    if (st == DF_OK) m->n_forward++;
+    return st;
+}
+
+df_status df_generate(df_model* m, int32_t first_token, int32_t n_steps, int32_t* tokens_dev,
+                      float* logits_dev)
+{
+    if (!m) return DF_ERR_INVALID_ARGUMENT;
+    BusyGuard guard(m);
+    if (!guard.ok) return DF_ERR_BUSY;
+    if (n_steps <= 0 || !tokens_dev)
+        return set_err(m, DF_ERR_INVALID_ARGUMENT, "df_generate: n_steps <= 0 or tokens_dev NULL");
+    if (first_token < 0 || first_token >= m->cfg.vocab)
+        return set_err(m, DF_ERR_INVALID_ARGUMENT,
+                       fmt("df_generate: first token %d outside [0, %d)", first_token, m->cfg.vocab));
+    if (int64_t(m->kv_len) + n_steps > m->cfg.max_ctx)
+        return set_err(m, DF_ERR_CONTEXT_FULL,
+                       fmt("df_generate: %d positions + %d steps > max_ctx %d", m->kv_len, n_steps,
+                           m->cfg.max_ctx));
+    if (hipSetDevice(m->device) != hipSuccess) {
+        (void)hipGetLastError();
+        return set_err(m, DF_ERR_DEVICE, "hipSetDevice failed");
+    }
+    collect_event_time(m);
+    Fail e{DF_OK, ""};
+    m->pool.reset();
+    StepBufs b{};
+    if (!step_buffers(m, &b, &e)) return set_err(m, e.code, e.msg);
+    float* lg = static_cast<float*>(m->pool.alloc(size_t(m->cfg.vocab) * 4, USAGE_DEVICE, &e));
+    if (!lg) return set_err(m, e.code, e.msg);
+    hipError_t r = launch_set_state(m->state, m->kv_len, first_token, 0, m->stream);
+    // One decode step + greedy argmax, position and token read from device
+    // state: the same launches serve every step, so they are captured into a
+    // graph once and replayed (unless a kernel class is being profiled).
+    const int max_splits = attn_splits(m->cfg.max_ctx - 1);
+    auto step_launches = [&]() -> hipError_t {
+        hipError_t rr = launch_step(m, b, max_splits, lg);
+        if (rr == hipSuccess) {
+            ProfScope ps(m, DF_K_ARGMAX);
+            rr = launch_argmax(lg, m->cfg.vocab, m->state, m->argmax_out, 1, m->gen_tokens, m->stream);
+        }
+        return rr;
+    };
+    const std::vector<void*> key{b.x, b.qkv, b.att, b.mid, lg};
+    const bool use_graph = m->prof_kernel < 0;
+    if (use_graph && (!m->gen_exec || m->gen_key != key) && r == hipSuccess) {
+        if (m->gen_exec) {
+            (void)hipGraphExecDestroy(m->gen_exec);
+            m->gen_exec = nullptr;
+        }
+        hipGraph_t graph = nullptr;
+        hipError_t c = hipStreamBeginCapture(m->stream, hipStreamCaptureModeThreadLocal);
+        if (c == hipSuccess) {
+            const hipError_t launched = step_launches();
+            c = hipStreamEndCapture(m->stream, &graph);
+            if (c == hipSuccess && launched != hipSuccess) c = launched;
+        }
+        if (c == hipSuccess) c = hipGraphInstantiate(&m->gen_exec, graph, nullptr, nullptr, 0);
+        if (graph) (void)hipGraphDestroy(graph);
+        if (c != hipSuccess) {
+            (void)hipGetLastError();
+            m->gen_exec = nullptr;
+        } else {
+            m->gen_key = key;
+        }
+    }
+    for (int32_t i = 0; i < n_steps && r == hipSuccess; ++i) {
+        if (use_graph && m->gen_exec) r = hipGraphLaunch(m->gen_exec, m->stream);
+        else r = step_launches();
+    }
+    if (r == hipSuccess)
+        r = hipMemcpyAsync(tokens_dev, m->gen_tokens, size_t(n_steps) * 4, hipMemcpyDeviceToDevice,
+                           m->stream);
+    if (r == hipSuccess && logits_dev)
+        r = hipMemcpyAsync(logits_dev, lg, size_t(m->cfg.vocab) * 4, hipMemcpyDeviceToDevice, m->stream);
+    if (r != hipSuccess) {
+        (void)hipGetLastError();
+        return set_err(m, DF_ERR_DEVICE, fmt("df_generate: launch failed: %s", hipGetErrorString(r)));
+    }
+    m->kv_len += n_steps;
+    m->n_forward += n_steps;
+    return DF_OK;
+}
+
+df_status df_reset_kv_cache(df_model* m)
+{
+    if (!m) return DF_ERR_INVALID_ARGUMENT;
+    BusyGuard guard(m);
+    if (!guard.ok) return DF_ERR_BUSY;
+    m->kv_len = 0;
+    return DF_OK;
+}
+
+void df_free(df_model** pm)
+{
+    if (!pm || !*pm) return;
+    df_model* m = *pm;
+    (void)hipSetDevice(m->device);
+    release(m);
+    delete m;
+    *pm = nullptr;
+}
+
+const char* df_last_error(const df_model* m)
+{
+    return m ? m->err.c_str() : g_load_error.c_str();
+}
+
+df_status df_get_timings(df_model* m, df_timings* out)
+{
+    if (!m || !out) return DF_ERR_INVALID_ARGUMENT;
+    (void)hipSetDevice(m->device);
+    (void)hipStreamSynchronize(m->stream);
+    collect_event_time(m);
+    out->load_ms = m->load_ms;
+    out->last_prefill_ms = m->last_prefill_ms;
+    out->last_step_ms = m->last_step_ms;
+    out->n_forward = m->n_forward;
+    out->weight_bytes = m->weight_bytes;
+    out->kv_bytes = m->kv_bytes;
+    out->pool_bytes = int64_t(m->pool.bytes());
+    return DF_OK;
+}
+
+df_status df_kv_length(const df_model* m, int32_t* out)
+{
+    if (!m || !out) return DF_ERR_INVALID_ARGUMENT;
+    *out = m->kv_len;
+    return DF_OK;
+}
+
+df_status df_argmax(df_model* m, const float* logits_dev, int32_t* token_host)
+{
+    if (!m || !logits_dev || !token_host) return DF_ERR_INVALID_ARGUMENT;
+    (void)hipSetDevice(m->device);
+    hipError_t r = launch_argmax(logits_dev, m->cfg.vocab, m->state, m->argmax_out, 0, nullptr, m->stream);
+    if (r == hipSuccess)
+        r = hipMemcpyAsync(token_host, m->argmax_out, 4, hipMemcpyDeviceToHost, m->stream);
+    if (r == hipSuccess) r = hipStreamSynchronize(m->stream);
+    if (r != hipSuccess) {
+        (void)hipGetLastError();
+        return set_err(m, DF_ERR_DEVICE, fmt("df_argmax: %s", hipGetErrorString(r)));
+    }
+    return DF_OK;
+}
+
+static df_status kv_copy(df_model* m, int32_t layer, int32_t which, int32_t pos0, int32_t n,
+                         float* host, bool to_host)
+{
+    const df_config& c = m->cfg;
+    if (layer < 0 || layer >= c.n_layers || (which != 0 && which != 1) || pos0 < 0 || n < 0 ||
+        int64_t(pos0) + n > c.max_ctx || (!host && n > 0))
+        return set_err(m, DF_ERR_INVALID_ARGUMENT,
+                       fmt("kv rows: layer %d which %d rows [%d, %d) out of range", layer, which,
+                           pos0, pos0 + n));
+    (void)hipSetDevice(m->device);
+    float* base = (which ? m->vc : m->kc) +
+                  size_t(layer) * size_t(c.n_kv_heads) * size_t(c.max_ctx) * size_t(c.head_dim);
+    for (int g = 0; g < c.n_kv_heads && n > 0; ++g) {
+        float* dev = base + (size_t(g) * c.max_ctx + size_t(pos0)) * c.head_dim;
+        float* h = host + size_t(g) * n * c.head_dim;
+        const size_t bytes = size_t(n) * c.head_dim * 4;
+        hipError_t r = to_host ? hipMemcpyAsync(h, dev, bytes, hipMemcpyDeviceToHost, m->stream)
+                               : hipMemcpyAsync(dev, h, bytes, hipMemcpyHostToDevice, m->stream);
+        if (r != hipSuccess) {
+            (void)hipGetLastError();
+            return set_err(m, DF_ERR_DEVICE, fmt("kv copy: %s", hipGetErrorString(r)));
+        }
+    }
+    if (hipStreamSynchronize(m->stream) != hipSuccess) {
+        (void)hipGetLastError();
+        return set_err(m, DF_ERR_DEVICE, "kv copy: synchronise failed");
+    }
+    return DF_OK;
+}
+
+df_status df_read_kv(df_model* m, int32_t layer, int32_t which, int32_t pos0, int32_t n, float* host)
+{
+    if (!m) return DF_ERR_INVALID_ARGUMENT;
+    return kv_copy(m, layer, which, pos0, n, host, true);
+}
+
+df_status df_write_kv(df_model* m, int32_t layer, int32_t which, int32_t pos0, int32_t n,
+                      const float* host, int32_t kv_len_after)
+{
+    if (!m) return DF_ERR_INVALID_ARGUMENT;
+    BusyGuard guard(m);
+    if (!guard.ok) return DF_ERR_BUSY;
+    if (kv_len_after < 0 || kv_len_after > m->cfg.max_ctx)
+        return set_err(m, DF_ERR_INVALID_ARGUMENT,
+                       fmt("df_write_kv: kv_len_after %d outside [0, %d]", kv_len_after, m->cfg.max_ctx));
+    df_status st = kv_copy(m, layer, which, pos0, n, const_cast<float*>(host), false);
+    if (st == DF_OK) m->kv_len = kv_len_after;
+    return st;
+}
+
+void* df_stream(const df_model* m)
+{
+    return m ? static_cast<void*>(m->stream) : nullptr;
+}
+
+df_status df_profile(df_model* m, int32_t kernel, int32_t enable)
+{
+    if (!m || kernel < 0 || kernel >= DF_K_COUNT) return DF_ERR_INVALID_ARGUMENT;
+    m->prof_kernel = enable ? kernel : -1;
+    return DF_OK;
+}
+
+df_status df_profile_read(df_model* m, int32_t kernel, int64_t* launches, double* total_ms)
+{
+    if (!m || !launches || !total_ms || kernel < 0 || kernel >= DF_K_COUNT)
+        return DF_ERR_INVALID_ARGUMENT;
+    (void)hipSetDevice(m->device);
+    if (hipStreamSynchronize(m->stream) != hipSuccess) {
+        (void)hipGetLastError();
+        return set_err(m, DF_ERR_DEVICE, "df_profile_read: synchronise failed");
+    }
+    double ms_sum = 0;
+    for (size_t i = 0; i < m->prof_used; ++i) {
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, m->prof_events[i].first, m->prof_events[i].second) == hipSuccess)
+            ms_sum += ms;
+        else
+            (void)hipGetLastError();
+    }
+    *launches = int64_t(m->prof_used);
+    *total_ms = ms_sum;
+    m->prof_used = 0;
+    return DF_OK;
+}
+
+}  // extern "C"
