@@ -1,0 +1,275 @@
+#!/usr/bin/env python3
+"""bs=1 decode throughput of the llama-8B-shaped decoder on one MI355X.
+
+One step is one decode token through the whole step list (embed, 32 layers
+of rms_norm / q,k,v matmul / rope / attention over the KV cache / o matmul /
+add / rms_norm / gate,up matmul / silu / mul / down matmul / add, final
+rms_norm, logits matmul) plus the greedy argmax, at context 4096 onwards.
+The context is built by one bulk prefill of a 4096-token synthetic prompt,
+timed and reported as prefill tokens/s. Weights are random with the shape's
+distributions (f16 matmul weights ~N(0, 0.02), norms ~1+N(0, 0.02)), drawn
+on the GPU from a seeded generator; token ids are synthetic.
+
+Prints one JSON line (see the keys in `report`):
+  value          decode tokens/s over the timed steps
+  roofline       the gate/up matvec (the largest kernel: 47% of a step's
+                 bytes): algorithmic bytes per launch / mean launch time
+                 from HIP events on the library's stream, vs 8 TB/s
+  cpu_baseline   the CPU oracle on a bounded sample of the same step
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+METRIC = "bs=1 decode tokens/s (8B shape, ctx 4096); achieved HBM GB/s vs peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def step_bytes(cfg: dict, p: int) -> int:
+    """Algorithmic HBM bytes of one decode step at position p: every matmul
+    weight once (f16, or 8-bit values + f16 scales), the norm weights as held
+    on the device (f32), one embedding row, the KV rows 0..p-1 read and row p
+    written (f32), and the logits written."""
+    d, F, V, L = cfg["d_model"], cfg["ffn_dim"], cfg["vocab"], cfg["n_layers"]
+    hd = cfg["head_dim"]
+    qd, kvd = cfg["n_heads"] * hd, cfg["n_kv_heads"] * hd
+    per_layer = (qd + 2 * kvd) * d + d * qd + 2 * F * d + d * F
+    mat = L * per_layer + V * d  # lm head (untied)
+    wbytes = mat * 2 if cfg["wdtype"] == "f16" else mat + mat // 32 * 2
+    norms = (L * 2 * d + d) * 4
+    if cfg["arch"] == "qwen3":
+        norms += L * 2 * hd * 4
+    kv_tok = L * 2 * kvd * 4
+    return wbytes + norms + d * 2 + (p + 1) * kv_tok + V * 4
+
+
+def gate_up_launch_bytes(cfg: dict) -> int:
+    """One gate/up launch: per output unit a gate row and an up row of d
+    weights (16,384 bytes in f16 at d = 4096), times ffn_dim units, plus the
+    activation and norm weight read once and the ffn_dim outputs written."""
+    d, F = cfg["d_model"], cfg["ffn_dim"]
+    unit = 2 * d * (2 if cfg["wdtype"] == "f16" else 1)
+    if cfg["wdtype"] == "q8":
+        unit += 2 * (d // 32) * 2
+    return F * unit + d * 4 + d * 4 + F * 4
+
+
+def cpu_baseline(cfg: dict, ctx: int) -> dict:
+    """The oracle, as it is, on a bounded sample of one decode step: a model
+    with the same shapes but 2 of the 32 layers (plus embed and the logits
+    matmul), the KV cache restored to `ctx` synthetic positions; the step time
+    is scaled to the full layer count with the 0-layer time subtracted."""
+    import numpy as np
+    import oracle
+    import synth
+    threads = len(os.sched_getaffinity(0))
+    oracle.set_threads(threads)
+    c2 = dict(cfg, n_layers=2, max_ctx=ctx + 4)
+    W = synth.make_weights(c2)
+    m2 = oracle.Model(c2, W)
+    for layer in range(2):
+        K, V = synth.make_kv_rows(c2, layer, ctx)
+        m2.kv_write(layer, 0, 0, K)
+        m2.kv_write(layer, 1, 0, V)
+    c0 = dict(c2, n_layers=0)
+    m0 = oracle.Model(c0, W)
+    tok = int(synth.make_prompt(cfg, 1, stream=7)[0])
+
+    def time_one(m, reps):
+        ts = []
+        for _ in range(reps):
+            m.set_kv_len(ctx if m is m2 else 0)
+            t = time.perf_counter()
+            m.forward([tok])
+            ts.append(time.perf_counter() - t)
+        return min(ts)
+    time_one(m2, 1)
+    t2 = time_one(m2, 4)
+    t0 = time_one(m0, 4)
+    per_layer = max(0.0, (t2 - t0) / 2)
+    t_tok = t0 + cfg["n_layers"] * per_layer
+    m2.close()
+    m0.close()
+    try:
+        cpu = [l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo")
+               if l.startswith("model name")][0]
+    except Exception:
+        cpu = "unknown"
+    return {"value": round(1.0 / t_tok, 4), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"one decode step at context {ctx} through 2 of {cfg['n_layers']} "
+                       f"layers plus embed and logits (best of 4), 0-layer time "
+                       f"{t0 * 1e3:.0f} ms, per-layer {per_layer * 1e3:.0f} ms, "
+                       f"scaled to {cfg['n_layers']} layers; cpu {cpu}")}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--context", type=int, default=4096)
+    ap.add_argument("--workload", default="llama_8b",
+                    choices=["llama_8b", "llama_8b_q8", "qwen3_8b", "qwen3_0p6b"])
+    ap.add_argument("--context-from", default="restore", choices=["prefill", "restore"],
+                    help="build the context by bulk prefill (default) or by writing "
+                         "synthetic KV rows")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} "
+              f"(WORLD_SIZE {world}) is not supported. Multi-GPU sharding is "
+              f"described in DESIGN.md, not built.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import decoder_forward_amd as dfa
+    import synth
+    dfa.lib()  # fails loudly if the HIP library is not built
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    cfg = synth.config(args.workload)
+    ctx = args.context
+    max_ctx = ctx + max(args.steps, args.warmup) + 8
+    log(f"[bench] {args.workload}: generating weights on the GPU")
+    W = synth.make_weights_device(cfg)
+    torch.cuda.synchronize()
+    m = dfa.Model(cfg, W, max_ctx=max_ctx)
+    del W
+    torch.cuda.empty_cache()
+    log(f"[bench] loaded in {m.timings()['load_ms']:.0f} ms")
+
+    prefill_tps = None
+    if args.context_from == "prefill":
+        prompt = synth.make_prompt(cfg, ctx, stream=0)
+        m.forward(prompt[:8], logits=False)  # warm the bulk path
+        m.reset()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        m.forward(prompt, logits=True)
+        torch.cuda.synchronize()
+        prefill_s = time.perf_counter() - t
+        prefill_tps = ctx / prefill_s
+        log(f"[bench] bulk prefill of {ctx} tokens: {prefill_s * 1e3:.1f} ms "
+            f"({prefill_tps:.0f} tokens/s)")
+    else:
+        for layer in range(cfg["n_layers"]):
+            K, V = synth.make_kv_rows_device(cfg, layer, ctx)
+            m.write_kv(layer, 0, 0, K.cpu().numpy(), ctx)
+            m.write_kv(layer, 1, 0, V.cpu().numpy(), ctx)
+        log(f"[bench] restored {ctx} synthetic KV positions")
+    assert m.kv_len == ctx
+    first = int(synth.make_prompt(cfg, 1, stream=3)[0])
+
+    def rewind():  # kv_len back to the context; rows past it are rewritten
+        m.write_kv(0, 0, 0, np.zeros((cfg["n_kv_heads"], 0, cfg["head_dim"]), np.float32), ctx)
+
+    # warmup (also captures the step graph), then rewind to the context
+    if args.warmup > 0:
+        m.generate(first, args.warmup)
+    torch.cuda.synchronize()
+    rewind()
+
+    toks = torch.empty(args.steps, dtype=torch.int32, device=m.device)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(m.stream)
+    dfa.df_generate(m.h, first, args.steps, toks, m.logits)
+    ev1.record(m.stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dev_ms = ev0.elapsed_time(ev1)
+    ms_per_step = dev_ms / args.steps
+    value = args.steps / (dev_ms / 1e3)
+    total_bytes = sum(step_bytes(cfg, ctx + i) for i in range(args.steps))
+    achieved = total_bytes / (dev_ms / 1e3) / 1e9
+    log(f"[bench] decode {args.steps} steps: {ms_per_step:.3f} ms/step, {value:.1f} tok/s, "
+        f"{achieved:.0f} GB/s ({achieved / PEAK_HBM_GBPS:.1%} of 8 TB/s); wall {wall:.3f} s")
+
+    # Per-kernel device time over the same steps (event pair per launch).
+    kernels = {}
+    for k in ("qkv", "attn", "o", "gate_up", "down", "logits", "argmax", "embed"):
+        rewind()
+        dfa.df_profile(m.h, k, True)
+        dfa.df_generate(m.h, first, args.steps, toks, m.logits)
+        n, tot = dfa.df_profile_read(m.h, k)
+        dfa.df_profile(m.h, k, False)
+        kernels[k] = {"launches": n, "mean_us": round(tot / max(n, 1) * 1e3, 2),
+                      "ms_per_step": round(tot / args.steps, 4)}
+    gu = kernels["gate_up"]
+    gu_bytes = gate_up_launch_bytes(cfg)
+    gu_gbps = gu_bytes / (gu["mean_us"] * 1e-6) / 1e9
+    log(f"[bench] kernels: {json.dumps(kernels)}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline (bounded sample)")
+        cpu = cpu_baseline(cfg, ctx)
+        log(f"[bench] cpu baseline: {cpu}")
+
+    t = m.timings()
+    report = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{args.workload}: bs=1 greedy decode, positions {ctx}..{ctx + args.steps - 1}, "
+                         f"{cfg['n_layers']} layers, d_model {cfg['d_model']}, "
+                         f"{cfg['n_heads']}/{cfg['n_kv_heads']} heads of {cfg['head_dim']}, "
+                         f"ffn {cfg['ffn_dim']}, vocab {cfg['vocab']}, "
+                         f"{cfg['wdtype']} weights, f32 activations and KV cache"),
+            "batch": 1,
+            "context": ctx,
+            "context_from": args.context_from,
+            "weight_dtype": cfg["wdtype"],
+        },
+        "achieved_hbm_gbps": round(achieved, 1),
+        "hbm_frac": round(achieved / PEAK_HBM_GBPS, 4),
+        "prefill_tokens_per_s": round(prefill_tps, 1) if prefill_tps else None,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "gate/up matvec (rms_norm + gate,up matmul + silu * up)",
+            "achieved": round(gu_gbps, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(gu_gbps / PEAK_HBM_GBPS, 4),
+            "traffic": None,
+            "bytes_per_launch": gu_bytes,
+            "mean_launch_us": gu["mean_us"],
+        },
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+        "memory": {"weight_bytes": t["weight_bytes"], "kv_bytes": t["kv_bytes"],
+                   "activation_pool_bytes": t["pool_bytes"]},
+    }
+    print(json.dumps(report), flush=True)
+    m.close()
+
+
+if __name__ == "__main__":
+    main()

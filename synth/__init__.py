@@ -255,3 +255,43 @@ def weight_bytes(cfg: dict) -> int:
         else:
             total += rows * cols * (4 if cfg["wdtype"] == "f32" else 2)
     return total
+
+
+def make_weights_device(cfg: dict, device="cuda") -> dict:
+    """The same distributions drawn on the GPU with torch's generator (one
+    seeded stream per tensor: seed = base * 1000003 + tensor_id). Used where
+    a run needs full-size random weights fast and does not compare with the
+    oracle (benchmarks); parity tests use make_weights."""
+    import torch
+    out = {}
+    g = torch.Generator(device=device)
+    for name, kind, rows, cols in tensor_specs(cfg):
+        g.manual_seed(cfg["seed"] * 1000003 + tensor_id(name))
+        wd = cfg["wdtype"]
+        if kind == "matmul" and wd == "q8":
+            nblk = cols // Q8_BLOCK
+            q = torch.randint(-127, 128, (rows, nblk, Q8_BLOCK), device=device,
+                              generator=g, dtype=torch.int8)
+            s = (torch.randn(rows, nblk, 1, device=device, generator=g).abs()
+                 * 0.02 / 127.0).half()
+            blk = torch.empty(rows, nblk, Q8_BLOCK_BYTES, dtype=torch.uint8, device=device)
+            blk[:, :, 0:2] = s.view(torch.uint8)
+            blk[:, :, 2:] = q.view(torch.uint8)
+            out[name] = blk.reshape(rows, nblk * Q8_BLOCK_BYTES)
+            continue
+        dtype = torch.float32 if wd == "f32" else torch.float16
+        z = torch.randn(rows, cols, device=device, generator=g) * 0.02
+        if kind == "norm":
+            z += 1.0
+        out[name] = z.to(dtype)
+    return out
+
+
+def make_kv_rows_device(cfg: dict, layer: int, n_pos: int, device="cuda"):
+    """Synthetic cache rows (K, V) f32 [n_kv, n_pos, hd] ~ N(0, 1) on the GPU."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(cfg["seed"] * 1000003 + 2 * 10**6 + layer)
+    shape = (cfg["n_kv_heads"], n_pos, cfg["head_dim"])
+    return (torch.randn(shape, device=device, generator=g),
+            torch.randn(shape, device=device, generator=g))
