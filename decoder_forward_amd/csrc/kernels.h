@@ -90,6 +90,54 @@ hipError_t launch_argmax(const float* v, int n, DevState* st, int* out_dev,
 hipError_t launch_set_state(DevState* st, int pos, int tok, int step,
                             hipStream_t s);
 
+// ---- bulk prefill ----------------------------------------------------------
+
+// out[s] = f16(w . x[s] / rms(x[s])) for `rows` rows of d floats.
+hipError_t launch_rmsnorm_rows(const float* x, const float* w, int rows, int d, float eps,
+                               uint16_t* out, hipStream_t s);
+
+// C[M][N] = A[M][K] B[N][K]^T on matrix cores, f16 operands, f32 accumulation.
+enum GemmMode {
+    GEMM_STORE_F32 = 0,   // C f32  = A B^T
+    GEMM_ADD_F32 = 1,     // C f32 += A B^T (residual)
+    GEMM_STORE_F16 = 2,   // C f16  = A B^T
+    GEMM_SWIGLU_F16 = 3,  // C f16 [M][N] = silu(A Bg^T) * (A Bu^T); Bu = B + up_rows rows
+};
+struct GemmArgs {
+    const uint16_t* A;
+    int64_t lda;
+    const uint16_t* B;
+    int64_t ldb;
+    void* C;
+    int64_t ldc;
+    int M, N, K;
+    int64_t up_rows;
+};
+hipError_t launch_gemm(const GemmArgs& g, int mode, hipStream_t s);
+
+struct QkPostArgs {
+    const float* qkv;     // [S][qd | kvd | kvd] f32
+    const float* q_norm;  // [hd] or null
+    const float* k_norm;
+    float eps;
+    const float* cos_t;
+    const float* sin_t;
+    float* kc;            // layer K cache [n_kv][max_ctx][hd]
+    float* vc;
+    uint16_t* q16;        // [S][n_heads][hd] f16
+    int S, p0, n_heads, n_kv, head_dim, max_ctx;
+};
+hipError_t launch_qk_post_rows(const QkPostArgs& a, hipStream_t s);
+
+struct AttnPrefillArgs {
+    const uint16_t* q16;  // [S][n_heads][hd] f16 (after RoPE)
+    const float* kc;      // layer K cache [n_kv][max_ctx][hd]
+    const float* vc;
+    uint16_t* out16;      // [S][n_heads * hd] f16
+    int S, p0, n_heads, n_kv, head_dim, max_ctx;
+};
+hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t s);
+
 // Upload helpers.
 hipError_t launch_to_f32(const void* src, int src_dtype, int64_t n, float* dst,
                          hipStream_t s);

@@ -724,6 +724,97 @@ df_status decode_one(df_model* m, int32_t tok, float* logits)
     return DF_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Bulk prefill: n tokens at positions kv_len .. kv_len+n-1 in one pass of
+// the step list over n rows (page "Execution contract", "Forward phase":
+// bulk prefill must match token-by-token within epsilon). Per layer:
+// [rms_norm rows -> f16] [q/k/v GEMM] [norm_heads + rope + KV append]
+// [causal flash attention] [o GEMM + add] [rms_norm rows -> f16]
+// [gate/up GEMM + silu * up] [down GEMM + add]; then the last row's
+// [rms_norm + logits matvec]. Needs f16 block weights.
+// ---------------------------------------------------------------------------
+bool bulk_supported(const df_model* m)
+{
+    return m->cfg.n_layers == 0 || m->layers[0].wqkv.dtype == W_F16;
+}
+
+df_status prefill(df_model* m, const int32_t* tokens, int32_t n, float* logits)
+{
+    const df_config& c = m->cfg;
+    Fail e{DF_OK, ""};
+    const int S = n, p0 = m->kv_len;
+    const int d = c.d_model, hd = c.head_dim, F = c.ffn_dim;
+    const int qd = c.n_heads * hd, kvd = c.n_kv_heads * hd;
+    const float eps = float(c.rms_eps);
+    m->pool.reset();
+    auto A = [&](size_t bytes) { return m->pool.alloc(bytes, USAGE_DEVICE, &e); };
+    float* x = static_cast<float*>(A(size_t(S) * d * 4));
+    uint16_t* h16 = static_cast<uint16_t*>(A(size_t(S) * d * 2));
+    float* qkv = static_cast<float*>(A(size_t(S) * (qd + 2 * kvd) * 4));
+    uint16_t* q16 = static_cast<uint16_t*>(A(size_t(S) * qd * 2));
+    uint16_t* att16 = static_cast<uint16_t*>(A(size_t(S) * qd * 2));
+    uint16_t* mid16 = static_cast<uint16_t*>(A(size_t(S) * F * 2));
+    int* toks = static_cast<int*>(A(size_t(S) * 4));
+    if (!x || !h16 || !qkv || !q16 || !att16 || !mid16 || !toks) return set_err(m, e.code, e.msg);
+    const size_t kv_layer = size_t(c.n_kv_heads) * size_t(c.max_ctx) * size_t(hd);
+    hipError_t r = hipMemcpyAsync(toks, tokens, size_t(S) * 4, hipMemcpyHostToDevice, m->stream);
+    if (r == hipSuccess) r = launch_embed(m->embd, toks, nullptr, S, x, m->stream);
+    for (int l = 0; l < c.n_layers && r == hipSuccess; ++l) {
+        const Layer& L = m->layers[size_t(l)];
+        r = launch_rmsnorm_rows(x, L.attn_norm, S, d, eps, h16, m->stream);
+        if (r != hipSuccess) break;
+        GemmArgs g{};
+        g.A = h16; g.lda = d;
+        g.B = static_cast<const uint16_t*>(L.wqkv.data); g.ldb = d;
+        g.C = qkv; g.ldc = qd + 2 * kvd;
+        g.M = S; g.N = qd + 2 * kvd; g.K = d;
+        r = launch_gemm(g, GEMM_STORE_F32, m->stream);
+        if (r != hipSuccess) break;
+        QkPostArgs qa{};
+        qa.qkv = qkv; qa.q_norm = L.q_norm; qa.k_norm = L.k_norm; qa.eps = eps;
+        qa.cos_t = m->cos_t; qa.sin_t = m->sin_t;
+        qa.kc = m->kc + size_t(l) * kv_layer; qa.vc = m->vc + size_t(l) * kv_layer;
+        qa.q16 = q16; qa.S = S; qa.p0 = p0; qa.n_heads = c.n_heads; qa.n_kv = c.n_kv_heads;
+        qa.head_dim = hd; qa.max_ctx = c.max_ctx;
+        r = launch_qk_post_rows(qa, m->stream);
+        if (r != hipSuccess) break;
+        AttnPrefillArgs aa{};
+        aa.q16 = q16; aa.kc = qa.kc; aa.vc = qa.vc; aa.out16 = att16;
+        aa.S = S; aa.p0 = p0; aa.n_heads = c.n_heads; aa.n_kv = c.n_kv_heads;
+        aa.head_dim = hd; aa.max_ctx = c.max_ctx;
+        r = launch_attn_prefill(aa, m->stream);
+        if (r != hipSuccess) break;
+        g = GemmArgs{};
+        g.A = att16; g.lda = qd;
+        g.B = static_cast<const uint16_t*>(L.wo.data); g.ldb = qd;
+        g.C = x; g.ldc = d; g.M = S; g.N = d; g.K = qd;
+        r = launch_gemm(g, GEMM_ADD_F32, m->stream);
+        if (r != hipSuccess) break;
+        r = launch_rmsnorm_rows(x, L.ffn_norm, S, d, eps, h16, m->stream);
+        if (r != hipSuccess) break;
+        g = GemmArgs{};
+        g.A = h16; g.lda = d;
+        g.B = static_cast<const uint16_t*>(L.wgu.data); g.ldb = d;
+        g.C = mid16; g.ldc = F; g.M = S; g.N = F; g.K = d; g.up_rows = F;
+        r = launch_gemm(g, GEMM_SWIGLU_F16, m->stream);
+        if (r != hipSuccess) break;
+        g = GemmArgs{};
+        g.A = mid16; g.lda = F;
+        g.B = static_cast<const uint16_t*>(L.wd.data); g.ldb = F;
+        g.C = x; g.ldc = d; g.M = S; g.N = d; g.K = F;
+        r = launch_gemm(g, GEMM_ADD_F32, m->stream);
+    }
+    if (r == hipSuccess && logits)
+        r = launch_matvec(m->out, MV_STORE, x + size_t(S - 1) * d, m->out_norm, eps, c.vocab, 0,
+                          logits, m->stream);
+    if (r != hipSuccess) {
+        (void)hipGetLastError();
+        return set_err(m, DF_ERR_DEVICE, fmt("bulk prefill launch failed: %s", hipGetErrorString(r)));
+    }
+    m->kv_len = p0 + S;
+    return DF_OK;
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -839,8 +930,14 @@ df_status df_forward(df_model* m, const int32_t* tokens, int32_t n, float* logit
     collect_event_time(m);
     (void)hipEventRecord(m->ev0, m->stream);
     df_status st = DF_OK;
-    for (int32_t i = 0; i < n && st == DF_OK; ++i)
-        st = decode_one(m, tokens[i], i == n - 1 ? logits_dev : nullptr);
+    if (n > 1 && bulk_supported(m)) {
+        st = prefill(m, tokens, n, logits_dev);
+    } else {
+        // One token, or block weights the matrix-core path does not take
+        // (f32, 8-bit): the decode kernels, one position after another.
+        for (int32_t i = 0; i < n && st == DF_OK; ++i)
+            st = decode_one(m, tokens[i], i == n - 1 ? logits_dev : nullptr);
+    }
     (void)hipEventRecord(m->ev1, m->stream);
     m->ev_kind = n == 1 ? 1 : 2;
     if (st == DF_OK) m->n_forward++;

@@ -1,0 +1,127 @@
+"""Bulk prefill parity on the GPU (df_forward with n > 1, matrix-core path).
+
+Bulk prefill must give the same result as token-by-token within epsilon
+(page "Execution contract", "Forward phase"). The GEMM operands are rounded
+to f16, so the bar is rel-L2 <= 5e-3 on logits against the oracle, with the
+greedy token identical unless the oracle's top-2 gap is a near-tie. Cases
+span several 128-row tiles with a ragged tail, prefill on top of an
+existing cache (absolute positions), and the decode steps that follow.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from parity import check_steps, first_argmax, near_tie, rel_l2
+
+pytestmark = pytest.mark.gpu
+TOL = 5e-3
+
+
+@pytest.fixture(scope="module")
+def dfa():
+    import torch
+    assert torch.cuda.is_available()
+    import decoder_forward_amd as dfa
+    dfa.lib()
+    return dfa
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def oracle_run(cfg, W, chunks, max_ctx):
+    """Feeds the chunks token by token; logits after the last token of each."""
+    m = oracle.Model(cfg, W, max_ctx=max_ctx)
+    out = []
+    for ch in chunks:
+        for t in ch[:-1]:
+            m.forward([t], logits=False)
+        out.append(m.forward([ch[-1]]))
+    return m, out
+
+
+def check_logits(got, ref, what):
+    e = rel_l2(got, ref)
+    say(f"  {what}: rel-L2 {e:.2e}")
+    assert e <= TOL, f"{what}: rel-L2 {e:.3e}"
+    if first_argmax(got) != first_argmax(ref):
+        assert near_tie(ref, TOL), f"{what}: argmax differs off a near-tie"
+
+
+def check_kv(m, om, cfg, n, tol=TOL):
+    for layer in range(cfg["n_layers"]):
+        for which in (0, 1):
+            a = m.read_kv(layer, which, 0, n)
+            b = om.kv_read(layer, which, 0, n)
+            err = np.linalg.norm(a - b) / np.linalg.norm(b)
+            assert err <= tol, (layer, which, err)
+
+
+@pytest.mark.parametrize("arch", ["qwen3", "llama"])
+def test_tiny_f16_bulk_then_bulk_then_decode(dfa, arch):
+    say(f"[tiny {arch} f16] bulk 40 + bulk 7 (on top) + 6 decode steps")
+    cfg = synth.config("tiny", arch=arch, wdtype="f16", max_ctx=64)
+    W = synth.make_weights(cfg)
+    toks = synth.make_prompt(cfg, 47)
+    om, ref = oracle_run(cfg, W, [toks[:40], toks[40:]], 64)
+    m = dfa.Model(cfg, W)
+    g1 = m.forward(toks[:40]).cpu().numpy().copy()
+    g2 = m.forward(toks[40:]).cpu().numpy().copy()
+    assert m.kv_len == 47
+    check_logits(g1, ref[0], "after 40")
+    check_logits(g2, ref[1], "after 47")
+    check_kv(m, om, cfg, 47)
+    nxt = first_argmax(ref[1])
+    for i in range(6):
+        r = om.forward([nxt])
+        g = m.forward([nxt]).cpu().numpy()
+        check_logits(g, r, f"decode {i}")
+        nxt = first_argmax(r)
+    m.close()
+
+
+@pytest.mark.parametrize("name,S,vocab", [("qwen3_8b", 300, None), ("llama_8b", 200, 4096),
+                                          ("qwen3_0p6b", 137, None)])
+def test_one_layer_real_shape_bulk(dfa, name, S, vocab):
+    over = dict(n_layers=1, max_ctx=S + 8)
+    if vocab:
+        over["vocab"] = vocab
+    cfg = synth.config(name, **over)
+    say(f"[{name} 1 layer] bulk prefill of {S} rows (ragged tiles) vs the oracle")
+    W = synth.make_weights(cfg)
+    toks = synth.make_prompt(cfg, S)
+    om, ref = oracle_run(cfg, W, [toks], S + 8)
+    m = dfa.Model(cfg, W)
+    got = m.forward(toks).cpu().numpy()
+    check_logits(got, ref[0], f"{name} S={S}")
+    check_kv(m, om, cfg, S)
+    # one decode step on top of the bulk-filled cache
+    t = first_argmax(ref[0])
+    check_logits(m.forward([t]).cpu().numpy(), om.forward([t]), "next decode step")
+    m.close()
+
+
+def test_full_depth_bulk_equals_token_by_token(dfa):
+    cfg = synth.config("qwen3_0p6b")
+    S = 256
+    say(f"[qwen3-0.6B shape, 28 layers] GPU bulk {S} vs GPU token-by-token and the oracle")
+    W = synth.make_weights(cfg)
+    toks = synth.make_prompt(cfg, S)
+    a = dfa.Model(cfg, W, max_ctx=S + 8)
+    la = a.forward(toks).cpu().numpy()
+    b = dfa.Model(cfg, W, max_ctx=S + 8)
+    for t in toks[:-1]:
+        b.forward([t], logits=False)
+    lb = b.forward([toks[-1]]).cpu().numpy()
+    check_logits(la, lb, "bulk vs token-by-token (GPU)")
+    om = oracle.Model(cfg, W, max_ctx=S + 8)
+    for t in toks[:-1]:
+        om.forward([t], logits=False)
+    ref = om.forward([toks[-1]])
+    check_logits(la, ref, "bulk vs oracle")
+    check_logits(lb, ref, "token-by-token vs oracle")
+    assert rel_l2(lb, ref) <= 1e-4
+    a.close()
+    b.close()
