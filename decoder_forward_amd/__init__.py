@@ -34,9 +34,9 @@ DF_F32, DF_F16, DF_Q8_32 = 0, 1, 2
 EXPORTS = ("df_load", "df_forward", "df_generate", "df_reset_kv_cache",
            "df_free", "df_last_error", "df_get_timings", "df_kv_length",
            "df_argmax", "df_read_kv", "df_write_kv", "df_stream",
-           "df_profile", "df_profile_read")
+           "df_profile", "df_profile_read", "df_time_kernel")
 KERNELS = {"embed": 0, "qkv": 1, "attn": 2, "o": 3, "gate_up": 4, "down": 5,
-           "logits": 6, "argmax": 7}
+           "logits": 6, "argmax": 7, "attn_merge": 8}
 
 
 class DecFwdError(RuntimeError):
@@ -104,6 +104,7 @@ def lib() -> C.CDLL:
     L.df_stream.restype = vp
     L.df_profile.argtypes = [vp, i32, i32]
     L.df_profile_read.argtypes = [vp, i32, P(C.c_int64), P(C.c_double)]
+    L.df_time_kernel.argtypes = [vp, i32, i32, P(C.c_double)]
     for name in EXPORTS:
         if name not in ("df_free", "df_last_error", "df_stream"):
             getattr(L, name).restype = i32
@@ -235,6 +236,13 @@ def df_stream(h) -> int:
 
 def df_profile(h, kernel: str, enable: bool = True) -> None:
     _check(lib().df_profile(h, KERNELS[kernel], 1 if enable else 0), h)
+
+
+def df_time_kernel(h, kernel: str, reps: int = 8) -> float:
+    """Mean microseconds of one launch of a kernel class, back-to-back replay."""
+    us = C.c_double()
+    _check(lib().df_time_kernel(h, KERNELS[kernel], reps, C.byref(us)), h)
+    return us.value
 
 
 def df_profile_read(h, kernel: str):

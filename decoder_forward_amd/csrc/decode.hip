@@ -405,7 +405,7 @@ hipError_t launch_mv_t(const Weight& W, const float* x, const float* nw,
     const int NR = MODE == MV_SWIGLU ? 2 : 1;
     const size_t lds = size_t(L.K) * sizeof(float) +
                        (S > 1 ? size_t(upb * S * NR) * sizeof(float) : 0);
-    hipLaunchKernelGGL((matvec_kernel<WT, MODE, NORM>), dim3(unsigned(blocks)),
+    DFK_LAUNCH((matvec_kernel<WT, MODE, NORM>), dim3(unsigned(blocks)),
                        dim3(threads), lds, s, W.data, W.scales, L, x, nw, eps, out);
     return hipGetLastError();
 }
@@ -904,10 +904,10 @@ hipError_t launch_embed(const Weight& E, const int* tokens_dev,
                         hipStream_t s)
 {
     if (E.dtype == W_F32)
-        hipLaunchKernelGGL(embed_kernel<W_F32>, dim3(n_rows), dim3(256), 0, s,
+        DFK_LAUNCH(embed_kernel<W_F32>, dim3(n_rows), dim3(256), 0, s,
                            E.data, E.cols, tokens_dev, state_tok, x);
     else
-        hipLaunchKernelGGL(embed_kernel<W_F16>, dim3(n_rows), dim3(256), 0, s,
+        DFK_LAUNCH(embed_kernel<W_F16>, dim3(n_rows), dim3(256), 0, s,
                            E.data, E.cols, tokens_dev, state_tok, x);
     return hipGetLastError();
 }
@@ -916,10 +916,10 @@ template <int HD>
 hipError_t launch_attn_hd(const AttnDecodeArgs& a, dim3 grid, hipStream_t s)
 {
     switch (a.n_heads / a.n_kv) {
-    case 1: hipLaunchKernelGGL((attn_decode_kernel<HD, 1>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((attn_decode_kernel<HD, 2>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((attn_decode_kernel<HD, 4>), grid, dim3(256), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((attn_decode_kernel<HD, 8>), grid, dim3(256), 0, s, a); break;
+    case 1: DFK_LAUNCH((attn_decode_kernel<HD, 1>), grid, dim3(256), 0, s, a); break;
+    case 2: DFK_LAUNCH((attn_decode_kernel<HD, 2>), grid, dim3(256), 0, s, a); break;
+    case 4: DFK_LAUNCH((attn_decode_kernel<HD, 4>), grid, dim3(256), 0, s, a); break;
+    case 8: DFK_LAUNCH((attn_decode_kernel<HD, 8>), grid, dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -941,10 +941,10 @@ hipError_t launch_attn_combine(const AttnDecodeArgs& a, hipStream_t s)
 {
     const dim3 grid(a.n_heads);
     switch (a.head_dim) {
-    case 16: hipLaunchKernelGGL(attn_combine_kernel<16>, grid, dim3(64), 0, s, a); break;
-    case 32: hipLaunchKernelGGL(attn_combine_kernel<32>, grid, dim3(128), 0, s, a); break;
-    case 64: hipLaunchKernelGGL(attn_combine_kernel<64>, grid, dim3(256), 0, s, a); break;
-    case 128: hipLaunchKernelGGL(attn_combine_kernel<128>, grid, dim3(512), 0, s, a); break;
+    case 16: DFK_LAUNCH(attn_combine_kernel<16>, grid, dim3(64), 0, s, a); break;
+    case 32: DFK_LAUNCH(attn_combine_kernel<32>, grid, dim3(128), 0, s, a); break;
+    case 64: DFK_LAUNCH(attn_combine_kernel<64>, grid, dim3(256), 0, s, a); break;
+    case 128: DFK_LAUNCH(attn_combine_kernel<128>, grid, dim3(512), 0, s, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -956,7 +956,7 @@ hipError_t launch_argmax(const float* v, int n, DevState* st, int* out_dev,
     int blocks = (n + 1023) / 1024;
     if (blocks > 256) blocks = 256;
     if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL(argmax_kernel, dim3(blocks), dim3(256), 0, s, v, n, st,
+    DFK_LAUNCH(argmax_kernel, dim3(blocks), dim3(256), 0, s, v, n, st,
                        out_dev, advance, gen_out);
     return hipGetLastError();
 }
@@ -964,7 +964,7 @@ hipError_t launch_argmax(const float* v, int n, DevState* st, int* out_dev,
 hipError_t launch_set_state(DevState* st, int pos, int tok, int step,
                             hipStream_t s)
 {
-    hipLaunchKernelGGL(set_state_kernel, dim3(1), dim3(64), 0, s, st, pos, tok, step);
+    DFK_LAUNCH(set_state_kernel, dim3(1), dim3(64), 0, s, st, pos, tok, step);
     return hipGetLastError();
 }
 
@@ -974,7 +974,7 @@ hipError_t launch_to_f32(const void* src, int src_dtype, int64_t n, float* dst,
     if (n <= 0) return hipSuccess;
     int64_t blocks = (n + 255) / 256;
     if (blocks > 4096) blocks = 4096;
-    hipLaunchKernelGGL(to_f32_kernel, dim3(unsigned(blocks)), dim3(256), 0, s,
+    DFK_LAUNCH(to_f32_kernel, dim3(unsigned(blocks)), dim3(256), 0, s,
                        src, src_dtype, n, dst);
     return hipGetLastError();
 }
@@ -986,7 +986,7 @@ hipError_t launch_q8_split(const uint8_t* blocks, int64_t rows, int64_t cols,
     if (nb <= 0) return hipSuccess;
     int64_t g = (nb + 255) / 256;
     if (g > 8192) g = 8192;
-    hipLaunchKernelGGL(q8_split_kernel, dim3(unsigned(g)), dim3(256), 0, s,
+    DFK_LAUNCH(q8_split_kernel, dim3(unsigned(g)), dim3(256), 0, s,
                        blocks, nb, values, scales);
     return hipGetLastError();
 }

@@ -2,11 +2,32 @@
 // C++). Internal to the library; the public surface is include/decfwd.h.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
 
 namespace dfk {
+
+// Events that the next launch stamps with its own start and end (set by the
+// runtime around a profiled launch; both null otherwise). The stamps come
+// from the dispatch itself, so they measure the kernel without the cost of
+// separate event records.
+struct LaunchTiming {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+LaunchTiming& launch_timing();
+
+#define DFK_LAUNCH(kernel, grid, block, lds, stream, ...)                                      \
+    do {                                                                                      \
+        ::dfk::LaunchTiming& lt_ = ::dfk::launch_timing();                                    \
+        if (lt_.start)                                                                        \
+            hipExtLaunchKernelGGL(kernel, grid, block, lds, stream, lt_.start, lt_.stop, 0u,  \
+                                  __VA_ARGS__);                                               \
+        else                                                                                  \
+            hipLaunchKernelGGL(kernel, grid, block, lds, stream, __VA_ARGS__);                \
+    } while (0)
 
 enum WType { W_F32 = 0, W_F16 = 1, W_Q8 = 2 };
 

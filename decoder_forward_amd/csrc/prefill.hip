@@ -429,10 +429,10 @@ hipError_t launch_attn_prefill_hd(const AttnPrefillArgs& a, hipStream_t s)
 {
     const dim3 grid((a.S + 15) / 16, a.n_kv);
     switch (a.n_heads / a.n_kv) {
-    case 1: hipLaunchKernelGGL((attn_prefill_kernel<HD, 1>), grid, dim3(64), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((attn_prefill_kernel<HD, 2>), grid, dim3(128), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((attn_prefill_kernel<HD, 4>), grid, dim3(256), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((attn_prefill_kernel<HD, 8>), grid, dim3(512), 0, s, a); break;
+    case 1: DFK_LAUNCH((attn_prefill_kernel<HD, 1>), grid, dim3(64), 0, s, a); break;
+    case 2: DFK_LAUNCH((attn_prefill_kernel<HD, 2>), grid, dim3(128), 0, s, a); break;
+    case 4: DFK_LAUNCH((attn_prefill_kernel<HD, 4>), grid, dim3(256), 0, s, a); break;
+    case 8: DFK_LAUNCH((attn_prefill_kernel<HD, 8>), grid, dim3(512), 0, s, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -444,7 +444,7 @@ hipError_t launch_rmsnorm_rows(const float* x, const float* w, int rows, int d, 
                                uint16_t* out, hipStream_t s)
 {
     if (rows <= 0) return hipSuccess;
-    hipLaunchKernelGGL(rmsnorm_rows_kernel, dim3(rows), dim3(256), 0, s, x, w, d, eps, out);
+    DFK_LAUNCH(rmsnorm_rows_kernel, dim3(rows), dim3(256), 0, s, x, w, d, eps, out);
     return hipGetLastError();
 }
 
@@ -454,10 +454,10 @@ hipError_t launch_gemm(const GemmArgs& g, int mode, hipStream_t s)
     const int ncols = mode == GEMM_SWIGLU_F16 ? GBN / 2 : GBN;
     const int blocks = ((g.N + ncols - 1) / ncols) * ((g.M + GBM - 1) / GBM);
     switch (mode) {
-    case GEMM_STORE_F32: hipLaunchKernelGGL(gemm_kernel<GEMM_STORE_F32>, dim3(blocks), dim3(256), 0, s, g); break;
-    case GEMM_ADD_F32: hipLaunchKernelGGL(gemm_kernel<GEMM_ADD_F32>, dim3(blocks), dim3(256), 0, s, g); break;
-    case GEMM_STORE_F16: hipLaunchKernelGGL(gemm_kernel<GEMM_STORE_F16>, dim3(blocks), dim3(256), 0, s, g); break;
-    case GEMM_SWIGLU_F16: hipLaunchKernelGGL(gemm_kernel<GEMM_SWIGLU_F16>, dim3(blocks), dim3(256), 0, s, g); break;
+    case GEMM_STORE_F32: DFK_LAUNCH(gemm_kernel<GEMM_STORE_F32>, dim3(blocks), dim3(256), 0, s, g); break;
+    case GEMM_ADD_F32: DFK_LAUNCH(gemm_kernel<GEMM_ADD_F32>, dim3(blocks), dim3(256), 0, s, g); break;
+    case GEMM_STORE_F16: DFK_LAUNCH(gemm_kernel<GEMM_STORE_F16>, dim3(blocks), dim3(256), 0, s, g); break;
+    case GEMM_SWIGLU_F16: DFK_LAUNCH(gemm_kernel<GEMM_SWIGLU_F16>, dim3(blocks), dim3(256), 0, s, g); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -466,7 +466,7 @@ hipError_t launch_gemm(const GemmArgs& g, int mode, hipStream_t s)
 hipError_t launch_qk_post_rows(const QkPostArgs& a, hipStream_t s)
 {
     if (a.S <= 0) return hipSuccess;
-    hipLaunchKernelGGL(qk_post_rows_kernel, dim3(a.S, a.n_heads + a.n_kv), dim3(64),
+    DFK_LAUNCH(qk_post_rows_kernel, dim3(a.S, a.n_heads + a.n_kv), dim3(64),
                        size_t(a.head_dim) * sizeof(float), s, a);
     return hipGetLastError();
 }

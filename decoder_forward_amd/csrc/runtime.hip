@@ -25,6 +25,14 @@
 
 using namespace dfk;
 
+namespace dfk {
+LaunchTiming& launch_timing()
+{
+    thread_local LaunchTiming t;
+    return t;
+}
+}  // namespace dfk
+
 namespace {
 
 thread_local std::string g_load_error;
@@ -581,10 +589,11 @@ bool step_buffers(df_model* m, StepBufs* b, Fail* e)
     return b->x && b->qkv && b->att && b->mid;
 }
 
-// Event pair around one launch when its class is being profiled.
+// Start / end stamps of one launch when its class is being profiled: the
+// scope hands an event pair to the launch, which the dispatch stamps.
 struct ProfScope {
     df_model* m;
-    hipEvent_t end = nullptr;
+    bool on = false;
     ProfScope(df_model* mm, int kernel) : m(mm)
     {
         if (m->prof_kernel != kernel) return;
@@ -597,39 +606,31 @@ struct ProfScope {
             m->prof_events.emplace_back(a, b);
         }
         auto& ev = m->prof_events[m->prof_used++];
-        (void)hipEventRecord(ev.first, m->stream);
-        end = ev.second;
+        launch_timing() = LaunchTiming{ev.first, ev.second};
+        on = true;
     }
     ~ProfScope()
     {
-        if (end) (void)hipEventRecord(end, m->stream);
+        if (on) launch_timing() = LaunchTiming{};
     }
 };
 
-hipError_t launch_step(df_model* m, const StepBufs& b, int grid_splits, float* logits)
+// The launches of one kernel class for layer l of a decode step (layer is
+// ignored for embed / logits / argmax).
+hipError_t launch_class(df_model* m, const StepBufs& b, int kernel, int l, int grid_splits,
+                        float* logits)
 {
     const df_config& c = m->cfg;
     const float eps = float(c.rms_eps);
     const int hd = c.head_dim;
     const int64_t qd = int64_t(c.n_heads) * hd, kvd = int64_t(c.n_kv_heads) * hd;
     const size_t kv_layer = size_t(c.n_kv_heads) * size_t(c.max_ctx) * size_t(hd);
-    hipError_t r;
-    {
-        ProfScope ps(m, DF_K_EMBED);
-        r = launch_embed(m->embd, nullptr, &m->state->tok, 1, b.x, m->stream);
-    }
-    if (r != hipSuccess) return r;
-    for (int l = 0; l < c.n_layers; ++l) {
-        const Layer& L = m->layers[size_t(l)];
-        {
-            ProfScope ps(m, DF_K_QKV);
-            r = launch_matvec(L.wqkv, MV_STORE, b.x, L.attn_norm, eps, qd + 2 * kvd, 0, b.qkv, m->stream);
-        }
-        if (r != hipSuccess) return r;
-        AttnDecodeArgs a{};
+    const Layer* L = (l >= 0 && l < c.n_layers) ? &m->layers[size_t(l)] : nullptr;
+    AttnDecodeArgs a{};
+    if (L) {
         a.qkv = b.qkv;
-        a.q_norm = L.q_norm;
-        a.k_norm = L.k_norm;
+        a.q_norm = L->q_norm;
+        a.k_norm = L->k_norm;
         a.eps = eps;
         a.cos_t = m->cos_t;
         a.sin_t = m->sin_t;
@@ -643,32 +644,39 @@ hipError_t launch_step(df_model* m, const StepBufs& b, int grid_splits, float* l
         a.part = m->attn_part;
         a.out = b.att;
         a.grid_splits = grid_splits;
-        {
-            ProfScope ps(m, DF_K_ATTN);
-            r = launch_attn_decode(a, m->stream);
-            if (r == hipSuccess) r = launch_attn_combine(a, m->stream);
-        }
-        if (r != hipSuccess) return r;
-        {
-            ProfScope ps(m, DF_K_O);
-            r = launch_matvec(L.wo, MV_RESID, b.att, nullptr, eps, c.d_model, 0, b.x, m->stream);
-        }
-        if (r != hipSuccess) return r;
-        {
-            ProfScope ps(m, DF_K_GATE_UP);
-            r = launch_matvec(L.wgu, MV_SWIGLU, b.x, L.ffn_norm, eps, c.ffn_dim, c.ffn_dim, b.mid,
-                              m->stream);
-        }
-        if (r != hipSuccess) return r;
-        {
-            ProfScope ps(m, DF_K_DOWN);
-            r = launch_matvec(L.wd, MV_RESID, b.mid, nullptr, eps, c.d_model, 0, b.x, m->stream);
-        }
-        if (r != hipSuccess) return r;
     }
-    if (logits) {
+    switch (kernel) {
+    case DF_K_EMBED: return launch_embed(m->embd, nullptr, &m->state->tok, 1, b.x, m->stream);
+    case DF_K_QKV: return launch_matvec(L->wqkv, MV_STORE, b.x, L->attn_norm, eps, qd + 2 * kvd, 0, b.qkv, m->stream);
+    case DF_K_ATTN: return launch_attn_decode(a, m->stream);
+    case DF_K_ATTN_MERGE: return launch_attn_combine(a, m->stream);
+    case DF_K_O: return launch_matvec(L->wo, MV_RESID, b.att, nullptr, eps, c.d_model, 0, b.x, m->stream);
+    case DF_K_GATE_UP:
+        return launch_matvec(L->wgu, MV_SWIGLU, b.x, L->ffn_norm, eps, c.ffn_dim, c.ffn_dim, b.mid, m->stream);
+    case DF_K_DOWN: return launch_matvec(L->wd, MV_RESID, b.mid, nullptr, eps, c.d_model, 0, b.x, m->stream);
+    case DF_K_LOGITS: return launch_matvec(m->out, MV_STORE, b.x, m->out_norm, eps, c.vocab, 0, logits, m->stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_step(df_model* m, const StepBufs& b, int grid_splits, float* logits)
+{
+    static const int per_layer[] = {DF_K_QKV, DF_K_ATTN, DF_K_ATTN_MERGE, DF_K_O, DF_K_GATE_UP, DF_K_DOWN};
+    hipError_t r;
+    {
+        ProfScope ps(m, DF_K_EMBED);
+        r = launch_class(m, b, DF_K_EMBED, -1, grid_splits, logits);
+    }
+    for (int l = 0; l < m->cfg.n_layers && r == hipSuccess; ++l) {
+        for (int k : per_layer) {
+            ProfScope ps(m, k);
+            r = launch_class(m, b, k, l, grid_splits, logits);
+            if (r != hipSuccess) break;
+        }
+    }
+    if (r == hipSuccess && logits) {
         ProfScope ps(m, DF_K_LOGITS);
-        r = launch_matvec(m->out, MV_STORE, b.x, m->out_norm, eps, c.vocab, 0, logits, m->stream);
+        r = launch_class(m, b, DF_K_LOGITS, -1, grid_splits, logits);
     }
     return r;
 }
@@ -1139,6 +1147,46 @@ df_status df_write_kv(df_model* m, int32_t layer, int32_t which, int32_t pos0, i
 void* df_stream(const df_model* m)
 {
     return m ? static_cast<void*>(m->stream) : nullptr;
+}
+
+df_status df_time_kernel(df_model* m, int32_t kernel, int32_t reps, double* mean_us)
+{
+    if (!m || !mean_us || reps <= 0 || kernel < 0 || kernel >= DF_K_COUNT)
+        return DF_ERR_INVALID_ARGUMENT;
+    BusyGuard guard(m);
+    if (!guard.ok) return DF_ERR_BUSY;
+    if (m->pool.bytes() == 0)
+        return set_err(m, DF_ERR_INVALID_ARGUMENT, "df_time_kernel: run a decode step first");
+    (void)hipSetDevice(m->device);
+    Fail e{DF_OK, ""};
+    m->pool.reset();
+    StepBufs b{};
+    if (!step_buffers(m, &b, &e)) return set_err(m, e.code, e.msg);
+    float* lg = static_cast<float*>(m->pool.alloc(size_t(m->cfg.vocab) * 4, USAGE_DEVICE, &e));
+    if (!lg) return set_err(m, e.code, e.msg);
+    const bool per_layer = kernel != DF_K_EMBED && kernel != DF_K_LOGITS && kernel != DF_K_ARGMAX;
+    const int nl = per_layer ? m->cfg.n_layers : 1;
+    if (nl == 0) return set_err(m, DF_ERR_INVALID_ARGUMENT, "df_time_kernel: no layers");
+    const int splits = attn_splits(m->kv_len < m->cfg.max_ctx ? m->kv_len : m->cfg.max_ctx - 1);
+    hipError_t r = launch_set_state(m->state, m->kv_len < m->cfg.max_ctx ? m->kv_len : m->cfg.max_ctx - 1,
+                                    0, 0, m->stream);
+    if (r == hipSuccess) r = hipEventRecord(m->ev0, m->stream);
+    for (int rep = 0; rep < reps && r == hipSuccess; ++rep)
+        for (int l = 0; l < nl && r == hipSuccess; ++l)
+            r = kernel == DF_K_ARGMAX
+                    ? launch_argmax(lg, m->cfg.vocab, m->state, m->argmax_out, 0, nullptr, m->stream)
+                    : launch_class(m, b, kernel, l, splits, lg);
+    if (r == hipSuccess) r = hipEventRecord(m->ev1, m->stream);
+    if (r == hipSuccess) r = hipEventSynchronize(m->ev1);
+    float ms = 0.f;
+    if (r == hipSuccess) r = hipEventElapsedTime(&ms, m->ev0, m->ev1);
+    if (r != hipSuccess) {
+        (void)hipGetLastError();
+        return set_err(m, DF_ERR_DEVICE, fmt("df_time_kernel: %s", hipGetErrorString(r)));
+    }
+    m->ev_kind = 0;
+    *mean_us = double(ms) * 1e3 / double(reps * nl);
+    return DF_OK;
 }
 
 df_status df_profile(df_model* m, int32_t kernel, int32_t enable)

@@ -190,23 +190,34 @@ void* df_stream(const df_model* m);
  * "Observability": a timing breakdown of every forward). */
 #define DF_K_EMBED 0        /* token row gather */
 #define DF_K_QKV 1          /* rms_norm + q/k/v matvec */
-#define DF_K_ATTN 2         /* norm_heads + rope + KV append + attention */
+#define DF_K_ATTN 2         /* norm_heads + rope + KV append + split attention */
 #define DF_K_O 3            /* o matvec + residual add */
 #define DF_K_GATE_UP 4      /* rms_norm + gate/up matvec + silu * up */
 #define DF_K_DOWN 5         /* down matvec + residual add */
 #define DF_K_LOGITS 6       /* final rms_norm + logits matvec */
 #define DF_K_ARGMAX 7       /* greedy token */
-#define DF_K_COUNT 8
+#define DF_K_ATTN_MERGE 8   /* merge of the attention splits */
+#define DF_K_COUNT 9
 
-/* Time every launch of one kernel class with a HIP event pair on the
- * model's stream (enable = 1), or stop (enable = 0). Timing costs two event
- * records per launch of that class only. */
+/* Time every launch of one kernel class (enable = 1) with start / end
+ * stamps taken by the kernel dispatch itself, or stop (enable = 0). The
+ * device-resident step graph is not used while a class is profiled. */
 df_status df_profile(df_model* m, int32_t kernel, int32_t enable);
 
 /* Synchronise, then report the launches timed since the last read and their
  * summed device time in milliseconds; clears the record. */
 df_status df_profile_read(df_model* m, int32_t kernel, int64_t* launches,
                           double* total_ms);
+
+/* Mean device time of one launch of a kernel class in the decode step's
+ * launch configuration: the class's launches of one step (one per layer, or
+ * one for embed / logits / argmax) are replayed `reps` times back to back on
+ * the model's stream between one pair of HIP events, with no other work in
+ * between. Needs a prior decode step (its buffers are reused; their contents
+ * and the cache row at kv_len are overwritten, so the next df_forward /
+ * df_generate starts from its own inputs as always). Synchronises. */
+df_status df_time_kernel(df_model* m, int32_t kernel, int32_t reps,
+                         double* mean_us);
 
 #ifdef __cplusplus
 }
