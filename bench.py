@@ -128,6 +128,8 @@ def main():
                     help="build the context by bulk prefill (default) or by writing "
                          "synthetic KV rows")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--persistent-step", action="store_true",
+                    help="one persistent launch per step instead of one per operation class")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -149,7 +151,7 @@ def main():
     log(f"[bench] {args.workload}: generating weights on the GPU")
     W = synth.make_weights_device(cfg)
     torch.cuda.synchronize()
-    m = dfa.Model(cfg, W, max_ctx=max_ctx)
+    m = dfa.Model(cfg, W, max_ctx=max_ctx, persistent_step=args.persistent_step)
     del W
     torch.cuda.empty_cache()
     log(f"[bench] loaded in {m.timings()['load_ms']:.0f} ms")

@@ -36,7 +36,9 @@ EXPORTS = ("df_load", "df_forward", "df_generate", "df_reset_kv_cache",
            "df_argmax", "df_read_kv", "df_write_kv", "df_stream",
            "df_profile", "df_profile_read", "df_time_kernel")
 KERNELS = {"embed": 0, "qkv": 1, "attn": 2, "o": 3, "gate_up": 4, "down": 5,
-           "logits": 6, "argmax": 7, "attn_merge": 8}
+           "logits": 6, "argmax": 7, "attn_merge": 8, "step": 9}
+# df_options.flags: every decode step as one persistent launch (opt-in).
+DF_FLAG_PERSISTENT_STEP = 1
 
 
 class DecFwdError(RuntimeError):
@@ -71,7 +73,8 @@ class df_timings(C.Structure):
     _fields_ = [("load_ms", C.c_double), ("last_prefill_ms", C.c_double),
                 ("last_step_ms", C.c_double), ("n_forward", C.c_int64),
                 ("weight_bytes", C.c_int64), ("kv_bytes", C.c_int64),
-                ("pool_bytes", C.c_int64)]
+                ("pool_bytes", C.c_int64), ("persistent_step", C.c_int32),
+                ("step_blocks", C.c_int32)]
 
 
 _lib = None
@@ -154,7 +157,7 @@ def _tensor_entry(name: str, a, keep: list) -> df_tensor:
 
 
 def df_load(cfg: dict, weights: dict, stream=None, device: int = 0,
-            max_ctx: int | None = None):
+            max_ctx: int | None = None, flags: int = 0):
     """Load a model; returns an opaque handle (c_void_p)."""
     keep: list = []
     names = list(weights)
@@ -162,7 +165,7 @@ def df_load(cfg: dict, weights: dict, stream=None, device: int = 0,
     for i, n in enumerate(names):
         arr[i] = _tensor_entry(n, weights[n], keep)
     c = make_config(cfg, max_ctx)
-    opt = df_options(stream, device, 0)
+    opt = df_options(stream, device, flags)
     h = C.c_void_p()
     rc = lib().df_load(C.byref(c), arr, len(names), C.byref(opt), C.byref(h))
     _check(rc, None)
@@ -261,7 +264,7 @@ class Model:
     code before and after sees the results in order."""
 
     def __init__(self, cfg: dict, weights: dict, max_ctx: int | None = None,
-                 device: int = 0):
+                 device: int = 0, persistent_step: bool = False):
         import torch
         self._torch = torch
         self.cfg = dict(cfg)
@@ -271,7 +274,8 @@ class Model:
         self.stream = torch.cuda.Stream(self.device)
         self.h = None
         self.h = df_load(self.cfg, weights, stream=self.stream.cuda_stream,
-                         device=device)
+                         device=device,
+                         flags=DF_FLAG_PERSISTENT_STEP if persistent_step else 0)
         self.logits = torch.empty(self.cfg["vocab"], dtype=torch.float32,
                                   device=self.device)
 

@@ -1,0 +1,339 @@
+// attn_core.h — decode attention for one (KV head, row range) item, shared
+// by the separate attention kernel and the persistent step kernel.
+//
+// Page "Local inference and architectures", "The format" (the attention
+// step of the step list): for each query head j of KV head g,
+//   s_t = q_j . k_t / sqrt(hd),  out_j = sum_t softmax(s)_t v_t
+// over the cache rows t = 0 .. p, where row p is this step's k (after
+// norm_heads and rope) and v, appended to the cache by the item that covers
+// it. q and k get norm_heads (qwen3) and rope at position p first.
+//
+// Work layout. A block of NW waves walks its rows in sweeps of NW*4*ITER
+// rows: wave w takes rows w*4*ITER .. w*4*ITER + 4*ITER - 1 of a sweep, 16
+// lanes per row (4 rows per wave instruction, hd/16 dims per lane), so a K or
+// V row is one contiguous 16-lane load. Each wave keeps its own online
+// softmax (running max m, running sum l, accumulator) across sweeps: no
+// block-wide synchronisation inside the row loop. With DBUF the next sweep's
+// rows are loaded while the current one is consumed (twice the registers).
+// At the end the waves' states meet in LDS and are merged with weights
+// exp(m_w - M) in wave order.
+//
+// Result: with `out` set (the item covers every row) the normalised output
+// of the G heads; otherwise the partial (sum_t e^{s_t - M} v_t, M, sum_t
+// e^{s_t - M}) per head, merged across items by attn_merge_group.
+#pragma once
+
+#include "device_common.h"
+
+namespace dfk {
+namespace dev {
+
+struct AttnItem {
+    const float* qkv;      // this step's q (all heads) | k | v
+    const float* q_norm;   // norm_heads weights (qwen3), null for llama
+    const float* k_norm;
+    float eps;
+    const float* cos_row;  // rope cos / sin at position p, hd/2 each
+    const float* sin_row;
+    float* kc;             // this KV head's cache rows [max_ctx][hd]
+    float* vc;
+    int qd, kvd;           // widths of q and of k (= v) inside qkv
+    int g;                 // KV head
+    int p;                 // position of this step's row
+    int pos0, pos1;        // rows [pos0, pos1) of the item; pos1 <= p + 1
+    float* out;            // [n_heads][hd], or null: write `part`
+    float* part;           // attn_part_stride floats: acc [G][hd], max [G], sum [G]
+};
+
+template <int HD, int G, int NW>
+constexpr int attn_core_lds_floats()
+{
+    return G * HD + 2 * HD + NW * G * HD + 2 * NW * G;
+}
+
+template <int N>
+__device__ inline void load_row_slice(const float* p, float (&v)[N])
+{
+    if constexpr (N % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < N; i += 4) {
+            const float4 x = load16f_nt(p + i);
+            v[i] = x.x; v[i + 1] = x.y; v[i + 2] = x.z; v[i + 3] = x.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) v[i] = *gmem(p + i);
+    }
+}
+
+template <int HD, int G, int NW, int ITER, bool DBUF, bool COH>
+__device__ void attn_core(const AttnItem& a, float* lds, int tid)
+{
+    constexpr int LPR = 16;
+    constexpr int RG = WAVE / LPR;               // rows per wave instruction
+    constexpr int DPL = HD / LPR;                // dims per lane
+    constexpr int SW = NW * RG * ITER;           // rows per sweep
+    constexpr int HALF = HD / 2;
+    float* qs = lds;                  // [G][HD]
+    float* knew = qs + G * HD;        // [HD]
+    float* vnew = knew + HD;          // [HD]
+    float* red = vnew + HD;           // [NW][G][HD]
+    float* sm = red + NW * G * HD;    // [NW][G]
+    float* sl = sm + NW * G;          // [NW][G]
+    const int lane = tid & (WAVE - 1);
+    const int w = tid >> 6;
+    const int rg = lane >> 4;
+    const int ds = (lane & (LPR - 1)) * DPL;
+    const int p = a.p;
+    const bool owner = a.pos1 == p + 1;
+    const int n_sweeps = (a.pos1 - a.pos0 + SW - 1) / SW;
+    const int lim = min(a.pos1, p);   // cache rows below lim are read from memory
+
+    auto row_of = [&](int s, int it) { return a.pos0 + s * SW + w * (RG * ITER) + it * RG + rg; };
+    float ka[ITER][DPL], va[ITER][DPL];
+    float kb[DBUF ? ITER : 1][DPL], vb[DBUF ? ITER : 1][DPL];
+    auto load = [&](int s, float (&kk)[ITER][DPL], float (&vv)[ITER][DPL]) {
+#pragma unroll
+        for (int it = 0; it < ITER; ++it) {
+            const int t = row_of(s, it);
+            if (t < lim) {
+                load_row_slice<DPL>(a.kc + int64_t(t) * HD + ds, kk[it]);
+                load_row_slice<DPL>(a.vc + int64_t(t) * HD + ds, vv[it]);
+            } else {
+#pragma unroll
+                for (int d = 0; d < DPL; ++d) { kk[it][d] = 0.f; vv[it][d] = 0.f; }
+            }
+        }
+    };
+    load(0, ka, va);
+
+    // q of the group's heads (and, for the owner, this step's k): one wave
+    // per vector, lane i < hd/2 holding the rope pair (i, i + hd/2);
+    // norm_heads, then rope, then into LDS.
+    const int nv = G + (owner ? 1 : 0);
+    for (int j = w; j < nv; j += NW) {
+        const float* src = a.qkv + (j < G ? (a.g * G + j) * HD : a.qd + a.g * HD);
+        float x0 = 0.f, x1 = 0.f;
+        if (lane < HALF) {
+            x0 = act_ld<COH>(src + lane);
+            x1 = act_ld<COH>(src + lane + HALF);
+        }
+        if (a.q_norm) {
+            const float ss = wave_sum(fmaf(x0, x0, x1 * x1));
+            const float r = 1.0f / sqrtf(ss / static_cast<float>(HD) + a.eps);
+            if (lane < HALF) {
+                const float* nw = j < G ? a.q_norm : a.k_norm;
+                x0 = *gmem(nw + lane) * (x0 * r);
+                x1 = *gmem(nw + lane + HALF) * (x1 * r);
+            }
+        }
+        if (lane < HALF) {
+            const float c = *gmem(a.cos_row + lane), s = *gmem(a.sin_row + lane);
+            const float y0 = fmaf(x0, c, -x1 * s);
+            const float y1 = fmaf(x0, s, x1 * c);
+            float* dst = j < G ? qs + j * HD : knew;
+            dst[lane] = y0;
+            dst[lane + HALF] = y1;
+            if (j == G) {  // append k at slot p
+                *gmem(a.kc + int64_t(p) * HD + lane) = y0;
+                *gmem(a.kc + int64_t(p) * HD + lane + HALF) = y1;
+            }
+        }
+    }
+    if (owner) {
+        for (int i = tid; i < HD; i += NW * WAVE) {
+            const float v = act_ld<COH>(a.qkv + a.qd + a.kvd + a.g * HD + i);
+            vnew[i] = v;
+            *gmem(a.vc + int64_t(p) * HD + i) = v;  // append v at slot p
+        }
+    }
+    __syncthreads();
+
+    float q[G][DPL], acc[G][DPL], m[G], l[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+#pragma unroll
+        for (int d = 0; d < DPL; ++d) {
+            q[j][d] = qs[j * HD + ds + d];
+            acc[j][d] = 0.f;
+        }
+        m[j] = -INFINITY;
+        l[j] = 0.f;
+    }
+    const float scale = 1.0f / sqrtf(static_cast<float>(HD));
+
+    auto consume = [&](int s, float (&kk)[ITER][DPL], float (&vv)[ITER][DPL]) {
+#pragma unroll
+        for (int it = 0; it < ITER; ++it) {
+            if (row_of(s, it) == p) {
+#pragma unroll
+                for (int d = 0; d < DPL; ++d) { kk[it][d] = knew[ds + d]; vv[it][d] = vnew[ds + d]; }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            float sc[ITER];
+            float mt = -INFINITY;
+#pragma unroll
+            for (int it = 0; it < ITER; ++it) {
+                float x = 0.f;
+#pragma unroll
+                for (int d = 0; d < DPL; ++d) x = fmaf(q[j][d], kk[it][d], x);
+                x = row16_sum(x);
+                sc[it] = row_of(s, it) < a.pos1 ? x * scale : -INFINITY;
+                mt = fmaxf(mt, sc[it]);
+            }
+            mt = fmaxf(fmaxf(lane_value(mt, 0), lane_value(mt, 16)),
+                       fmaxf(lane_value(mt, 32), lane_value(mt, 48)));
+            const float mn = fmaxf(m[j], mt);
+            const float resc = m[j] == -INFINITY ? 0.f : expf(m[j] - mn);
+            float ps = 0.f;
+#pragma unroll
+            for (int d = 0; d < DPL; ++d) acc[j][d] *= resc;
+#pragma unroll
+            for (int it = 0; it < ITER; ++it) {
+                const float pr = sc[it] == -INFINITY ? 0.f : expf(sc[it] - mn);
+                ps += pr;
+#pragma unroll
+                for (int d = 0; d < DPL; ++d) acc[j][d] = fmaf(pr, vv[it][d], acc[j][d]);
+            }
+            l[j] = fmaf(l[j], resc, ps);
+            m[j] = mn;
+        }
+    };
+    if constexpr (DBUF) {
+        for (int s = 0; s < n_sweeps; s += 2) {
+            if (s + 1 < n_sweeps) load(s + 1, kb, vb);
+            consume(s, ka, va);
+            if (s + 1 < n_sweeps) {
+                if (s + 2 < n_sweeps) load(s + 2, ka, va);
+                consume(s + 1, kb, vb);
+            }
+        }
+    } else {
+        for (int s = 0; s < n_sweeps; ++s) {
+            if (s > 0) load(s, ka, va);
+            consume(s, ka, va);
+        }
+    }
+
+    // The wave's four row groups, then the waves, in fixed order.
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+#pragma unroll
+        for (int d = 0; d < DPL; ++d) {
+            acc[j][d] += __shfl_xor(acc[j][d], 16, WAVE);
+            acc[j][d] += __shfl_xor(acc[j][d], 32, WAVE);
+        }
+        const float lw = (lane_value(l[j], 0) + lane_value(l[j], 16)) +
+                         (lane_value(l[j], 32) + lane_value(l[j], 48));
+        if (lane < LPR) {
+#pragma unroll
+            for (int d = 0; d < DPL; ++d) red[(w * G + j) * HD + ds + d] = acc[j][d];
+        }
+        if (lane == 0) {
+            sm[w * G + j] = m[j];
+            sl[w * G + j] = lw;
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < G * HD; i += NW * WAVE) {
+        const int j = i / HD, d = i % HD;
+        float M = -INFINITY;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, sm[ww * G + j]);
+        float v = 0.f, L = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) {
+            const float mw = sm[ww * G + j];
+            const float f = mw == -INFINITY ? 0.f : expf(mw - M);
+            v = fmaf(f, red[(ww * G + j) * HD + d], v);
+            L = fmaf(f, sl[ww * G + j], L);
+        }
+        if (a.out) {
+            act_st<COH>(a.out + (a.g * G + j) * HD + d, v / L);
+        } else {
+            act_st<COH>(a.part + j * HD + d, v);
+            if (d == 0) {
+                act_st<COH>(a.part + G * HD + j, M);
+                act_st<COH>(a.part + G * HD + G + j, L);
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// Merge of the partials of one KV head's items (part_g: n_items items of
+// attn_part_stride floats, in row order) into out[G][hd]: weights
+// exp(m_c - M_j), sums in item order. The maxima and sums go through LDS
+// first; each thread then owns one float4 column of the accumulators and a
+// fixed residue class of items (loaded 8 at a time, all in flight), and the
+// classes are added in order through LDS. Needs G*hd/4 <= nthreads.
+// COH as for act_ld.
+template <int HD, int G, bool COH>
+__device__ void attn_merge_group(const float* part_g, int n_items, float* out, float* lds, int tid,
+                                 int nthreads)
+{
+    constexpr int CB = 8;
+    constexpr int STRIDE = attn_part_stride(G, HD);
+    constexpr int COLS = G * HD / 4;
+    const int P = nthreads / COLS;              // threads per column
+    float* ms = lds;                            // [n_items][G]
+    float* ls = ms + n_items * G;               // [n_items][G]
+    float4* pv = reinterpret_cast<float4*>(ls + n_items * G + ((4 - (2 * n_items * G) % 4) % 4));  // [P][COLS]
+    float* pl = reinterpret_cast<float*>(pv + P * COLS);                                          // [P][G]
+    for (int i = tid; i < n_items * G; i += nthreads) {
+        const int c = i / G, j = i % G;
+        ms[i] = act_ld<COH>(part_g + c * STRIDE + G * HD + j);
+        ls[i] = act_ld<COH>(part_g + c * STRIDE + G * HD + G + j);
+    }
+    __syncthreads();
+    const int col = tid % COLS, sub = tid / COLS;
+    const int j = col * 4 / HD;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    float L = 0.f;
+    if (sub < P) {
+        float M = -INFINITY;
+        for (int c = 0; c < n_items; ++c) M = fmaxf(M, ms[c * G + j]);
+        for (int c0 = sub; c0 < n_items; c0 += P * CB) {
+            float4 x[CB];
+#pragma unroll
+            for (int b = 0; b < CB; ++b) {
+                const int c = c0 + b * P;
+                x[b] = c < n_items ? act_ld4<COH>(part_g, c * STRIDE + col * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int b = 0; b < CB; ++b) {
+                const int c = c0 + b * P;
+                if (c < n_items) {
+                    const float f = expf(ms[c * G + j] - M);
+                    v.x = fmaf(f, x[b].x, v.x);
+                    v.y = fmaf(f, x[b].y, v.y);
+                    v.z = fmaf(f, x[b].z, v.z);
+                    v.w = fmaf(f, x[b].w, v.w);
+                    L = fmaf(f, ls[c * G + j], L);
+                }
+            }
+        }
+        pv[sub * COLS + col] = v;
+        if ((col * 4) % HD == 0) pl[sub * G + j] = L;
+    }
+    __syncthreads();
+    if (tid < COLS) {
+        float4 t = pv[col];
+        float Lt = pl[j];
+        for (int s2 = 1; s2 < P; ++s2) {
+            const float4 u = pv[s2 * COLS + col];
+            t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
+            Lt += pl[s2 * G + j];
+        }
+        act_st<COH>(out + col * 4 + 0, t.x / Lt);
+        act_st<COH>(out + col * 4 + 1, t.y / Lt);
+        act_st<COH>(out + col * 4 + 2, t.z / Lt);
+        act_st<COH>(out + col * 4 + 3, t.w / Lt);
+    }
+    __syncthreads();
+}
+
+}  // namespace dev
+}  // namespace dfk

@@ -1,0 +1,490 @@
+// device_common.h — device-side building blocks shared by the decode
+// kernels (separate launches and the persistent step kernel): 16-byte
+// streaming loads, hand-off between work-groups of one kernel, DPP
+// reductions, and the per-lane dot product of a weight vector.
+#pragma once
+
+#include "kernels.h"
+
+namespace dfk {
+namespace dev {
+
+constexpr int WAVE = 64;
+
+// Global and constant address spaces. Pointers that a kernel loads from
+// memory (rather than receives as arguments) are generic to the compiler:
+// accesses through them become flat instructions, which also count against
+// the LDS wait counter, so every LDS access would wait for all loads in
+// flight. Casting to the global address space gives global instructions;
+// a step description read through a constant-space pointer gives scalar
+// loads of its fields.
+#define DFK_GLOBAL __attribute__((address_space(1)))
+#define DFK_CONST __attribute__((address_space(4)))
+
+template <class T>
+__device__ inline DFK_GLOBAL T* gmem(T* p)
+{
+    return (DFK_GLOBAL T*)(p);
+}
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte loads marked non-temporal: streamed data is read once.
+__device__ inline uint4 load16_nt(const void* p)
+{
+    const u32x4 v = __builtin_nontemporal_load(gmem(static_cast<const u32x4*>(p)));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ inline float4 load16f_nt(const float* p)
+{
+    const f32x4 v = __builtin_nontemporal_load(gmem(reinterpret_cast<const f32x4*>(p)));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+
+// Plain 16-byte load of 4 floats from global memory.
+__device__ inline float4 load4f(const float* p)
+{
+    const f32x4 v = *gmem(reinterpret_cast<const f32x4*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+
+__device__ inline float f16_bits_to_f32(uint16_t b)
+{
+    return static_cast<float>(__builtin_bit_cast(_Float16, b));
+}
+
+// Cross-work-group hand-off without cache-wide fences. Values another
+// work-group will read are stored with relaxed agent-scope atomics (written
+// through to the coherence point, bypassing the per-XCD L2), every wave waits
+// for its stores to be acknowledged before the block takes its ticket, and
+// the reader loads with relaxed agent-scope atomics (bypassing stale L2
+// lines). A device-scope fence would instead write back and invalidate the
+// whole L2 of the XCD once per work-group.
+__device__ inline void st_shared_f(float* p, float v)
+{
+    __hip_atomic_store(gmem(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void st_shared_i(int* p, int v)
+{
+    __hip_atomic_store(gmem(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline float ld_shared_f(const float* p)
+{
+    return __hip_atomic_load(gmem(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline int ld_shared_i(const int* p)
+{
+    return __hip_atomic_load(gmem(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until this wave's memory operations are complete.
+__device__ inline void drain_memory() { __builtin_amdgcn_s_waitcnt(0); }
+// Ticket: returns true in the last of `n` work-groups to arrive (all
+// threads). Call after every thread has issued its hand-off stores.
+__device__ inline bool last_to_arrive(int* counter, int n, int* flag_lds)
+{
+    drain_memory();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int prev = __hip_atomic_fetch_add(gmem(counter), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = prev == n - 1;
+        if (last) __hip_atomic_store(gmem(counter), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *flag_lds = last;
+    }
+    __syncthreads();
+    return *flag_lds != 0;
+}
+
+// Cross-lane reductions with DPP row operations (no LDS traffic):
+// quad_perm [1,0,3,2] and [2,3,0,1] combine lanes within quads, row half
+// mirror and row mirror combine quads within a 16-lane row. After
+// row16_sum every lane of a row holds the row's sum; the four rows of a
+// wave are then combined with readlane into a wave-uniform value.
+template <int CTRL>
+__device__ inline float dpp_f(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+constexpr int DPP_QUAD_XOR1 = 0xB1;
+constexpr int DPP_QUAD_XOR2 = 0x4E;
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_ROW_MIRROR = 0x140;
+
+__device__ inline float row16_sum(float v)
+{
+    v += dpp_f<DPP_QUAD_XOR1>(v);
+    v += dpp_f<DPP_QUAD_XOR2>(v);
+    v += dpp_f<DPP_ROW_HALF_MIRROR>(v);
+    v += dpp_f<DPP_ROW_MIRROR>(v);
+    return v;
+}
+
+__device__ inline float row16_max(float v)
+{
+    v = fmaxf(v, dpp_f<DPP_QUAD_XOR1>(v));
+    v = fmaxf(v, dpp_f<DPP_QUAD_XOR2>(v));
+    v = fmaxf(v, dpp_f<DPP_ROW_HALF_MIRROR>(v));
+    v = fmaxf(v, dpp_f<DPP_ROW_MIRROR>(v));
+    return v;
+}
+
+__device__ inline float lane_value(float v, int lane)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Sum over the 64 lanes, the same value in every lane.
+__device__ inline float wave_sum(float v)
+{
+    v = row16_sum(v);
+    return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
+}
+
+__device__ inline float wave_max(float v)
+{
+    v = row16_max(v);
+    return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)),
+                 fmaxf(lane_value(v, 32), lane_value(v, 48)));
+}
+
+// Elements of a weight row covered by one lane's 16-byte load.
+template <int WT> struct Epl;
+template <> struct Epl<W_F32> { static constexpr int v = 4; };
+template <> struct Epl<W_F16> { static constexpr int v = 8; };
+template <> struct Epl<W_Q8> { static constexpr int v = 16; };
+
+template <int WT>
+__device__ inline uint4 load_w(const void* base, int64_t elem)
+{
+    const char* p = static_cast<const char*>(base) +
+                    elem * (WT == W_F32 ? 4 : WT == W_F16 ? 2 : 1);
+    return load16_nt(p);
+}
+
+// dot of a lane's 16-byte weight vector with hs[k .. k + Epl).
+template <int WT>
+__device__ inline float lane_dot(uint4 w, const float* hs, int64_t k,
+                                 const uint16_t* srow)
+{
+    if constexpr (WT == W_F32) {
+        const float4 h = *reinterpret_cast<const float4*>(hs + k);
+        float a = __uint_as_float(w.x) * h.x;
+        a = fmaf(__uint_as_float(w.y), h.y, a);
+        a = fmaf(__uint_as_float(w.z), h.z, a);
+        return fmaf(__uint_as_float(w.w), h.w, a);
+    } else if constexpr (WT == W_F16) {
+        const half8 hw = __builtin_bit_cast(half8, w);
+        const float4 h0 = *reinterpret_cast<const float4*>(hs + k);
+        const float4 h1 = *reinterpret_cast<const float4*>(hs + k + 4);
+        float a = static_cast<float>(hw[0]) * h0.x;
+        float b = static_cast<float>(hw[1]) * h0.y;
+        a = fmaf(static_cast<float>(hw[2]), h0.z, a);
+        b = fmaf(static_cast<float>(hw[3]), h0.w, b);
+        a = fmaf(static_cast<float>(hw[4]), h1.x, a);
+        b = fmaf(static_cast<float>(hw[5]), h1.y, b);
+        a = fmaf(static_cast<float>(hw[6]), h1.z, a);
+        b = fmaf(static_cast<float>(hw[7]), h1.w, b);
+        return a + b;
+    } else {
+        // 16 int8 of one 32-value block: scale * sum(q * h)
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+        float a = 0.f, b = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float4 h = *reinterpret_cast<const float4*>(hs + k + 4 * j);
+            const uint32_t v = ww[j];
+            a = fmaf(static_cast<float>(static_cast<int8_t>(v & 0xff)), h.x, a);
+            b = fmaf(static_cast<float>(static_cast<int8_t>((v >> 8) & 0xff)), h.y, b);
+            a = fmaf(static_cast<float>(static_cast<int8_t>((v >> 16) & 0xff)), h.z, a);
+            b = fmaf(static_cast<float>(static_cast<int8_t>(v >> 24)), h.w, b);
+        }
+        return f16_bits_to_f32(*gmem(srow + (k >> 5))) * (a + b);
+    }
+}
+
+
+// ---------------------------------------------------------------------------
+// Decode matvec: out = epilogue(r * W (x . w)).
+//
+// Work layout (MvLayout, computed on the host by make_mv_layout). A block
+// owns `upb` consecutive output units (a row, or a gate row with its up row)
+// and splits each unit's K range into S equal slices of whole 64-lane chunks
+// so that its 8 waves get equal numbers of (unit, slice) items: no straggler
+// waves. Each wave walks its items as one stream of chunks, U chunks per
+// batch, and issues the loads of batch i+1 before it consumes batch i. The
+// first batch is issued by mv_begin, before the activation is even needed
+// (the persistent step kernel issues it before waiting at the barrier that
+// publishes the activation). The (unit, slice) sums meet in LDS and are
+// added in slice order after the streaming loop, so results do not depend
+// on timing.
+//
+// COH selects how the activation and the outputs are accessed: plain loads
+// and stores when they cross a kernel boundary, relaxed agent-scope atomics
+// when another work-group of the same kernel wrote them (see st_shared_f).
+// ---------------------------------------------------------------------------
+template <int WT, int NR, int U>
+struct ChunkBatch {
+    uint4 w[U][NR];
+};
+
+// Position in a block's stream of (unit, slice) items, chunk by chunk.
+// Advanced incrementally: no division on the hot path. Wave-uniform.
+struct Cursor {
+    int item;
+    int within;
+};
+
+__device__ inline void advance(Cursor& c, int cps)
+{
+    if (++c.within == cps) {
+        c.within = 0;
+        ++c.item;
+    }
+}
+
+template <int WT, int NR, int U>
+__device__ inline void fetch(const void* W, const MvLayout L, int64_t unit0, Cursor& c,
+                             int item_end, int lane, ChunkBatch<WT, NR, U>& b)
+{
+    constexpr int E = Epl<WT>::v;
+    constexpr int64_t CH = int64_t(WAVE) * E;
+    const int smask = (1 << L.log_s) - 1;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t unit = unit0 + (c.item >> L.log_s);
+        const int64_t k = (int64_t((c.item & smask) * L.cps + c.within)) * CH + int64_t(lane) * E;
+        // Chunks past the end are loaded from the start of W (a valid
+        // address) and never consumed: the loads stay unconditional, so the
+        // wait before consuming a batch can leave the next batch in flight
+        // (a branch around each load makes the compiler wait for all).
+        const bool ok = c.item < item_end && unit < L.n_out && k < L.K;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const int64_t row = unit + (r == 1 ? L.up_rows : 0);
+            b.w[u][r] = load_w<WT>(W, ok ? row * L.K + k : 0);
+        }
+        advance(c, L.cps);
+    }
+}
+
+// DEPTH scales the chunks per batch (registers per lane: 2 batches of
+// U * NR * 4 VGPRs): more bytes in flight per wave where fewer waves share a
+// compute unit.
+template <int WT, int MODE, int DEPTH = 1>
+struct MvState {
+    static constexpr int NR = (MODE == MV_SWIGLU) ? 2 : 1;
+    static constexpr int U = DEPTH * ((WT == W_F32) ? 8 : (NR == 1 ? 8 : 4));
+    ChunkBatch<WT, NR, U> cur;
+    Cursor fc, uc;
+    int item_end;
+    int n_chunks;
+    int64_t unit0;
+};
+
+template <bool COH>
+__device__ inline float act_ld(const float* p)
+{
+    if constexpr (COH) return ld_shared_f(p);
+    else return *gmem(p);
+}
+
+// 16 bytes at base[i .. i+4) through a buffer load that bypasses the
+// per-XCD L2 (cache policy sc1, as the relaxed agent-scope atomic loads):
+// sees what other work-groups of the same kernel stored with st_shared_f.
+// base must be wave-uniform; i is the lane's float index.
+constexpr int CPOL_SC1 = 16;
+constexpr int BUF_RSRC_WORD3 = 0x00020000;
+
+__device__ inline float4 coh_load4(const float* base, int i)
+{
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, 0x7fffffff, BUF_RSRC_WORD3);
+    const f32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, i * 4, 0, CPOL_SC1);
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+
+template <bool COH>
+__device__ inline float4 act_ld4(const float* base, int i)
+{
+    if constexpr (COH) return coh_load4(base, i);
+    else return load4f(base + i);
+}
+
+template <bool COH>
+__device__ inline void act_st(float* p, float v)
+{
+    if constexpr (COH) st_shared_f(p, v);
+    else *gmem(p) = v;
+}
+
+// Part 1: the block's item range and its first batch of weight loads.
+// tid is threadIdx.x, passed in so that a caller running several phases in
+// one kernel can keep each phase's per-lane values local to that phase.
+template <int WT, int MODE, int DEPTH>
+__device__ inline void mv_begin(const void* W, const MvLayout L, int block, MvState<WT, MODE, DEPTH>& st,
+                                int tid)
+{
+    const int lane = tid & (WAVE - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int S = 1 << L.log_s;
+    const int item_begin = wave * L.ipw;
+    st.unit0 = int64_t(block) * L.upb;
+    st.item_end = min(item_begin + L.ipw, L.upb * S);
+    st.n_chunks = (st.item_end > item_begin ? st.item_end - item_begin : 0) * L.cps;
+    if (st.unit0 >= L.n_out) st.n_chunks = 0;
+    st.fc = Cursor{item_begin, 0};
+    st.uc = Cursor{item_begin, 0};
+    if (st.n_chunks > 0) {
+        fetch<WT, MvState<WT, MODE, DEPTH>::NR, MvState<WT, MODE, DEPTH>::U>(W, L, st.unit0, st.fc, st.item_end,
+                                                                            lane, st.cur);
+    } else {
+        // Defined contents: an undefined batch lets the register allocator
+        // merge it with live ranges of other phases.
+#pragma unroll
+        for (int u = 0; u < MvState<WT, MODE, DEPTH>::U; ++u)
+#pragma unroll
+            for (int r = 0; r < MvState<WT, MODE, DEPTH>::NR; ++r) st.cur.w[u][r] = make_uint4(0u, 0u, 0u, 0u);
+    }
+}
+
+// Part 2: stage x (times the norm weight) in LDS (hs: K floats, then the
+// slice sums), then consume the batches and write the epilogue.
+template <int WT, int MODE, bool NORM, bool COH, int DEPTH, bool ALT = true>
+__device__ inline void mv_finish(const uint16_t* scales, const void* W, const MvLayout L,
+                                 MvState<WT, MODE, DEPTH>& st, const float* __restrict__ x,
+                                 const float* __restrict__ norm_w, float eps,
+                                 float* __restrict__ out, float* hs, float* red, int tid)
+{
+    constexpr int NR = MvState<WT, MODE, DEPTH>::NR;
+    constexpr int U = MvState<WT, MODE, DEPTH>::U;
+    constexpr int E = Epl<WT>::v;
+    constexpr int64_t CH = int64_t(WAVE) * E;
+    const int lane = tid & (WAVE - 1);
+    const int wave = tid >> 6;
+    const int nwaves = blockDim.x >> 6;
+    const int S = 1 << L.log_s;
+    float* part = hs + L.K;
+
+    float ss = 0.f;
+    for (int k = tid * 4; k < L.K; k += blockDim.x * 4) {
+        float4 v = act_ld4<COH>(x, k);
+        if constexpr (NORM) {
+            ss = fmaf(v.x, v.x, ss);
+            ss = fmaf(v.y, v.y, ss);
+            ss = fmaf(v.z, v.z, ss);
+            ss = fmaf(v.w, v.w, ss);
+            const float4 w = load4f(norm_w + k);
+            v.x *= w.x; v.y *= w.y; v.z *= w.z; v.w *= w.w;
+        }
+        *reinterpret_cast<float4*>(hs + k) = v;
+    }
+    float r = 1.f;
+    if constexpr (NORM) {
+        ss = wave_sum(ss);
+        if (lane == 0) red[wave] = ss;
+        __syncthreads();
+        float tot = 0.f;
+        for (int i = 0; i < nwaves; ++i) tot += red[i];
+        r = 1.0f / sqrtf(tot / static_cast<float>(L.K) + eps);
+    } else {
+        __syncthreads();
+    }
+
+    auto finish = [&](int64_t unit, float (&acc)[NR]) {
+        if constexpr (MODE == MV_SWIGLU) {
+            const float g = acc[0] * r;
+            const float u = acc[1] * r;
+            act_st<COH>(out + unit, (g / (1.0f + expf(-g))) * u);
+        } else if constexpr (MODE == MV_RESID) {
+            act_st<COH>(out + unit, act_ld<COH>(out + unit) + acc[0] * r);
+        } else {
+            act_st<COH>(out + unit, acc[0] * r);
+        }
+    };
+
+    // Each (unit, slice) sum goes to LDS; the epilogues (global loads and
+    // stores) run after the streaming loop, so that no wait inside the loop
+    // covers anything but the batch being consumed.
+    float acc[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) acc[i] = 0.f;
+    const int smask = S - 1;
+    auto consume = [&](const ChunkBatch<WT, NR, U>& cb) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (st.uc.item >= st.item_end) break;
+            const int64_t unit = st.unit0 + (st.uc.item >> L.log_s);
+            if (unit >= L.n_out) break;
+            const int64_t k = (int64_t((st.uc.item & smask) * L.cps + st.uc.within)) * CH +
+                              int64_t(lane) * E;
+            if (k < L.K) {
+#pragma unroll
+                for (int i = 0; i < NR; ++i) {
+                    const uint16_t* srow = nullptr;
+                    if constexpr (WT == W_Q8)
+                        srow = scales + (unit + (i == 1 ? L.up_rows : 0)) * (L.K >> 5);
+                    acc[i] += lane_dot<WT>(cb.w[u][i], hs, k, srow);
+                }
+            }
+            if (st.uc.within == L.cps - 1) {
+#pragma unroll
+                for (int i = 0; i < NR; ++i) acc[i] = wave_sum(acc[i]);
+                if (lane == 0) {
+#pragma unroll
+                    for (int i = 0; i < NR; ++i) part[st.uc.item * NR + i] = acc[i];
+                }
+#pragma unroll
+                for (int i = 0; i < NR; ++i) acc[i] = 0.f;
+            }
+            advance(st.uc, L.cps);
+        }
+    };
+    // Batch i+1 is in flight while batch i is consumed; the last batch is
+    // consumed on its own (no fetch past the end). With ALT two named
+    // buffers alternate (copying one batch into the other would wait for its
+    // loads); without it, fewer registers and a copy per batch.
+    if constexpr (ALT) {
+        ChunkBatch<WT, NR, U> nb;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int r = 0; r < NR; ++r) nb.w[u][r] = make_uint4(0u, 0u, 0u, 0u);  // defined (see mv_begin)
+        for (int q = 0; q < st.n_chunks;) {
+            if (q + U >= st.n_chunks) { consume(st.cur); break; }
+            fetch<WT, NR, U>(W, L, st.unit0, st.fc, st.item_end, lane, nb);
+            consume(st.cur);
+            q += U;
+            if (q + U >= st.n_chunks) { consume(nb); break; }
+            fetch<WT, NR, U>(W, L, st.unit0, st.fc, st.item_end, lane, st.cur);
+            consume(nb);
+            q += U;
+        }
+    } else {
+        for (int q = 0; q < st.n_chunks; q += U) {
+            ChunkBatch<WT, NR, U> nxt;
+            const bool more = q + U < st.n_chunks;
+            if (more) fetch<WT, NR, U>(W, L, st.unit0, st.fc, st.item_end, lane, nxt);
+            consume(st.cur);
+            if (more) st.cur = nxt;
+        }
+    }
+    __syncthreads();
+    for (int j = tid; j < L.upb; j += blockDim.x) {
+        const int64_t unit = st.unit0 + j;
+        if (unit >= L.n_out) break;
+        float sum[NR];
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            sum[i] = 0.f;
+            for (int s2 = 0; s2 < S; ++s2) sum[i] += part[(j * S + s2) * NR + i];
+        }
+        finish(unit, sum);
+    }
+}
+
+}  // namespace dev
+}  // namespace dfk

@@ -49,6 +49,23 @@ struct Weight {
 // when a norm weight is given, else x and r = 1.
 enum MatvecMode { MV_STORE = 0, MV_RESID = 1, MV_SWIGLU = 2 };
 
+// Work layout of a decode matvec over a grid of blocks of waves (see
+// device_common.h): units per block, K slices per unit, chunks per slice,
+// items per wave.
+struct MvLayout {
+    int64_t K, n_out, up_rows;
+    int upb;
+    int log_s;
+    int cps;
+    int ipw;
+};
+// Layout for at most max_blocks blocks of nwaves waves; *blocks gets the
+// blocks it uses.
+MvLayout make_mv_layout(int wdtype, int64_t K, int64_t n_out, int64_t up_rows, int max_blocks,
+                        int nwaves, int64_t* blocks);
+// LDS bytes a block needs: the staged activation and the (unit, slice) sums.
+size_t mv_lds_bytes(const MvLayout& L, int mode);
+
 // Device-side decode state: the position and the token of the step being
 // computed, so that a captured step needs no per-step arguments.
 struct DevState {
@@ -65,6 +82,10 @@ struct DevState {
 // query heads per KV head (1, 2, 4 or 8).
 constexpr int ATTN_T = 64;
 constexpr int ATTN_MAX_SPLIT = 128;
+// Floats of one attention partial (one item of G query heads): the
+// accumulators [G][hd], then the G running maxima, the G sums, padded to a
+// multiple of 4 floats so that every item starts 16-byte aligned.
+inline constexpr int attn_part_stride(int G, int hd) { return G * hd + ((2 * G + 3) & ~3); }
 constexpr int ATTN_MAX_GROUP = 8;
 
 // Work-groups per KV head that decode attention uses at position p.
@@ -94,7 +115,7 @@ struct AttnDecodeArgs {
     float* vc;
     int max_ctx, n_heads, n_kv, head_dim;
     const int* state_pos;      // device int: position p
-    float* part;               // [n_kv][ATTN_MAX_SPLIT][group][hd + 2]
+    float* part;               // [n_kv][ATTN_MAX_SPLIT] items of attn_part_stride floats
     float* out;                // [n_heads][hd]
     int grid_splits;           // work-groups launched per KV head (>= in use)
 };
@@ -110,6 +131,57 @@ hipError_t launch_argmax(const float* v, int n, DevState* st, int* out_dev,
 
 hipError_t launch_set_state(DevState* st, int pos, int tok, int step,
                             hipStream_t s);
+
+// ---- persistent decode step -------------------------------------------------
+
+// One layer's device pointers for the persistent step kernel.
+struct StepLayer {
+    const void* wqkv; const uint16_t* sqkv;  // values; 8-bit scales (else null)
+    const void* wo; const uint16_t* so;
+    const void* wgu; const uint16_t* sgu;
+    const void* wd; const uint16_t* sd;
+    const float* attn_norm;
+    const float* ffn_norm;
+    const float* q_norm;                     // null for llama
+    const float* k_norm;
+    float* kc;                               // layer K cache [n_kv][max_ctx][hd]
+    float* vc;
+};
+
+struct StepArgs {
+    const StepLayer* layers;
+    int n_layers, d, qd, kvd, F, V, hd, n_heads, n_kv, max_ctx;
+    float eps;
+    const void* embd;                        // token embedding (f16 or f32)
+    int embd_dtype;
+    const void* wout; const uint16_t* sout;  // logits matrix
+    const float* out_norm;
+    const float* cos_t;
+    const float* sin_t;
+    float* x; float* qkv; float* att; float* mid;
+    float* part;                             // attention partials [n_kv][splits][G][hd+2]
+    int max_splits;                          // split capacity per KV head
+    float* amax_val; int* amax_idx;          // argmax partials, one per block
+    DevState* st;                            // position, token, step
+    int* gen_out;                            // generated tokens
+    int* bar;                                // grid barrier: arrivals, exits, error flag
+    int* attn_cnt;                           // per KV head: splits finished (ticket)
+    MvLayout mv_qkv, mv_o, mv_gu, mv_down, mv_logits;
+};
+
+// The step kernel runs one block of STEP_THREADS threads per compute unit.
+constexpr int STEP_THREADS = 1024;
+// True if the configuration has a step kernel and one block with its LDS
+// fits on a compute unit; *lds gets the dynamic LDS bytes. The matvec
+// layouts in `a` must be made for one block per compute unit.
+bool step_fits(const StepArgs& a, int wdtype, int odtype, size_t* lds);
+// Launch one decode step (cooperative launch: every block resident). `a`
+// is the host copy of the step description, `a_dev` the same bytes in device
+// memory. With logits == nullptr the logits are not computed; with
+// `advance` the greedy token is written to gen_out[step] and becomes the
+// next step's token (position and step count move on by one).
+hipError_t launch_decode_step(const StepArgs& a, const StepArgs* a_dev, float* logits, int advance,
+                              int wdtype, int odtype, int blocks, size_t lds, hipStream_t s);
 
 // ---- bulk prefill ----------------------------------------------------------
 

@@ -109,8 +109,17 @@ typedef struct df_tensor {
 typedef struct df_options {
     void* stream;        /* hipStream_t to order all work on; NULL: the library makes one */
     int32_t device;      /* HIP device ordinal; used when stream is NULL */
-    int32_t flags;       /* reserved, 0 */
+    int32_t flags;       /* DF_FLAG_* bits; other bits are rejected */
 } df_options;
+
+/* Run every decode step as one persistent cooperative launch (all layers,
+ * logits and greedy token; phases separated by grid barriers) instead of one
+ * launch per operation class (DF_K_EMBED .. DF_K_ATTN_MERGE). Taken where the
+ * configuration has a step kernel (f16 or 8-bit block weights, head_dim 64
+ * or 128); otherwise the separate launches run. Results agree with the
+ * separate launches within rounding; on MI355X it is slower today, so it is
+ * not the default. */
+#define DF_FLAG_PERSISTENT_STEP 1
 
 typedef struct df_timings {
     double load_ms;          /* wall time of df_load, upload included */
@@ -120,6 +129,8 @@ typedef struct df_timings {
     int64_t weight_bytes;    /* device bytes held for weights */
     int64_t kv_bytes;        /* device bytes held for the KV cache */
     int64_t pool_bytes;      /* device bytes held by the activation frame pool */
+    int32_t persistent_step; /* 1: a decode step is one persistent launch; 0: separate launches */
+    int32_t step_blocks;     /* blocks of the persistent launch (0 without it) */
 } df_timings;
 
 typedef struct df_model df_model;
@@ -139,7 +150,9 @@ df_status df_load(const df_config* cfg, const df_tensor* tensors,
  * n == 1 runs the decode path; n > 1 runs bulk prefill on matrix cores,
  * which matches n single calls within the prefill tolerance. Arguments are
  * checked before any launch; on error kv_len is unchanged. Stream-ordered:
- * the host may reuse `tokens` on return. */
+ * the host may reuse `tokens` on return. When decode steps ran as the
+ * persistent launch, the call returns after they complete, so that a grid
+ * barrier that ran out of spins is reported here (DF_ERR_DEVICE). */
 df_status df_forward(df_model* m, const int32_t* tokens, int32_t n,
                      float* logits_dev);
 
@@ -147,7 +160,8 @@ df_status df_forward(df_model* m, const int32_t* tokens, int32_t n,
  * computes the logits, takes t_{i+1} = argmax (lowest index on ties) and
  * writes it to tokens_dev[i], for i < n_steps, with no host round trip.
  * The last step's logits go to logits_dev unless it is NULL. Equivalent to
- * n_steps df_forward(n = 1) + df_argmax calls. */
+ * n_steps df_forward(n = 1) + df_argmax calls. Synchronises when the steps
+ * run as the persistent launch (see df_forward). */
 df_status df_generate(df_model* m, int32_t first_token, int32_t n_steps,
                       int32_t* tokens_dev, float* logits_dev);
 
@@ -197,7 +211,8 @@ void* df_stream(const df_model* m);
 #define DF_K_LOGITS 6       /* final rms_norm + logits matvec */
 #define DF_K_ARGMAX 7       /* greedy token */
 #define DF_K_ATTN_MERGE 8   /* merge of the attention splits */
-#define DF_K_COUNT 9
+#define DF_K_STEP 9         /* the whole decode step as one persistent launch */
+#define DF_K_COUNT 10
 
 /* Time every launch of one kernel class (enable = 1) with start / end
  * stamps taken by the kernel dispatch itself, or stop (enable = 0). The
@@ -213,9 +228,10 @@ df_status df_profile_read(df_model* m, int32_t kernel, int64_t* launches,
  * launch configuration: the class's launches of one step (one per layer, or
  * one for embed / logits / argmax) are replayed `reps` times back to back on
  * the model's stream between one pair of HIP events, with no other work in
- * between. Needs a prior decode step (its buffers are reused; their contents
- * and the cache row at kv_len are overwritten, so the next df_forward /
- * df_generate starts from its own inputs as always). Synchronises. */
+ * between. Activation buffers and the cache row at kv_len are overwritten
+ * (the next df_forward / df_generate starts from its own inputs as always).
+ * DF_K_STEP needs a model that runs the persistent step (else
+ * DF_ERR_UNSUPPORTED_OP). Synchronises. */
 df_status df_time_kernel(df_model* m, int32_t kernel, int32_t reps,
                          double* mean_us);
 

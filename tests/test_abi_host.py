@@ -41,8 +41,10 @@ def test_library_links_no_torch():
     import subprocess
     import decoder_forward_amd as dfa
     out = subprocess.run(["ldd", dfa.LIB_PATH], capture_output=True, text=True).stdout
-    assert "torch" not in out and "c10" not in out
-    assert "amdhip64" in out
+    # library names only (the load addresses are hex and can contain "c10")
+    names = [line.split()[0] for line in out.splitlines() if line.strip()]
+    assert not any("torch" in n or n.startswith("libc10") for n in names), names
+    assert any(n.startswith("libamdhip64") for n in names), names
 
 
 def tiny_table(**kw):
