@@ -205,6 +205,7 @@ struct GemmArgs {
     int64_t ldc;
     int M, N, K;
     int64_t up_rows;
+    const uint16_t* zeros;     // >= 16 zero bytes (device): source of out-of-range chunks
 };
 hipError_t launch_gemm(const GemmArgs& g, int mode, hipStream_t s);
 

@@ -10,6 +10,8 @@
 // reads the f32 KV cache and rounds K and V to f16 in LDS.
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace dfk {
 namespace {
 
@@ -18,9 +20,12 @@ constexpr int WAVE = 64;
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ inline float h2f(uint16_t b) { return static_cast<float>(__builtin_bit_cast(_Float16, b)); }
 __device__ inline uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f)); }
+// Two floats rounded to f16, a in the low half.
+__device__ inline uint32_t pack_h2(float a, float b) { return uint32_t(f2h(a)) | (uint32_t(f2h(b)) << 16); }
 
 template <int CTRL>
 __device__ inline float dpp_f(float v)
@@ -89,34 +94,47 @@ rmsnorm_rows_kernel(const float* __restrict__ x, const float* __restrict__ w,
 
 // ---------------------------------------------------------------------------
 // GEMM C[M][N] = A[M][K] B[N][K]^T, f16 operands (both K-contiguous), f32
-// accumulation on v_mfma_f32_32x32x16_f16. 128x128 work-group tile, 64-deep
+// accumulation on v_mfma_f32_32x32x16_f16. BM x BN work-group tile, 64-deep
 // K stages double-buffered in LDS (rows padded by 16 bytes), four waves in a
-// 2x2 arrangement of 64x64 wave tiles (2x2 MFMA blocks each).
+// 2x2 arrangement of (BM/2) x (BN/2) wave tiles. A wave reads BM/64 A and
+// BN/64 B fragments from LDS per 16-deep step and issues (BM/64)(BN/64)
+// MFMAs, so larger tiles need less LDS bandwidth per flop.
 //
 // Lane layout of v_mfma_f32_32x32x16_f16 (checked on the device): lane l
 // supplies A[l%32][(l/32)*8 + i] and B[(l/32)*8 + i][l%32] for i < 8 and
 // receives C[(i/4)*8 + (l/32)*4 + i%4][l%32] for i < 16.
 //
 // Epilogues: store f32; add into f32 (residual); store f16; SwiGLU — the
-// tile's 128 B rows are gate rows f0..f0+63 and up rows f0..f0+63 in blocks
-// of 32 (gate, up, gate, up) so that each lane holds matching gate and up
+// tile's B rows are gate and up rows in alternating blocks of 32 (gate
+// f..f+31, up f..f+31, ...) so that each lane holds matching gate and up
 // sums, and writes f16(silu(g) * u).
 // ---------------------------------------------------------------------------
-constexpr int GBM = 128, GBN = 128, GBK = 64, GPAD = GBK + 8;
+constexpr int GBK = 64, GPAD = GBK + 8;
+// Work-group tile of the prefill GEMMs. The gate/up GEMM (twice the columns)
+// takes 256 x 256: half the LDS traffic per flop, and still enough tiles to
+// fill the device at prefill sizes; the others keep 128 x 128 for tile count.
+constexpr int GBM_ = 128, GBN_ = 128;
 
-template <int MODE>
+template <int BM, int BN>
+constexpr size_t gemm_lds_bytes() { return size_t(2) * (BM + BN) * GPAD * sizeof(_Float16); }
+
+template <int BM, int BN, int MODE>
 __global__ void __launch_bounds__(256)
 gemm_kernel(GemmArgs g)
 {
-    __shared__ _Float16 As[2][GBM][GPAD];
-    __shared__ _Float16 Bs[2][GBN][GPAD];
+    constexpr int WTM = BM / 2, WTN = BN / 2;
+    constexpr int MI = WTM / 32, NI = WTN / 32;
+    constexpr int CA = BM / 32, CB = BN / 32;  // 16-byte chunks per thread per stage
+    extern __shared__ _Float16 gsm[];
+    _Float16 (*As)[BM][GPAD] = reinterpret_cast<_Float16 (*)[BM][GPAD]>(gsm);
+    _Float16 (*Bs)[BN][GPAD] = reinterpret_cast<_Float16 (*)[BN][GPAD]>(gsm + 2 * BM * GPAD);
     const int tid = threadIdx.x;
     const int l = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int ncols = (MODE == GEMM_SWIGLU_F16) ? GBN / 2 : GBN;  // outputs per tile
+    constexpr int ncols = (MODE == GEMM_SWIGLU_F16) ? BN / 2 : BN;  // outputs per tile
     const int ntn = (g.N + ncols - 1) / ncols;
-    const int ntm = (g.M + GBM - 1) / GBM;
+    const int ntm = (g.M + BM - 1) / BM;
     // XCD-aware order: blocks b, b+8, b+16, ... run on one XCD; give them the
     // same n tile (weights) so its rows are reused from that XCD's L2.
     const int b = blockIdx.x;
@@ -129,22 +147,23 @@ gemm_kernel(GemmArgs g)
         tn = b / ntm;
         tm = b % ntm;
     }
-    const int m0 = tm * GBM;
+    const int m0 = tm * BM;
     const int n0 = tn * ncols;
 
-    // Global rows this thread copies: 4 chunks of 16 bytes for A and for B.
-    const uint16_t* aptr[4];
-    const uint16_t* bptr[4];
-    int srow[4], scol[4];
+    // Global rows this thread copies: chunk c of a stage is row c / 8, K
+    // offset (c % 8) * 8.
+    const uint16_t* aptr[CA];
+    const uint16_t* bptr[CB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < CA; ++i) {
+        const int c = tid + i * 256;
+        const int am = m0 + (c >> 3);
+        aptr[i] = am < g.M ? g.A + int64_t(am) * g.lda + (c & 7) * 8 : nullptr;
+    }
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
         const int c = tid + i * 256;
         const int row = c >> 3;
-        const int kc = (c & 7) * 8;
-        srow[i] = row;
-        scol[i] = kc;
-        const int am = m0 + row;
-        aptr[i] = am < g.M ? g.A + int64_t(am) * g.lda + kc : nullptr;
         int bn;
         bool ok;
         if constexpr (MODE == GEMM_SWIGLU_F16) {
@@ -156,77 +175,124 @@ gemm_kernel(GemmArgs g)
             bn = n0 + row;
             ok = bn < g.N;
         }
-        bptr[i] = ok ? g.B + int64_t(bn) * g.ldb + kc : nullptr;
+        bptr[i] = ok ? g.B + int64_t(bn) * g.ldb + (c & 7) * 8 : nullptr;
     }
-    uint4 ra[4], rb[4];
-    auto load_stage = [&](int k0) {
+    // Two register sets: the loads of stage s+2 are issued while stage s is
+    // computed, so each load has two stages of MFMA work to arrive. Loads
+    // are unconditional: rows or K chunks past the end read 16 zero bytes
+    // (g.zeros), so nothing is masked after the load and the waits count
+    // exactly.
+    u32x4 ra0[CA], rb0[CB], ra1[CA], rb1[CB];
+    auto load_stage = [&](auto set_c, int k0) {
+        constexpr int set = decltype(set_c)::value;
+        u32x4* ra = set == 0 ? ra0 : ra1;
+        u32x4* rb = set == 0 ? rb0 : rb1;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const bool kin = k0 + scol[i] < g.K;
-            ra[i] = (aptr[i] && kin) ? *reinterpret_cast<const uint4*>(aptr[i] + k0) : make_uint4(0, 0, 0, 0);
-            rb[i] = (bptr[i] && kin) ? *reinterpret_cast<const uint4*>(bptr[i] + k0) : make_uint4(0, 0, 0, 0);
+        for (int i = 0; i < CA; ++i) {
+            const bool ok = aptr[i] && k0 + ((tid + i * 256) & 7) * 8 < g.K;
+            ra[i] = *reinterpret_cast<const u32x4*>(ok ? aptr[i] + k0 : g.zeros);
+        }
+#pragma unroll
+        for (int i = 0; i < CB; ++i) {
+            const bool ok = bptr[i] && k0 + ((tid + i * 256) & 7) * 8 < g.K;
+            rb[i] = *reinterpret_cast<const u32x4*>(ok ? bptr[i] + k0 : g.zeros);
         }
     };
-    auto store_stage = [&](int buf) {
+    auto store_stage = [&](auto set_c) {
+        constexpr int set = decltype(set_c)::value, buf = set;
+        const u32x4* ra = set == 0 ? ra0 : ra1;
+        const u32x4* rb = set == 0 ? rb0 : rb1;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            *reinterpret_cast<uint4*>(&As[buf][srow[i]][scol[i]]) = ra[i];
-            *reinterpret_cast<uint4*>(&Bs[buf][srow[i]][scol[i]]) = rb[i];
+        for (int i = 0; i < CA; ++i) {
+            const int c = tid + i * 256;
+            *reinterpret_cast<u32x4*>(&As[buf][c >> 3][(c & 7) * 8]) = ra[i];
+        }
+#pragma unroll
+        for (int i = 0; i < CB; ++i) {
+            const int c = tid + i * 256;
+            *reinterpret_cast<u32x4*>(&Bs[buf][c >> 3][(c & 7) * 8]) = rb[i];
         }
     };
 
-    f32x16 acc[2][2];
+    f32x16 acc[MI][NI];
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
+        for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.f;
 
-    const int nst = (g.K + GBK - 1) / GBK;
-    load_stage(0);
-    store_stage(0);
-    __syncthreads();
-    for (int st = 0; st < nst; ++st) {
-        const int buf = st & 1;
-        if (st + 1 < nst) load_stage((st + 1) * GBK);
+    auto compute = [&](auto buf_c) {
+        constexpr int buf = decltype(buf_c)::value;
 #pragma unroll
         for (int kk = 0; kk < GBK / 16; ++kk) {
-            half8 af[2], bf[2];
+            half8 af[MI], bf[NI];
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
-                af[mi] = *reinterpret_cast<const half8*>(&As[buf][wm * 64 + mi * 32 + (l & 31)][kk * 16 + (l >> 5) * 8]);
+            for (int mi = 0; mi < MI; ++mi)
+                af[mi] = *reinterpret_cast<const half8*>(&As[buf][wm * WTM + mi * 32 + (l & 31)][kk * 16 + (l >> 5) * 8]);
 #pragma unroll
-            for (int ni = 0; ni < 2; ++ni)
-                bf[ni] = *reinterpret_cast<const half8*>(&Bs[buf][wn * 64 + ni * 32 + (l & 31)][kk * 16 + (l >> 5) * 8]);
+            for (int ni = 0; ni < NI; ++ni)
+                bf[ni] = *reinterpret_cast<const half8*>(&Bs[buf][wn * WTN + ni * 32 + (l & 31)][kk * 16 + (l >> 5) * 8]);
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
+            for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-                for (int ni = 0; ni < 2; ++ni)
+                for (int ni = 0; ni < NI; ++ni)
                     acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
         }
-        if (st + 1 < nst) store_stage(buf ^ 1);
+    };
+
+    // Stage s lives in LDS buffer s & 1. A register set is stored to LDS two
+    // stages of compute after its loads were issued: while stage s is
+    // computed, the set holding stage s+1 is stored and reloaded with stage
+    // s+3, and the other set holds stage s+2 in flight.
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    const int nst = (g.K + GBK - 1) / GBK;
+    // Loads and stores run unconditionally (past the last stage they repeat
+    // the last stage into a buffer nobody reads again), so every path keeps
+    // the same loads in flight and the waits stay exact.
+    auto kof = [&](int stage) { return min(stage, nst - 1) * GBK; };
+    load_stage(S0{}, 0);
+    load_stage(S1{}, kof(1));
+    store_stage(S0{});
+    load_stage(S0{}, kof(2));
+    __syncthreads();
+    int st = 0;
+    for (; st + 1 < nst; st += 2) {
+        // even stage st (LDS 0); set 1 holds stage st+1, set 0 stage st+2
+        store_stage(S1{});
+        load_stage(S1{}, kof(st + 3));
+        compute(S0{});
+        __syncthreads();
+        // odd stage st+1 (LDS 1); set 0 holds stage st+2, set 1 stage st+3
+        store_stage(S0{});
+        load_stage(S0{}, kof(st + 4));
+        compute(S1{});
         __syncthreads();
     }
+    if (st < nst) compute(S0{});  // odd number of stages: the last one
 
     // Epilogue.
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
+    for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int r = m0 + wm * 64 + mi * 32 + (i >> 2) * 8 + (l >> 5) * 4 + (i & 3);
+            const int r = m0 + wm * WTM + mi * 32 + (i >> 2) * 8 + (l >> 5) * 4 + (i & 3);
             if (r >= g.M) continue;
             if constexpr (MODE == GEMM_SWIGLU_F16) {
-                const int f = n0 + wn * 32 + (l & 31);
-                if (f < g.N) {
-                    const float gt = acc[mi][0][i];
-                    const float up = acc[mi][1][i];
-                    static_cast<uint16_t*>(g.C)[int64_t(r) * g.ldc + f] = f2h((gt / (1.0f + expf(-gt))) * up);
+#pragma unroll
+                for (int ni = 0; ni < NI; ni += 2) {
+                    const int f = n0 + ((wn * WTN) / 64 + ni / 2) * 32 + (l & 31);
+                    if (f < g.N) {
+                        const float gt = acc[mi][ni][i];
+                        const float up = acc[mi][ni + 1][i];
+                        static_cast<uint16_t*>(g.C)[int64_t(r) * g.ldc + f] = f2h((gt / (1.0f + expf(-gt))) * up);
+                    }
                 }
             } else {
 #pragma unroll
-                for (int ni = 0; ni < 2; ++ni) {
-                    const int c = n0 + wn * 64 + ni * 32 + (l & 31);
+                for (int ni = 0; ni < NI; ++ni) {
+                    const int c = n0 + wn * WTN + ni * 32 + (l & 31);
                     if (c >= g.N) continue;
                     const int64_t o = int64_t(r) * g.ldc + c;
                     if constexpr (MODE == GEMM_STORE_F32) static_cast<float*>(g.C)[o] = acc[mi][ni][i];
@@ -236,6 +302,23 @@ gemm_kernel(GemmArgs g)
             }
         }
     }
+}
+
+template <int BM, int BN, int MODE>
+hipError_t launch_gemm_t(const GemmArgs& g, hipStream_t s)
+{
+    constexpr size_t lds = gemm_lds_bytes<BM, BN>();
+    static bool attr_set = false;
+    if (!attr_set) {
+        const hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<BM, BN, MODE>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+        if (r != hipSuccess) return r;
+        attr_set = true;
+    }
+    constexpr int ncols = (MODE == GEMM_SWIGLU_F16) ? BN / 2 : BN;
+    const int blocks = ((g.N + ncols - 1) / ncols) * ((g.M + BM - 1) / BM);
+    DFK_LAUNCH((gemm_kernel<BM, BN, MODE>), dim3(blocks), dim3(256), lds, s, g);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -307,8 +390,8 @@ attn_prefill_kernel(AttnPrefillArgs a)
     constexpr int KQ = HD < 32 ? 32 : HD;  // QK depth, zero padded to 32
     constexpr int TK = 32;                  // keys per tile
     constexpr int DB = HD / 16;             // 16-wide output blocks
-    __shared__ _Float16 Ks[TK][KQ + 8];
-    __shared__ _Float16 Vt[HD][TK + 8];
+    __shared__ __attribute__((aligned(16))) _Float16 Ks[TK][KQ + 8];
+    __shared__ __attribute__((aligned(16))) _Float16 Vt[HD][TK + 8];
     __shared__ _Float16 Ps[G][16][TK + 8];
     const int qb = blockIdx.x;
     const int g = blockIdx.y;
@@ -347,22 +430,29 @@ attn_prefill_kernel(AttnPrefillArgs a)
     const int tiles = (n_keys + TK - 1) / TK;
     for (int kt = 0; kt < tiles; ++kt) {
         const int t0 = kt * TK;
-        // K tile (row-major, zero-padded depth) and V tile (transposed).
+        // K tile (row-major, zero-padded depth): 4 halves per 8-byte store,
+        // consecutive threads on consecutive addresses.
         for (int e = tid; e < TK * (KQ / 4); e += 64 * G) {
             const int r = e / (KQ / 4);
             const int c = (e % (KQ / 4)) * 4;
             float4 kv = make_float4(0.f, 0.f, 0.f, 0.f);
-            float4 vv = kv;
-            if (t0 + r < n_keys && c < HD) {
+            if (t0 + r < n_keys && c < HD)
                 kv = *reinterpret_cast<const float4*>(a.kc + head_base + int64_t(t0 + r) * HD + c);
-                vv = *reinterpret_cast<const float4*>(a.vc + head_base + int64_t(t0 + r) * HD + c);
-            }
-            Ks[r][c] = _Float16(kv.x); Ks[r][c + 1] = _Float16(kv.y);
-            Ks[r][c + 2] = _Float16(kv.z); Ks[r][c + 3] = _Float16(kv.w);
-            if (c < HD) {
-                Vt[c][r] = _Float16(vv.x); Vt[c + 1][r] = _Float16(vv.y);
-                Vt[c + 2][r] = _Float16(vv.z); Vt[c + 3][r] = _Float16(vv.w);
-            }
+            *reinterpret_cast<uint2*>(&Ks[r][c]) = make_uint2(pack_h2(kv.x, kv.y), pack_h2(kv.z, kv.w));
+        }
+        // V tile transposed: a thread takes rows (2i, 2i+1) at 4 dims and
+        // writes 4 half pairs; consecutive threads write consecutive pairs
+        // of one transposed row (no bank conflicts).
+        for (int e = tid; e < (TK / 2) * (HD / 4); e += 64 * G) {
+            const int r = (e % (TK / 2)) * 2;
+            const int c = (e / (TK / 2)) * 4;
+            float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f), v1 = v0;
+            if (t0 + r < n_keys) v0 = *reinterpret_cast<const float4*>(a.vc + head_base + int64_t(t0 + r) * HD + c);
+            if (t0 + r + 1 < n_keys) v1 = *reinterpret_cast<const float4*>(a.vc + head_base + int64_t(t0 + r + 1) * HD + c);
+            *reinterpret_cast<uint32_t*>(&Vt[c][r]) = pack_h2(v0.x, v1.x);
+            *reinterpret_cast<uint32_t*>(&Vt[c + 1][r]) = pack_h2(v0.y, v1.y);
+            *reinterpret_cast<uint32_t*>(&Vt[c + 2][r]) = pack_h2(v0.z, v1.z);
+            *reinterpret_cast<uint32_t*>(&Vt[c + 3][r]) = pack_h2(v0.w, v1.w);
         }
         __syncthreads();
         // Scores for keys kb*16 + l%16, rows (l/16)*4 + i.
@@ -451,16 +541,13 @@ hipError_t launch_rmsnorm_rows(const float* x, const float* w, int rows, int d, 
 hipError_t launch_gemm(const GemmArgs& g, int mode, hipStream_t s)
 {
     if (g.M <= 0 || g.N <= 0) return hipSuccess;
-    const int ncols = mode == GEMM_SWIGLU_F16 ? GBN / 2 : GBN;
-    const int blocks = ((g.N + ncols - 1) / ncols) * ((g.M + GBM - 1) / GBM);
     switch (mode) {
-    case GEMM_STORE_F32: DFK_LAUNCH(gemm_kernel<GEMM_STORE_F32>, dim3(blocks), dim3(256), 0, s, g); break;
-    case GEMM_ADD_F32: DFK_LAUNCH(gemm_kernel<GEMM_ADD_F32>, dim3(blocks), dim3(256), 0, s, g); break;
-    case GEMM_STORE_F16: DFK_LAUNCH(gemm_kernel<GEMM_STORE_F16>, dim3(blocks), dim3(256), 0, s, g); break;
-    case GEMM_SWIGLU_F16: DFK_LAUNCH(gemm_kernel<GEMM_SWIGLU_F16>, dim3(blocks), dim3(256), 0, s, g); break;
-    default: return hipErrorInvalidValue;
+    case GEMM_STORE_F32: return launch_gemm_t<GBM_, GBN_, GEMM_STORE_F32>(g, s);
+    case GEMM_ADD_F32: return launch_gemm_t<GBM_, GBN_, GEMM_ADD_F32>(g, s);
+    case GEMM_STORE_F16: return launch_gemm_t<GBM_, GBN_, GEMM_STORE_F16>(g, s);
+    case GEMM_SWIGLU_F16: return launch_gemm_t<256, 256, GEMM_SWIGLU_F16>(g, s);
     }
-    return hipGetLastError();
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_qk_post_rows(const QkPostArgs& a, hipStream_t s)

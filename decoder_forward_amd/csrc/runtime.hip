@@ -133,6 +133,7 @@ struct df_model {
     DevState* state = nullptr;
     float* attn_part = nullptr;
     int* argmax_out = nullptr;
+    uint16_t* zeros = nullptr;  // 256 zero bytes: source of out-of-range GEMM chunks
     int* gen_tokens = nullptr;  // [max_ctx]
 
     FramePool pool;
@@ -575,6 +576,9 @@ bool build_model(df_model* m, const std::map<std::string, const df_tensor*>& T, 
     if (!m->attn_part) return false;
     m->argmax_out = static_cast<int*>(dev_alloc(m, 4, "argmax result", e));
     if (!m->argmax_out) return false;
+    m->zeros = static_cast<uint16_t*>(dev_alloc(m, 256, "zero block", e));
+    if (!m->zeros) return false;
+    if (!check(hipMemsetAsync(m->zeros, 0, 256, m->stream), "zero block init", e)) return false;
     m->gen_tokens = static_cast<int*>(dev_alloc(m, size_t(c.max_ctx) * 4, "generated tokens", e));
     if (!m->gen_tokens) return false;
     if (!check(hipMemsetAsync(m->state, 0, sizeof(DevState), m->stream), "state init", e)) return false;
@@ -925,6 +929,7 @@ df_status prefill(df_model* m, const int32_t* tokens, int32_t n, float* logits)
         r = launch_rmsnorm_rows(x, L.attn_norm, S, d, eps, h16, m->stream);
         if (r != hipSuccess) break;
         GemmArgs g{};
+        g.zeros = m->zeros;
         g.A = h16; g.lda = d;
         g.B = static_cast<const uint16_t*>(L.wqkv.data); g.ldb = d;
         g.C = qkv; g.ldc = qd + 2 * kvd;
@@ -946,6 +951,7 @@ df_status prefill(df_model* m, const int32_t* tokens, int32_t n, float* logits)
         r = launch_attn_prefill(aa, m->stream);
         if (r != hipSuccess) break;
         g = GemmArgs{};
+        g.zeros = m->zeros;
         g.A = att16; g.lda = qd;
         g.B = static_cast<const uint16_t*>(L.wo.data); g.ldb = qd;
         g.C = x; g.ldc = d; g.M = S; g.N = d; g.K = qd;
@@ -954,12 +960,14 @@ df_status prefill(df_model* m, const int32_t* tokens, int32_t n, float* logits)
         r = launch_rmsnorm_rows(x, L.ffn_norm, S, d, eps, h16, m->stream);
         if (r != hipSuccess) break;
         g = GemmArgs{};
+        g.zeros = m->zeros;
         g.A = h16; g.lda = d;
         g.B = static_cast<const uint16_t*>(L.wgu.data); g.ldb = d;
         g.C = mid16; g.ldc = F; g.M = S; g.N = F; g.K = d; g.up_rows = F;
         r = launch_gemm(g, GEMM_SWIGLU_F16, m->stream);
         if (r != hipSuccess) break;
         g = GemmArgs{};
+        g.zeros = m->zeros;
         g.A = mid16; g.lda = F;
         g.B = static_cast<const uint16_t*>(L.wd.data); g.ldb = F;
         g.C = x; g.ldc = d; g.M = S; g.N = d; g.K = F;
