@@ -67,6 +67,71 @@ def gate_up_launch_bytes(cfg: dict) -> int:
     return F * unit + d * 4 + d * 4 + F * 4
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_matvec_llama8b_traffic.txt")
+TRAFFIC_SOURCES = [os.path.join(ROOT, "decoder_forward_amd", "csrc", f)
+                   for f in ("device_common.h", "decode.hip")]
+
+
+def kernel_source_hash() -> str:
+    """sha1 of the sources the decode matvec is compiled from."""
+    import hashlib
+    h = hashlib.sha1()
+    for f in TRAFFIC_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic() -> dict | None:
+    """HBM bytes per gate/up launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by what the
+    same counter reads for a plain copy of known size), or None when that
+    summary is missing or was taken on other kernel sources."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as fh:
+            for line in fh:
+                if "=" in line and not line.startswith("#"):
+                    k, v = line.split("=", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("source_sha1") != kernel_source_hash():
+            return None
+        fetch = float(kv["fetch_kib_per_launch"]) * float(kv["copy_fetch_factor"]) * 1024
+        write = float(kv["write_kib_per_launch"]) * float(kv["copy_write_factor"]) * 1024
+        return {"fetch": fetch, "write": write}
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def pmc_summary(path: str, pattern: str) -> None:
+    """Mean of each counter per dispatch over the kernels whose name contains
+    `pattern`, from a rocprofv3 --pmc csv output directory."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+    acc: dict = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if pattern in r["Kernel_Name"]:
+                acc.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    for k, v in sorted(acc.items()):
+        print(f"{k}: dispatches {len(v)}, mean {sum(v) / len(v):.1f}, "
+              f"min {min(v):.1f}, max {max(v):.1f}")
+
+
+def copy_probe(mib: int) -> None:
+    """A plain device copy of `mib` MiB, 4 times (the reference kernel for
+    scaling the FETCH_SIZE / WRITE_SIZE counters)."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"copy probe: {mib} MiB x 4", flush=True)
+
+
 def cpu_baseline(cfg: dict, ctx: int) -> dict:
     """The oracle, as it is, on a bounded sample of one decode step: a model
     with the same shapes but 2 of the 32 layers (plus embed and the logits
@@ -130,7 +195,17 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--persistent-step", action="store_true",
                     help="one persistent launch per step instead of one per operation class")
+    ap.add_argument("--copy-probe", type=int, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("DIR", "KERNEL"),
+                    help="only summarise a rocprofv3 --pmc output directory")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} "
@@ -227,6 +302,7 @@ def main():
         cpu = cpu_baseline(cfg, ctx)
         log(f"[bench] cpu baseline: {cpu}")
 
+    traffic = measured_traffic() if args.workload == "llama_8b" and not args.persistent_step else None
     t = m.timings()
     report = {
         "metric": METRIC,
@@ -262,10 +338,13 @@ def main():
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": round(gu_gbps / PEAK_HBM_GBPS, 4),
-            "traffic": None,
+            "traffic": round(traffic["fetch"] + traffic["write"]) if traffic else None,
+            "traffic_read_write": ([round(traffic["fetch"]), round(traffic["write"])]
+                                   if traffic else None),
             "bytes_per_launch": gu_bytes,
             "mean_launch_us": gu["mean_us"],
-            "timing": "back-to-back replay of one step's 32 launches x 8, HIP events",
+            "timing": (f"back-to-back replay of one step's {cfg['n_layers']} launches x 8, "
+                       "HIP events on the library's stream"),
         },
         "kernels": kernels,
         "cpu_baseline": cpu,
