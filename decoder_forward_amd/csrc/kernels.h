@@ -206,6 +206,10 @@ struct GemmArgs {
     int M, N, K;
     int64_t up_rows;
     const uint16_t* zeros;     // >= 16 zero bytes (device): source of out-of-range chunks
+    // 8-bit block weights: B holds int8 values [N][ldb] (bytes) and Bsc the
+    // f16 scale of every 32 values [N][ldb / 32]; B rows are dequantised to
+    // f16 (scale * q) on their way into LDS. Null for f16 weights.
+    const uint16_t* Bsc;
 };
 hipError_t launch_gemm(const GemmArgs& g, int mode, hipStream_t s);
 

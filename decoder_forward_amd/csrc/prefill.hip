@@ -118,7 +118,7 @@ constexpr int GBM_ = 128, GBN_ = 128;
 template <int BM, int BN>
 constexpr size_t gemm_lds_bytes() { return size_t(2) * (BM + BN) * GPAD * sizeof(_Float16); }
 
-template <int BM, int BN, int MODE>
+template <int BM, int BN, int MODE, bool WQ8>
 __global__ void __launch_bounds__(256)
 gemm_kernel(GemmArgs g)
 {
@@ -154,6 +154,7 @@ gemm_kernel(GemmArgs g)
     // offset (c % 8) * 8.
     const uint16_t* aptr[CA];
     const uint16_t* bptr[CB];
+    const uint16_t* sptr[WQ8 ? CB : 1];
 #pragma unroll
     for (int i = 0; i < CA; ++i) {
         const int c = tid + i * 256;
@@ -175,13 +176,23 @@ gemm_kernel(GemmArgs g)
             bn = n0 + row;
             ok = bn < g.N;
         }
-        bptr[i] = ok ? g.B + int64_t(bn) * g.ldb + (c & 7) * 8 : nullptr;
+        if constexpr (WQ8) {
+            // values: 1 byte per weight (8 per chunk); scales: one f16 per 32
+            bptr[i] = ok ? reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(g.B) +
+                                                            int64_t(bn) * g.ldb + (c & 7) * 8)
+                         : nullptr;
+            sptr[i] = ok ? g.Bsc + int64_t(bn) * (g.ldb >> 5) : nullptr;
+        } else {
+            bptr[i] = ok ? g.B + int64_t(bn) * g.ldb + (c & 7) * 8 : nullptr;
+        }
     }
     // Two register sets: the loads of stage s+2 are issued while stage s is
     // computed, so each load has two stages of MFMA work to arrive. Loads
     // are unconditional: rows or K chunks past the end read 16 zero bytes
     // (g.zeros), so nothing is masked after the load and the waits count
     // exactly.
+    // B registers: 16 bytes of f16, or for 8-bit blocks 8 value bytes (in
+    // .x, .y) and the block's f16 scale (in .z).
     u32x4 ra0[CA], rb0[CB], ra1[CA], rb1[CB];
     auto load_stage = [&](auto set_c, int k0) {
         constexpr int set = decltype(set_c)::value;
@@ -194,9 +205,33 @@ gemm_kernel(GemmArgs g)
         }
 #pragma unroll
         for (int i = 0; i < CB; ++i) {
-            const bool ok = bptr[i] && k0 + ((tid + i * 256) & 7) * 8 < g.K;
-            rb[i] = *reinterpret_cast<const u32x4*>(ok ? bptr[i] + k0 : g.zeros);
+            const int kc = k0 + ((tid + i * 256) & 7) * 8;
+            const bool ok = bptr[i] && kc < g.K;
+            if constexpr (WQ8) {
+                const uint2 q = *reinterpret_cast<const uint2*>(
+                    ok ? reinterpret_cast<const uint8_t*>(bptr[i]) + k0 : reinterpret_cast<const uint8_t*>(g.zeros));
+                const uint16_t sc = *(ok ? sptr[i] + (kc >> 5) : g.zeros);
+                rb[i] = u32x4{q.x, q.y, uint32_t(sc), 0u};
+            } else {
+                rb[i] = *reinterpret_cast<const u32x4*>(ok ? bptr[i] + k0 : g.zeros);
+            }
         }
+    };
+    // 8 int8 values times the f16 scale, rounded to f16 (RNE).
+    auto dequant = [](u32x4 r) {
+        const float sc = h2f(uint16_t(r.z));
+        u32x4 o;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t v = h == 0 ? r.x : r.y;
+            const float f0 = static_cast<float>(static_cast<int8_t>(v & 0xff)) * sc;
+            const float f1 = static_cast<float>(static_cast<int8_t>((v >> 8) & 0xff)) * sc;
+            const float f2 = static_cast<float>(static_cast<int8_t>((v >> 16) & 0xff)) * sc;
+            const float f3 = static_cast<float>(static_cast<int8_t>(v >> 24)) * sc;
+            o[2 * h] = pack_h2(f0, f1);
+            o[2 * h + 1] = pack_h2(f2, f3);
+        }
+        return o;
     };
     auto store_stage = [&](auto set_c) {
         constexpr int set = decltype(set_c)::value, buf = set;
@@ -210,7 +245,8 @@ gemm_kernel(GemmArgs g)
 #pragma unroll
         for (int i = 0; i < CB; ++i) {
             const int c = tid + i * 256;
-            *reinterpret_cast<u32x4*>(&Bs[buf][c >> 3][(c & 7) * 8]) = rb[i];
+            if constexpr (WQ8) *reinterpret_cast<u32x4*>(&Bs[buf][c >> 3][(c & 7) * 8]) = dequant(rb[i]);
+            else *reinterpret_cast<u32x4*>(&Bs[buf][c >> 3][(c & 7) * 8]) = rb[i];
         }
     };
 
@@ -304,21 +340,27 @@ gemm_kernel(GemmArgs g)
     }
 }
 
-template <int BM, int BN, int MODE>
-hipError_t launch_gemm_t(const GemmArgs& g, hipStream_t s)
+template <int BM, int BN, int MODE, bool WQ8>
+hipError_t launch_gemm_q(const GemmArgs& g, hipStream_t s)
 {
     constexpr size_t lds = gemm_lds_bytes<BM, BN>();
     static bool attr_set = false;
     if (!attr_set) {
-        const hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<BM, BN, MODE>),
+        const hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<BM, BN, MODE, WQ8>),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
         if (r != hipSuccess) return r;
         attr_set = true;
     }
     constexpr int ncols = (MODE == GEMM_SWIGLU_F16) ? BN / 2 : BN;
     const int blocks = ((g.N + ncols - 1) / ncols) * ((g.M + BM - 1) / BM);
-    DFK_LAUNCH((gemm_kernel<BM, BN, MODE>), dim3(blocks), dim3(256), lds, s, g);
+    DFK_LAUNCH((gemm_kernel<BM, BN, MODE, WQ8>), dim3(blocks), dim3(256), lds, s, g);
     return hipGetLastError();
+}
+
+template <int BM, int BN, int MODE>
+hipError_t launch_gemm_t(const GemmArgs& g, hipStream_t s)
+{
+    return g.Bsc ? launch_gemm_q<BM, BN, MODE, true>(g, s) : launch_gemm_q<BM, BN, MODE, false>(g, s);
 }
 
 // ---------------------------------------------------------------------------

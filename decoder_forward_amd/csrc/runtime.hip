@@ -896,11 +896,12 @@ df_status decode_one(df_model* m, int32_t tok, float* logits)
 // [rms_norm rows -> f16] [q/k/v GEMM] [norm_heads + rope + KV append]
 // [causal flash attention] [o GEMM + add] [rms_norm rows -> f16]
 // [gate/up GEMM + silu * up] [down GEMM + add]; then the last row's
-// [rms_norm + logits matvec]. Needs f16 block weights.
+// [rms_norm + logits matvec]. Needs f16 or 8-bit block weights (8-bit
+// blocks are dequantised to f16 inside the GEMM's weight load path).
 // ---------------------------------------------------------------------------
 bool bulk_supported(const df_model* m)
 {
-    return m->cfg.n_layers == 0 || m->layers[0].wqkv.dtype == W_F16;
+    return m->cfg.n_layers == 0 || m->layers[0].wqkv.dtype == W_F16 || m->layers[0].wqkv.dtype == W_Q8;
 }
 
 df_status prefill(df_model* m, const int32_t* tokens, int32_t n, float* logits)
@@ -931,7 +932,7 @@ df_status prefill(df_model* m, const int32_t* tokens, int32_t n, float* logits)
         GemmArgs g{};
         g.zeros = m->zeros;
         g.A = h16; g.lda = d;
-        g.B = static_cast<const uint16_t*>(L.wqkv.data); g.ldb = d;
+        g.B = static_cast<const uint16_t*>(L.wqkv.data); g.ldb = d; g.Bsc = L.wqkv.scales;
         g.C = qkv; g.ldc = qd + 2 * kvd;
         g.M = S; g.N = qd + 2 * kvd; g.K = d;
         r = launch_gemm(g, GEMM_STORE_F32, m->stream);
@@ -953,7 +954,7 @@ df_status prefill(df_model* m, const int32_t* tokens, int32_t n, float* logits)
         g = GemmArgs{};
         g.zeros = m->zeros;
         g.A = att16; g.lda = qd;
-        g.B = static_cast<const uint16_t*>(L.wo.data); g.ldb = qd;
+        g.B = static_cast<const uint16_t*>(L.wo.data); g.ldb = qd; g.Bsc = L.wo.scales;
         g.C = x; g.ldc = d; g.M = S; g.N = d; g.K = qd;
         r = launch_gemm(g, GEMM_ADD_F32, m->stream);
         if (r != hipSuccess) break;
@@ -962,14 +963,14 @@ df_status prefill(df_model* m, const int32_t* tokens, int32_t n, float* logits)
         g = GemmArgs{};
         g.zeros = m->zeros;
         g.A = h16; g.lda = d;
-        g.B = static_cast<const uint16_t*>(L.wgu.data); g.ldb = d;
+        g.B = static_cast<const uint16_t*>(L.wgu.data); g.ldb = d; g.Bsc = L.wgu.scales;
         g.C = mid16; g.ldc = F; g.M = S; g.N = F; g.K = d; g.up_rows = F;
         r = launch_gemm(g, GEMM_SWIGLU_F16, m->stream);
         if (r != hipSuccess) break;
         g = GemmArgs{};
         g.zeros = m->zeros;
         g.A = mid16; g.lda = F;
-        g.B = static_cast<const uint16_t*>(L.wd.data); g.ldb = F;
+        g.B = static_cast<const uint16_t*>(L.wd.data); g.ldb = F; g.Bsc = L.wd.scales;
         g.C = x; g.ldc = d; g.M = S; g.N = d; g.K = F;
         r = launch_gemm(g, GEMM_ADD_F32, m->stream);
     }
@@ -1109,7 +1110,7 @@ df_status df_forward(df_model* m, const int32_t* tokens, int32_t n, float* logit
         st = prefill(m, tokens, n, logits_dev);
     } else {
         // One token, or block weights the matrix-core path does not take
-        // (f32, 8-bit): the decode kernels, one position after another.
+        // (f32): the decode kernels, one position after another.
         for (int32_t i = 0; i < n && st == DF_OK; ++i)
             st = decode_one(m, tokens[i], i == n - 1 ? logits_dev : nullptr);
     }

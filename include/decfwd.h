@@ -147,8 +147,10 @@ df_status df_load(const df_config* cfg, const df_tensor* tensors,
 /* Append n tokens (host array of ids in [0, vocab)) at positions kv_len ..
  * kv_len+n-1 and write the logits of the last position, vocab f32 values,
  * to logits_dev (device memory, caller-owned; NULL skips the logits).
- * n == 1 runs the decode path; n > 1 runs bulk prefill on matrix cores,
- * which matches n single calls within the prefill tolerance. Arguments are
+ * n == 1 runs the decode path; n > 1 runs bulk prefill on matrix cores
+ * (f16 or 8-bit block weights; 8-bit blocks are dequantised to f16 on the
+ * way into the GEMM; f32 weights run the decode path n times), which matches
+ * n single calls within the prefill tolerance. Arguments are
  * checked before any launch; on error kv_len is unchanged. Stream-ordered:
  * the host may reuse `tokens` on return. When decode steps ran as the
  * persistent launch, the call returns after they complete, so that a grid

@@ -133,3 +133,36 @@ def test_qwen3_8b_bulk_2048(dfa):
         t = first_argmax(gb)
     a.close()
     b.close()
+
+
+def test_llama_8b_q8_bulk_1024(dfa):
+    """8-bit blocks, all 32 layers: one bulk prefill of 1024 tokens against
+    GPU token-by-token (5e-3, greedy token identical unless a near-tie), and
+    the cache rows of the first and last layer."""
+    import torch
+    cfg = synth.config("llama_8b_q8")
+    S = 1024
+    say(f"[llama-8B shape, 32 layers, 8-bit blocks] bulk prefill of {S} vs token-by-token")
+    Wd = synth.make_weights_device(cfg)
+    torch.cuda.synchronize()
+    toks = synth.make_prompt(cfg, S, stream=6)
+    a = dfa.Model(cfg, Wd, max_ctx=S + 16)
+    la = a.forward(toks).cpu().numpy()
+    b = dfa.Model(cfg, Wd, max_ctx=S + 16)
+    del Wd
+    torch.cuda.empty_cache()
+    for t in toks[:-1]:
+        b.forward([t], logits=False)
+    lb = b.forward([toks[-1]]).cpu().numpy()
+    e = rel_l2(la, lb)
+    say(f"  bulk vs token-by-token: rel-L2 {e:.2e}")
+    assert e <= 5e-3
+    if first_argmax(la) != first_argmax(lb):
+        assert near_tie(lb, 5e-3)
+    for layer in (0, cfg["n_layers"] - 1):
+        for which in (0, 1):
+            ka = a.read_kv(layer, which, 0, S)
+            kb = b.read_kv(layer, which, 0, S)
+            assert np.linalg.norm(ka - kb) / np.linalg.norm(kb) <= 5e-3, (layer, which)
+    a.close()
+    b.close()

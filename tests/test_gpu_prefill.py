@@ -1,4 +1,5 @@
-"""Bulk prefill parity on the GPU (df_forward with n > 1, matrix-core path).
+"""Bulk prefill parity on the GPU (df_forward with n > 1, matrix-core path;
+f16 and 8-bit block weights).
 
 Bulk prefill must give the same result as token-by-token within epsilon
 (page "Execution contract", "Forward phase"). The GEMM operands are rounded
@@ -82,8 +83,29 @@ def test_tiny_f16_bulk_then_bulk_then_decode(dfa, arch):
     m.close()
 
 
+@pytest.mark.parametrize("arch", ["qwen3", "llama"])
+def test_tiny_q8_bulk_then_decode(dfa, arch):
+    """8-bit block weights: the GEMMs dequantise the weight tiles to f16."""
+    say(f"[tiny {arch} q8] bulk 40 (ragged K and N tiles) + 4 decode steps vs the oracle")
+    cfg = synth.config("tiny", arch=arch, wdtype="q8", d_model=192, ffn_dim=416, max_ctx=64)
+    W = synth.make_weights(cfg)
+    toks = synth.make_prompt(cfg, 40)
+    om, ref = oracle_run(cfg, W, [toks], 64)
+    m = dfa.Model(cfg, W)
+    got = m.forward(toks).cpu().numpy().copy()
+    assert m.kv_len == 40
+    check_logits(got, ref[0], "after 40")
+    check_kv(m, om, cfg, 40)
+    nxt = first_argmax(ref[0])
+    for i in range(4):
+        r = om.forward([nxt])
+        check_logits(m.forward([nxt]).cpu().numpy(), r, f"decode {i}")
+        nxt = first_argmax(r)
+    m.close()
+
+
 @pytest.mark.parametrize("name,S,vocab", [("qwen3_8b", 300, None), ("llama_8b", 200, 4096),
-                                          ("qwen3_0p6b", 137, None)])
+                                          ("qwen3_0p6b", 137, None), ("llama_8b_q8", 160, 4096)])
 def test_one_layer_real_shape_bulk(dfa, name, S, vocab):
     over = dict(n_layers=1, max_ctx=S + 8)
     if vocab:

@@ -179,14 +179,17 @@ def test_step_kernel_rerun_is_bitwise_identical(dfa):
 
 
 def test_step_kernel_prompt_token_loop_without_logits(dfa):
-    """8-bit prompts run token by token through the step kernel with the
-    logits phase skipped; the last call's logits still match the oracle."""
+    """A prompt fed token by token with the logits phase skipped (logits
+    only on the last call) through the step kernel still matches the
+    oracle."""
     cfg = small("qwen3", "q8", 64, 4, tied=False)
-    say("[qwen3 q8 hd 64] 30-token prompt in one call (token loop) vs the oracle")
+    say("[qwen3 q8 hd 64] 30-token prompt one token per call, logits on the last only")
     W = synth.make_weights(cfg)
     prompt = synth.make_prompt(cfg, 30)
     m = dfa.Model(cfg, W, persistent_step=True)
-    got = m.forward(prompt).cpu().numpy()
+    for t in prompt[:-1]:
+        m.forward([t], logits=False)
+    got = m.forward([prompt[-1]]).cpu().numpy()
     om = oracle.Model(cfg, W)
     ref = om.forward(prompt)
     assert rel_l2(got, ref) <= 1e-3
