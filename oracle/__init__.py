@@ -19,16 +19,21 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liboracle.so")
 
 F32, F16, Q8 = 0, 1, 2
-LLAMA, QWEN3 = 0, 1
-SLOTS = ("attn_norm", "attn_q", "attn_k", "attn_v", "attn_q_norm",
-         "attn_k_norm", "attn_output", "ffn_norm", "ffn_gate", "ffn_up",
-         "ffn_down")
+LLAMA, QWEN3, QWEN2 = 0, 1, 2
+ARCHS = {"llama": LLAMA, "qwen3": QWEN3, "qwen2": QWEN2}
+ROPE_PAIRINGS = {"halves": 0, "adjacent": 1}
+# Per-layer tensors in the oracle's slot order (GGUF names after "blk.{i}.").
+SLOTS = ("attn_norm.weight", "attn_q.weight", "attn_k.weight",
+         "attn_v.weight", "attn_q_norm.weight", "attn_k_norm.weight",
+         "attn_output.weight", "ffn_norm.weight", "ffn_gate.weight",
+         "ffn_up.weight", "ffn_down.weight", "attn_q.bias", "attn_k.bias",
+         "attn_v.bias")
 
 MUTATIONS = {
     "none": 0, "norm_after_rope": 1, "rope_interleaved": 2,
     "no_attn_residual": 3, "scale_1_over_hd": 4, "gqa_modulo": 5,
     "eps_outside": 6, "exclude_self": 7, "silu_on_up": 8,
-    "rope_pos_plus1": 9, "matvec_transpose": 10,
+    "rope_pos_plus1": 9, "matvec_transpose": 10, "k_bias_after_rope": 11,
 }
 
 
@@ -37,7 +42,7 @@ class Config(C.Structure):
                 ("d_model", C.c_int32), ("n_heads", C.c_int32),
                 ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
                 ("ffn_dim", C.c_int32), ("vocab", C.c_int32),
-                ("max_ctx", C.c_int32), ("pad_", C.c_int32),
+                ("max_ctx", C.c_int32), ("rope_pairing", C.c_int32),
                 ("rope_theta", C.c_double), ("rms_eps", C.c_double)]
 
 
@@ -65,6 +70,8 @@ def lib():
         L.orc_embed.argtypes = [T, i64, i64, fp]
         L.orc_rope_table.argtypes = [i32, i32, dbl, fp, fp]
         L.orc_rope.argtypes = [fp, i32, i32, fp, fp]
+        L.orc_rope_pairs.argtypes = [fp, i32, i32, fp, fp, i32]
+        L.orc_add_bias.argtypes = [fp, T, i64]
         L.orc_attention.argtypes = [fp, i32, i32, i32, fp, fp, i64, i32, fp]
         L.orc_silu.argtypes = [fp, i64]
         L.orc_mul.argtypes = [fp, fp, i64]
@@ -170,12 +177,21 @@ def rope_table(n_pos: int, hd: int, theta: float):
     return c, s
 
 
-def rope(t: np.ndarray, hd: int, cos_row: np.ndarray, sin_row: np.ndarray) -> np.ndarray:
+def rope(t: np.ndarray, hd: int, cos_row: np.ndarray, sin_row: np.ndarray,
+         pairing: str = "halves") -> np.ndarray:
     t = np.array(t, np.float32, copy=True, order="C")
     cr = np.ascontiguousarray(cos_row, np.float32)
     sr = np.ascontiguousarray(sin_row, np.float32)
-    lib().orc_rope(_fp(t), t.size // hd, hd, _fp(cr), _fp(sr))
+    lib().orc_rope_pairs(_fp(t), t.size // hd, hd, _fp(cr), _fp(sr), ROPE_PAIRINGS[pairing])
     return t
+
+
+def add_bias(y: np.ndarray, b: np.ndarray) -> np.ndarray:
+    y = np.array(y, np.float32, copy=True, order="C")
+    b = np.ascontiguousarray(b)
+    t = tensor(b)
+    lib().orc_add_bias(_fp(y), C.byref(t), y.size)
+    return y
 
 
 def attention(q: np.ndarray, K: np.ndarray, V: np.ndarray) -> np.ndarray:
@@ -222,16 +238,17 @@ class Model:
             self._keep.append(a)
             return tensor(a)
 
-        self.ccfg = Config(QWEN3 if c["arch"] == "qwen3" else LLAMA,
+        self.ccfg = Config(ARCHS[c["arch"]],
                            c["n_layers"], c["d_model"], c["n_heads"],
                            c["n_kv_heads"], c["head_dim"], c["ffn_dim"],
-                           c["vocab"], c["max_ctx"], 0,
+                           c["vocab"], c["max_ctx"],
+                           ROPE_PAIRINGS[c.get("rope_pairing", "halves")],
                            float(c["rope_theta"]), float(c["rms_eps"]))
         nl = c["n_layers"]
         layers = (Tensor * max(1, nl * len(SLOTS)))()
         for i in range(nl):
             for s, slot in enumerate(SLOTS):
-                name = f"blk.{i}.{slot}.weight"
+                name = f"blk.{i}.{slot}"
                 if name in weights:
                     layers[i * len(SLOTS) + s] = T(name)
         self._layers = layers

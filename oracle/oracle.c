@@ -209,23 +209,41 @@ void orc_rope_table(int32_t n_pos, int32_t hd, double theta, float* cos_out,
     }
 }
 
-/* rope (section "The format"): each head's pair (a, b) = (t[i], t[i+hd/2])
- * becomes (a c - b s, a s + b c), computed in f64 and rounded once. */
-void orc_rope(float* t, int32_t n_heads, int32_t hd, const float* cos_row,
-              const float* sin_row)
+/* rope (section "The format"): each head's pair i, (a, b) = (t[i],
+ * t[i+hd/2]) with rotate-half pairing or (t[2i], t[2i+1]) with adjacent
+ * pairing, becomes (a c - b s, a s + b c) with the angle of pair i; computed
+ * in f64 and rounded once. */
+void orc_rope_pairs(float* t, int32_t n_heads, int32_t hd, const float* cos_row,
+                    const float* sin_row, int32_t pairing)
 {
     const int32_t half = hd / 2;
+    int32_t adjacent = pairing == ORC_ROPE_ADJACENT;
+    if (g_mutation == ORC_MUT_ROPE_INTERLEAVED) adjacent = !adjacent;
     for (int32_t j = 0; j < n_heads; ++j) {
         float* v = t + (int64_t)j * hd;
         for (int32_t i = 0; i < half; ++i) {
-            int32_t ia = i, ib = i + half;
-            if (g_mutation == ORC_MUT_ROPE_INTERLEAVED) { ia = 2 * i; ib = 2 * i + 1; }
+            const int32_t ia = adjacent ? 2 * i : i;
+            const int32_t ib = adjacent ? 2 * i + 1 : i + half;
             double a = v[ia], b = v[ib];
             double c = cos_row[i], s = sin_row[i];
             v[ia] = (float)(a * c - b * s);
             v[ib] = (float)(a * s + b * c);
         }
     }
+}
+
+void orc_rope(float* t, int32_t n_heads, int32_t hd, const float* cos_row,
+              const float* sin_row)
+{
+    orc_rope_pairs(t, n_heads, hd, cos_row, sin_row, ORC_ROPE_HALVES);
+}
+
+/* add_bias (section "The operations"): the bias vector added to the matmul
+ * output just computed; one f32 rounding of the exact sum. */
+void orc_add_bias(float* y, const orc_tensor* b, int64_t n)
+{
+    f16_table_init();
+    for (int64_t i = 0; i < n; ++i) y[i] = (float)((double)y[i] + (double)weight_elem(b, i));
 }
 
 /* ---------------------------------------------------------------------------
@@ -331,7 +349,9 @@ orc_model* orc_create(const orc_config* cfg, const orc_tensor* token_embd,
     if (!cfg || cfg->n_layers < 0 || cfg->d_model <= 0 || cfg->n_heads <= 0 ||
         cfg->n_kv_heads <= 0 || cfg->n_heads % cfg->n_kv_heads ||
         cfg->head_dim <= 0 || cfg->head_dim % 2 || cfg->ffn_dim <= 0 ||
-        cfg->vocab <= 0 || cfg->max_ctx <= 0)
+        cfg->vocab <= 0 || cfg->max_ctx <= 0 ||
+        (cfg->arch != ORC_LLAMA && cfg->arch != ORC_QWEN3 && cfg->arch != ORC_QWEN2) ||
+        (cfg->rope_pairing != ORC_ROPE_HALVES && cfg->rope_pairing != ORC_ROPE_ADJACENT))
         return NULL;
     orc_model* m = (orc_model*)calloc(1, sizeof(orc_model));
     if (!m) return NULL;
@@ -427,12 +447,17 @@ static void forward_one(orc_model* m, int32_t tok, float* logits)
         sec = '|';
         trace_op(m, "rms_norm", sec); sec = ',';
         orc_rmsnorm(m->x, &w[ORC_ATTN_NORM], d, eps, m->h);
+        const int bias = (c->arch == ORC_QWEN2);
         trace_op(m, "matmul", sec);
         orc_matvec(&w[ORC_ATTN_Q], qd, d, m->h, m->q);
+        if (bias) { trace_op(m, "add_bias", sec); orc_add_bias(m->q, &w[ORC_ATTN_Q_BIAS], qd); }
         trace_op(m, "matmul", sec);
         orc_matvec(&w[ORC_ATTN_K], kvd, d, m->h, m->k);
+        const int k_bias_late = (g_mutation == ORC_MUT_K_BIAS_AFTER_ROPE);
+        if (bias && !k_bias_late) { trace_op(m, "add_bias", sec); orc_add_bias(m->k, &w[ORC_ATTN_K_BIAS], kvd); }
         trace_op(m, "matmul", sec);
         orc_matvec(&w[ORC_ATTN_V], kvd, d, m->h, m->v);
+        if (bias) { trace_op(m, "add_bias", sec); orc_add_bias(m->v, &w[ORC_ATTN_V_BIAS], kvd); }
         const int qk_norm = (c->arch == ORC_QWEN3);
         const int norm_first = (g_mutation != ORC_MUT_NORM_AFTER_ROPE);
         if (qk_norm && norm_first) {
@@ -442,9 +467,10 @@ static void forward_one(orc_model* m, int32_t tok, float* logits)
             norm_heads(m->k, nkv, hd, &w[ORC_ATTN_K_NORM], eps, hbuf);
         }
         trace_op(m, "rope", sec);
-        orc_rope(m->q, nh, hd, cos_row, sin_row);
+        orc_rope_pairs(m->q, nh, hd, cos_row, sin_row, c->rope_pairing);
         trace_op(m, "rope", sec);
-        orc_rope(m->k, nkv, hd, cos_row, sin_row);
+        orc_rope_pairs(m->k, nkv, hd, cos_row, sin_row, c->rope_pairing);
+        if (bias && k_bias_late) orc_add_bias(m->k, &w[ORC_ATTN_K_BIAS], kvd);
         if (qk_norm && !norm_first) {
             trace_op(m, "norm_heads", sec);
             norm_heads(m->q, nh, hd, &w[ORC_ATTN_Q_NORM], eps, hbuf);

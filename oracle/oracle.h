@@ -5,10 +5,12 @@
  * calls this code; only the tests, the package's smoke check and the
  * benchmark's CPU-baseline leg load it. It shares no code with the GPU path.
  *
- * What it computes: the per-layer step list of a llama / qwen3 decoder as
- * the architecture-definition file lays it out (page "Local inference and
- * architectures", section "The format": prologue embed; block rms_norm,
- * q/k/v matmul, norm_heads q/k (qwen3 only), rope q/k, attention, o matmul,
+ * What it computes: the per-layer step list of a llama / qwen3 / qwen2
+ * decoder as the architecture-definition file lays it out (page "Local
+ * inference and architectures", section "The format": prologue embed; block
+ * rms_norm, q/k/v matmul (each followed by add_bias in qwen2, whose
+ * definition differs from llama's by those three lines, section "Adding an
+ * architecture"), norm_heads q/k (qwen3 only), rope q/k, attention, o matmul,
  * add, rms_norm, gate matmul, silu, up matmul, mul, down matmul, add;
  * epilogue rms_norm, last, logits matmul with the output weight or, if that
  * is absent, the token embedding). Multiplication is in f32 on f32 values
@@ -27,7 +29,10 @@
  * Readings where the pages are silent (each also listed in the design notes):
  *  - RMSNorm: y_i = w_i * (x_i / sqrt(mean(x^2) + eps)), weight multiplies.
  *  - norm_heads: the same RMSNorm over each head_dim slice, one shared weight.
- *  - RoPE: rotate-half pairs (i, i + hd/2), angle p * theta^(-2i/hd).
+ *  - RoPE: rotate-half pairs (i, i + hd/2) by default, or adjacent pairs
+ *    (2i, 2i+1) when the config asks for them; pair i turns by the angle
+ *    p * theta^(-2i/hd) either way.
+ *  - add_bias: y_i = y_i + b_i in f32, right after the matmul it follows.
  *  - attention: causal over positions 0..p including p, scale 1/sqrt(hd),
  *    grouped-query head j reads KV head j / (n_heads / n_kv_heads).
  *  - K is cached after RoPE, V as computed.
@@ -43,7 +48,8 @@ extern "C" {
 #endif
 
 enum { ORC_F32 = 0, ORC_F16 = 1, ORC_Q8 = 2 };
-enum { ORC_LLAMA = 0, ORC_QWEN3 = 1 };
+enum { ORC_LLAMA = 0, ORC_QWEN3 = 1, ORC_QWEN2 = 2 };
+enum { ORC_ROPE_HALVES = 0, ORC_ROPE_ADJACENT = 1 };
 
 enum {
     ORC_OK = 0,
@@ -57,14 +63,15 @@ enum {
 enum {
     ORC_ATTN_NORM = 0, ORC_ATTN_Q, ORC_ATTN_K, ORC_ATTN_V, ORC_ATTN_Q_NORM,
     ORC_ATTN_K_NORM, ORC_ATTN_OUTPUT, ORC_FFN_NORM, ORC_FFN_GATE,
-    ORC_FFN_UP, ORC_FFN_DOWN, ORC_NSLOT
+    ORC_FFN_UP, ORC_FFN_DOWN, ORC_ATTN_Q_BIAS, ORC_ATTN_K_BIAS,
+    ORC_ATTN_V_BIAS, ORC_NSLOT
 };
 
 /* Planted mistakes, used only by tests that prove the pins catch them. */
 enum {
     ORC_MUT_NONE = 0,
     ORC_MUT_NORM_AFTER_ROPE = 1,  /* norm_heads after rope instead of before */
-    ORC_MUT_ROPE_INTERLEAVED = 2, /* pairs (2i, 2i+1) instead of (i, i+hd/2) */
+    ORC_MUT_ROPE_INTERLEAVED = 2, /* the other rope pairing than configured */
     ORC_MUT_NO_ATTN_RESIDUAL = 3, /* x = o instead of x += o */
     ORC_MUT_SCALE_1_OVER_HD = 4,  /* scores / hd instead of / sqrt(hd) */
     ORC_MUT_GQA_MODULO = 5,       /* kv head j % n_kv instead of j / group */
@@ -72,14 +79,15 @@ enum {
     ORC_MUT_EXCLUDE_SELF = 7,     /* attend to 0..p-1 only */
     ORC_MUT_SILU_ON_UP = 8,       /* silu(up) * gate */
     ORC_MUT_ROPE_POS_PLUS1 = 9,   /* rotate by p+1 */
-    ORC_MUT_MATVEC_TRANSPOSE = 10 /* y = W^T h on square weights */
+    ORC_MUT_MATVEC_TRANSPOSE = 10, /* y = W^T h on square weights */
+    ORC_MUT_K_BIAS_AFTER_ROPE = 11 /* qwen2's k bias added after rope */
 };
 
 typedef struct {
     int32_t arch;
     int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn_dim, vocab;
     int32_t max_ctx;
-    int32_t pad_;
+    int32_t rope_pairing;  /* ORC_ROPE_HALVES or ORC_ROPE_ADJACENT */
     double rope_theta, rms_eps;
 } orc_config;
 
@@ -105,6 +113,11 @@ void orc_rope_table(int32_t n_pos, int32_t hd, double theta, float* cos_out,
                     float* sin_out);
 void orc_rope(float* t, int32_t n_heads, int32_t hd, const float* cos_row,
               const float* sin_row);
+/* orc_rope with the pairing given (ORC_ROPE_HALVES or ORC_ROPE_ADJACENT). */
+void orc_rope_pairs(float* t, int32_t n_heads, int32_t hd, const float* cos_row,
+                    const float* sin_row, int32_t pairing);
+/* y[i] = f32(y[i] + b[i]) for i < n; b is f32 or f16. */
+void orc_add_bias(float* y, const orc_tensor* b, int64_t n);
 /* q [n_heads][hd]; K, V: [n_kv][head_stride floats], row t of kv head g at
  * K + g*head_stride + t*hd; n_pos positions; out [n_heads][hd]. */
 void orc_attention(const float* q, int32_t n_heads, int32_t n_kv, int32_t hd,
@@ -113,8 +126,9 @@ void orc_attention(const float* q, int32_t n_heads, int32_t n_kv, int32_t hd,
 void orc_silu(float* g, int64_t n);
 void orc_mul(float* g, const float* u, int64_t n);
 
-/* The model. `layers` holds n_layers * ORC_NSLOT tensors; qwen3-only slots
- * are ignored for llama. `output` with data == NULL means tied weights. */
+/* The model. `layers` holds n_layers * ORC_NSLOT tensors; slots an
+ * architecture does not use (q/k norm outside qwen3, biases outside qwen2)
+ * are ignored. `output` with data == NULL means tied weights. */
 orc_model* orc_create(const orc_config* cfg, const orc_tensor* token_embd,
                       const orc_tensor* output_norm, const orc_tensor* output,
                       const orc_tensor* layers);

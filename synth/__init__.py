@@ -20,6 +20,7 @@ Value recipe (all seeded, chunked so that generation runs on many threads):
 * matrices and embeddings: ``standard_normal`` in f32 times 0.02, rounded to
   the storage dtype (RNE);
 * norm weights: ``1 + 0.02 * standard_normal`` in f32, rounded likewise;
+* q/k/v biases (qwen2): ``BIAS_SCALE * standard_normal``, kept in f32;
 * 8-bit blocks: 32 consecutive int8 along K drawn uniformly from
   [-127, 127] (stream 0) plus one f16 scale ``|N(0, 0.02)| / 127`` per block
   (stream 1); host bytes per block are the scale (little-endian f16) then the
@@ -37,6 +38,9 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 CHUNK = 1 << 22
+# q/k/v biases (qwen2): f32 vectors, N(0, BIAS_SCALE^2); large enough that a
+# dropped bias shows in the logits far above the decode tolerance.
+BIAS_SCALE = 0.5
 Q8_BLOCK = 32
 Q8_BLOCK_BYTES = 34
 
@@ -79,7 +83,8 @@ CONFIGS = {
 
 LAYER_SLOTS = ("attn_norm", "attn_q", "attn_k", "attn_v", "attn_q_norm",
                "attn_k_norm", "attn_output", "ffn_norm", "ffn_gate",
-               "ffn_up", "ffn_down")
+               "ffn_up", "ffn_down", "attn_q.bias", "attn_k.bias",
+               "attn_v.bias")
 
 
 def config(name: str, **overrides) -> dict:
@@ -98,8 +103,9 @@ def tensor_id(name: str) -> int:
         return 1
     if name == "output.weight":
         return 2
-    _, i, slot, _ = name.split(".")
-    return 100 + 16 * int(i) + LAYER_SLOTS.index(slot)
+    _, i, slot, kind = name.split(".")
+    key = slot + ".bias" if kind == "bias" else slot
+    return 100 + 16 * int(i) + LAYER_SLOTS.index(key)
 
 
 def tensor_specs(cfg: dict) -> list[tuple[str, str, int, int]]:
@@ -117,6 +123,10 @@ def tensor_specs(cfg: dict) -> list[tuple[str, str, int, int]]:
                   (b + "attn_q.weight", "matmul", qd, d),
                   (b + "attn_k.weight", "matmul", kvd, d),
                   (b + "attn_v.weight", "matmul", kvd, d)]
+        if cfg["arch"] == "qwen2":
+            specs += [(b + "attn_q.bias", "bias", 1, qd),
+                      (b + "attn_k.bias", "bias", 1, kvd),
+                      (b + "attn_v.bias", "bias", 1, kvd)]
         if cfg["arch"] == "qwen3":
             specs += [(b + "attn_q_norm.weight", "norm", 1, hd),
                       (b + "attn_k_norm.weight", "norm", 1, hd)]
@@ -199,10 +209,12 @@ def make_tensor(cfg: dict, name: str, kind: str, rows: int, cols: int,
             out[:, :, 0:2] = s.view(np.uint8).reshape(rows, nblk, 2)
             out[:, :, 2:] = q.view(np.uint8).reshape(rows, nblk, Q8_BLOCK)
             return out.reshape(rows, nblk * Q8_BLOCK_BYTES)
-        dtype = np.float32 if wd == "f32" else np.float16
+        dtype = np.float32 if wd == "f32" or kind == "bias" else np.float16
         out = np.empty(rows * cols, dtype)
         if kind == "norm":
             _fill_chunks(out, (base, tid, 0), _normal(0.02, 1.0, dtype), pool)
+        elif kind == "bias":
+            _fill_chunks(out, (base, tid, 0), _normal(BIAS_SCALE, 0.0, np.float32), pool)
         else:
             _fill_chunks(out, (base, tid, 0), _normal(0.02, 0.0, dtype), pool)
         return out.reshape(rows, cols)
@@ -252,6 +264,8 @@ def weight_bytes(cfg: dict) -> int:
     for name, kind, rows, cols in tensor_specs(cfg):
         if kind == "matmul" and cfg["wdtype"] == "q8":
             total += rows * cols // Q8_BLOCK * Q8_BLOCK_BYTES
+        elif kind == "bias":
+            total += rows * cols * 4
         else:
             total += rows * cols * (4 if cfg["wdtype"] == "f32" else 2)
     return total
@@ -283,6 +297,10 @@ def make_weights_device(cfg: dict, device="cuda") -> dict:
         z = torch.randn(rows, cols, device=device, generator=g) * 0.02
         if kind == "norm":
             z += 1.0
+        if kind == "bias":
+            z = z * (BIAS_SCALE / 0.02)
+            out[name] = z.to(torch.float32)
+            continue
         out[name] = z.to(dtype)
     return out
 

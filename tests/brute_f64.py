@@ -7,8 +7,9 @@ float64 with no intermediate rounding. Tiny shapes only.
 
 Follows the step list of page "Local inference and architectures", section
 "The format"; readings of the open points are the same as the oracle's
-(rotate-half RoPE pairs, eps inside the root, scale 1/sqrt(hd), GQA head j
-on KV head j // group).
+(rotate-half RoPE pairs unless the config asks for adjacent ones, eps inside
+the root, scale 1/sqrt(hd), GQA head j on KV head j // group, qwen2's biases
+added right after their matmuls).
 """
 from __future__ import annotations
 
@@ -31,14 +32,24 @@ def rms(X: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
     return X / np.sqrt(np.mean(X * X, axis=-1, keepdims=True) + eps) * w
 
 
-def rope_complex(T: np.ndarray, pos: np.ndarray, theta: float) -> np.ndarray:
-    """T [S, heads, hd]; pairs (i, i + hd/2) as the complex a + i b."""
+def rope_complex(T: np.ndarray, pos: np.ndarray, theta: float,
+                 pairing: str = "halves") -> np.ndarray:
+    """T [S, heads, hd]; pair i as the complex a + i b, with (a, b) =
+    (t[i], t[i + hd/2]) for "halves" or (t[2i], t[2i+1]) for "adjacent"."""
     hd = T.shape[-1]
     half = hd // 2
     inv = theta ** (-2.0 * np.arange(half) / hd)
     ang = pos[:, None].astype(np.float64) * inv[None, :]
-    z = T[..., :half] + 1j * T[..., half:]
+    if pairing == "adjacent":
+        z = T[..., 0::2] + 1j * T[..., 1::2]
+    else:
+        z = T[..., :half] + 1j * T[..., half:]
     z = z * np.exp(1j * ang)[:, None, :]
+    if pairing == "adjacent":
+        out = np.empty(T.shape)
+        out[..., 0::2] = z.real
+        out[..., 1::2] = z.imag
+        return out
     return np.concatenate([z.real, z.imag], axis=-1)
 
 
@@ -57,14 +68,22 @@ def forward_all(cfg: dict, W: dict, tokens) -> np.ndarray:
     for i in range(cfg["n_layers"]):
         b = f"blk.{i}."
         H = rms(X, W[b + "attn_norm.weight"], eps)
-        Q = (H @ dequant(W[b + "attn_q.weight"], d).T).reshape(S, nh, hd)
-        Kx = (H @ dequant(W[b + "attn_k.weight"], d).T).reshape(S, nkv, hd)
-        Vx = (H @ dequant(W[b + "attn_v.weight"], d).T).reshape(S, nkv, hd)
+        Q = H @ dequant(W[b + "attn_q.weight"], d).T
+        Kx = H @ dequant(W[b + "attn_k.weight"], d).T
+        Vx = H @ dequant(W[b + "attn_v.weight"], d).T
+        if cfg["arch"] == "qwen2":
+            Q = Q + W[b + "attn_q.bias"].reshape(-1).astype(np.float64)
+            Kx = Kx + W[b + "attn_k.bias"].reshape(-1).astype(np.float64)
+            Vx = Vx + W[b + "attn_v.bias"].reshape(-1).astype(np.float64)
+        Q = Q.reshape(S, nh, hd)
+        Kx = Kx.reshape(S, nkv, hd)
+        Vx = Vx.reshape(S, nkv, hd)
         if cfg["arch"] == "qwen3":
             Q = rms(Q, W[b + "attn_q_norm.weight"], eps)
             Kx = rms(Kx, W[b + "attn_k_norm.weight"], eps)
-        Q = rope_complex(Q, pos, theta)
-        Kx = rope_complex(Kx, pos, theta)
+        pairing = cfg.get("rope_pairing", "halves")
+        Q = rope_complex(Q, pos, theta, pairing)
+        Kx = rope_complex(Kx, pos, theta, pairing)
         A = np.empty((S, nh, hd))
         for j in range(nh):
             g = j // group

@@ -1,9 +1,11 @@
 """Pins of the oracle's whole forward pass (CPU only).
 
 * the float64 brute force (full-sequence, explicit causal mask) on the tiny
-  decoder in both architectures and with 8-bit weights, and on one-layer
+  decoder in all three architectures, both RoPE pairings and with 8-bit
+  weights, and on one-layer
   slices of the real shapes with a small vocabulary;
-* closed forms: zero layers, zero-output layers;
+* closed forms: zero layers, zero-output layers, qwen2 with zero biases ==
+  llama, add_bias on exact sums, adjacent RoPE == halves on permuted lanes;
 * the step list and steps-per-layer counts the pages print;
 * runtime invariants: bulk == token by token, reset, KV positions;
 * planted mistakes in the oracle, each of which one of these pins catches.
@@ -32,10 +34,14 @@ def tiny(**kw):
     return cfg, synth.make_weights(cfg)
 
 
-@pytest.mark.parametrize("arch,wdtype", [("qwen3", "f32"), ("llama", "f32"),
-                                         ("qwen3", "f16"), ("llama", "q8")])
-def test_tiny_matches_f64_brute_force_every_step(arch, wdtype):
-    cfg, W = tiny(arch=arch, wdtype=wdtype)
+@pytest.mark.parametrize("arch,wdtype,pairing", [
+    ("qwen3", "f32", "halves"), ("llama", "f32", "halves"),
+    ("qwen3", "f16", "halves"), ("llama", "q8", "halves"),
+    ("qwen2", "f32", "halves"), ("qwen2", "f16", "adjacent"),
+    ("qwen2", "q8", "halves"), ("llama", "f32", "adjacent"),
+    ("qwen3", "f32", "adjacent")])
+def test_tiny_matches_f64_brute_force_every_step(arch, wdtype, pairing):
+    cfg, W = tiny(arch=arch, wdtype=wdtype, rope_pairing=pairing)
     toks = synth.make_prompt(cfg, 40)
     cfg["max_ctx"] = 48
     got = run_token_by_token(cfg, W, toks)
@@ -109,7 +115,7 @@ def golden_lists():
     return ops, steps
 
 
-@pytest.mark.parametrize("arch", ["qwen3", "llama"])
+@pytest.mark.parametrize("arch", ["qwen3", "llama", "qwen2"])
 def test_step_list_matches_the_printed_definition(arch):
     gold, steps = golden_lists()
     cfg, W = tiny(arch=arch)
@@ -122,6 +128,60 @@ def test_step_list_matches_the_printed_definition(arch):
         assert blk.split(",") == gold[f"{arch} block"]
         assert len(blk.split(",")) == steps[arch]
     assert sections[-1].split(",") == gold[f"{arch} epilogue"]
+
+
+def test_qwen2_with_zero_biases_is_llama_bitwise():
+    # qwen2's definition is llama's plus three bias lines (page "Local
+    # inference and architectures", "The format"): with every bias zero the
+    # two must give the same bits (x + 0 == x in f32).
+    cfg, W = tiny(arch="qwen2")
+    for k in list(W):
+        if k.endswith(".bias"):
+            W[k] = np.zeros_like(W[k])
+    toks = synth.make_prompt(cfg, 8)
+    a = run_token_by_token(cfg, W, toks)
+    Wl = {k: v for k, v in W.items() if not k.endswith(".bias")}
+    b = run_token_by_token(dict(cfg, arch="llama"), Wl, toks)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_qwen2_biases_move_the_logits():
+    cfg, W = tiny(arch="qwen2")
+    toks = synth.make_prompt(cfg, 4)
+    a = run_token_by_token(cfg, W, toks)
+    Wl = {k: v for k, v in W.items() if not k.endswith(".bias")}
+    b = run_token_by_token(dict(cfg, arch="llama"), Wl, toks)
+    assert rel_l2(a[-1], b[-1]) > 1e-2
+
+
+def test_add_bias_exact():
+    # One rounding of an exact sum: values whose sum is exact in f32.
+    y = np.array([1.0, -2.5, 3.0e7, 0.125], np.float32)
+    b = np.array([0.5, 2.5, 1.0, -0.125], np.float32)
+    assert np.array_equal(oracle.add_bias(y.copy(), b),
+                          np.array([1.5, 0.0, 3.0e7 + 1.0, 0.0], np.float32))
+    # 1 + 2^-24 rounds to 1 (ties to even), 1 + 3*2^-24 to 1 + 2^-22
+    y = np.ones(2, np.float32)
+    b = np.array([2.0 ** -24, 3 * 2.0 ** -24], np.float32)
+    assert np.array_equal(oracle.add_bias(y, b),
+                          np.array([1.0, 1.0 + 2.0 ** -22], np.float32))
+
+
+def test_rope_adjacent_is_halves_on_permuted_lanes():
+    # Pairing (2i, 2i+1) is pairing (i, i + hd/2) after the permutation that
+    # deals even lanes to the first half and odd lanes to the second.
+    hd, heads = 16, 3
+    cos, sin = oracle.rope_table(9, hd, 10000.0)
+    t = np.random.default_rng(4).standard_normal(heads * hd).astype(np.float32)
+    perm = np.concatenate([np.arange(0, hd, 2), np.arange(1, hd, 2)])
+    for p in (0, 1, 8):
+        adj = oracle.rope(t.copy(), hd, cos[p], sin[p], pairing="adjacent")
+        tp = t.reshape(heads, hd)[:, perm].reshape(-1).copy()
+        hal = oracle.rope(tp, hd, cos[p], sin[p], pairing="halves")
+        assert np.array_equal(adj.reshape(heads, hd)[:, perm].reshape(-1), hal)
+        if p:
+            assert not np.array_equal(
+                adj, oracle.rope(t.copy(), hd, cos[p], sin[p]))
 
 
 def test_norm_heads_before_rope_matters():
@@ -250,7 +310,8 @@ def test_each_planted_mistake_is_caught(mutation):
     try:
         caught = (_rmsnorm_closed_form_fails() or _one_hot_fails()
                   or _kv_row_fails()
-                  or _brute_tiny_fails("qwen3") or _brute_tiny_fails("llama"))
+                  or _brute_tiny_fails("qwen3") or _brute_tiny_fails("llama")
+                  or _brute_tiny_fails("qwen2"))
     finally:
         oracle.set_mutation("none")
     assert caught, mutation
@@ -262,3 +323,4 @@ def test_pins_pass_without_mistakes():
     assert not _kv_row_fails()
     assert not _brute_tiny_fails("qwen3")
     assert not _brute_tiny_fails("llama")
+    assert not _brute_tiny_fails("qwen2")
