@@ -40,8 +40,8 @@ def log(*a):
 
 def step_bytes(cfg: dict, p: int) -> int:
     """Algorithmic HBM bytes of one decode step at position p: every matmul
-    weight once (f16, or 8-bit values + f16 scales), the norm weights as held
-    on the device (f32), one embedding row, the KV rows 0..p-1 read and row p
+    weight once (f16, or 8-bit values + f16 scales), the norm weights and
+    biases as held on the device (f32), one embedding row, the KV rows 0..p-1 read and row p
     written (f32), and the logits written."""
     d, F, V, L = cfg["d_model"], cfg["ffn_dim"], cfg["vocab"], cfg["n_layers"]
     hd = cfg["head_dim"]
@@ -52,6 +52,8 @@ def step_bytes(cfg: dict, p: int) -> int:
     norms = (L * 2 * d + d) * 4
     if cfg["arch"] == "qwen3":
         norms += L * 2 * hd * 4
+    if cfg["arch"] == "qwen2":  # q/k/v biases, f32 on the device
+        norms += L * (qd + 2 * kvd) * 4
     kv_tok = L * 2 * kvd * 4
     return wbytes + norms + d * 2 + (p + 1) * kv_tok + V * 4
 
@@ -188,7 +190,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--context", type=int, default=4096)
     ap.add_argument("--workload", default="llama_8b",
-                    choices=["llama_8b", "llama_8b_q8", "qwen3_8b", "qwen3_0p6b"])
+                    choices=["llama_8b", "llama_8b_q8", "qwen3_8b", "qwen3_0p6b", "qwen2_7b"])
     ap.add_argument("--context-from", default="restore", choices=["prefill", "restore"],
                     help="build the context by bulk prefill (default) or by writing "
                          "synthetic KV rows")

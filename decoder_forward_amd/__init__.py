@@ -27,7 +27,10 @@ STATUS_NAMES = {
     7: "INVALID_CONFIG", 8: "CONTEXT_FULL", 9: "BUSY", 10: "INVALID_ARGUMENT",
     11: "DEVICE",
 }
-DF_ARCH_LLAMA, DF_ARCH_QWEN3 = 0, 1
+DF_ARCH_LLAMA, DF_ARCH_QWEN3, DF_ARCH_QWEN2 = 0, 1, 2
+ARCHS = {"llama": DF_ARCH_LLAMA, "qwen3": DF_ARCH_QWEN3, "qwen2": DF_ARCH_QWEN2}
+DF_ROPE_HALVES, DF_ROPE_ADJACENT = 0, 1
+ROPE_PAIRINGS = {"halves": DF_ROPE_HALVES, "adjacent": DF_ROPE_ADJACENT}
 DF_F32, DF_F16, DF_Q8_32 = 0, 1, 2
 
 # Every entry point of include/decfwd.h.
@@ -53,7 +56,7 @@ class df_config(C.Structure):
                 ("d_model", C.c_int32), ("n_heads", C.c_int32),
                 ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
                 ("ffn_dim", C.c_int32), ("vocab", C.c_int32),
-                ("max_ctx", C.c_int32), ("reserved", C.c_int32),
+                ("max_ctx", C.c_int32), ("rope_pairing", C.c_int32),
                 ("rope_theta", C.c_double), ("rms_eps", C.c_double)]
 
 
@@ -122,11 +125,12 @@ def _check(rc: int, handle=None):
 
 
 def make_config(cfg: dict, max_ctx: int | None = None) -> df_config:
-    return df_config(DF_ARCH_QWEN3 if cfg["arch"] == "qwen3" else DF_ARCH_LLAMA,
+    return df_config(ARCHS[cfg["arch"]],
                      cfg["n_layers"], cfg["d_model"], cfg["n_heads"],
                      cfg["n_kv_heads"], cfg["head_dim"], cfg["ffn_dim"],
                      cfg["vocab"], max_ctx if max_ctx is not None else cfg["max_ctx"],
-                     0, float(cfg["rope_theta"]), float(cfg["rms_eps"]))
+                     ROPE_PAIRINGS[cfg.get("rope_pairing", "halves")],
+                     float(cfg["rope_theta"]), float(cfg["rms_eps"]))
 
 
 def _tensor_entry(name: str, a, keep: list) -> df_tensor:

@@ -32,7 +32,9 @@ struct AttnItem {
     const float* qkv;      // this step's q (all heads) | k | v
     const float* q_norm;   // norm_heads weights (qwen3), null for llama
     const float* k_norm;
+    const float* bias;     // qwen2's q | k | v bias, laid out as qkv; else null
     float eps;
+    int adjacent;          // rope pairs (2i, 2i+1) if set, else (i, i + hd/2)
     const float* cos_row;  // rope cos / sin at position p, hd/2 each
     const float* sin_row;
     float* kc;             // this KV head's cache rows [max_ctx][hd]
@@ -108,23 +110,30 @@ __device__ void attn_core(const AttnItem& a, float* lds, int tid)
     load(0, ka, va);
 
     // q of the group's heads (and, for the owner, this step's k): one wave
-    // per vector, lane i < hd/2 holding the rope pair (i, i + hd/2);
-    // norm_heads, then rope, then into LDS.
+    // per vector, lane i < hd/2 holding rope pair i, elements (i0, i1);
+    // bias (qwen2), norm_heads (qwen3), then rope, then into LDS.
     const int nv = G + (owner ? 1 : 0);
+    const int i0 = a.adjacent ? 2 * lane : lane;
+    const int i1 = a.adjacent ? 2 * lane + 1 : lane + HALF;
     for (int j = w; j < nv; j += NW) {
-        const float* src = a.qkv + (j < G ? (a.g * G + j) * HD : a.qd + a.g * HD);
+        const int off = j < G ? (a.g * G + j) * HD : a.qd + a.g * HD;
+        const float* src = a.qkv + off;
         float x0 = 0.f, x1 = 0.f;
         if (lane < HALF) {
-            x0 = act_ld<COH>(src + lane);
-            x1 = act_ld<COH>(src + lane + HALF);
+            x0 = act_ld<COH>(src + i0);
+            x1 = act_ld<COH>(src + i1);
+            if (a.bias) {
+                x0 += *gmem(a.bias + off + i0);
+                x1 += *gmem(a.bias + off + i1);
+            }
         }
         if (a.q_norm) {
             const float ss = wave_sum(fmaf(x0, x0, x1 * x1));
             const float r = 1.0f / sqrtf(ss / static_cast<float>(HD) + a.eps);
             if (lane < HALF) {
                 const float* nw = j < G ? a.q_norm : a.k_norm;
-                x0 = *gmem(nw + lane) * (x0 * r);
-                x1 = *gmem(nw + lane + HALF) * (x1 * r);
+                x0 = *gmem(nw + i0) * (x0 * r);
+                x1 = *gmem(nw + i1) * (x1 * r);
             }
         }
         if (lane < HALF) {
@@ -132,17 +141,19 @@ __device__ void attn_core(const AttnItem& a, float* lds, int tid)
             const float y0 = fmaf(x0, c, -x1 * s);
             const float y1 = fmaf(x0, s, x1 * c);
             float* dst = j < G ? qs + j * HD : knew;
-            dst[lane] = y0;
-            dst[lane + HALF] = y1;
+            dst[i0] = y0;
+            dst[i1] = y1;
             if (j == G) {  // append k at slot p
-                *gmem(a.kc + int64_t(p) * HD + lane) = y0;
-                *gmem(a.kc + int64_t(p) * HD + lane + HALF) = y1;
+                *gmem(a.kc + int64_t(p) * HD + i0) = y0;
+                *gmem(a.kc + int64_t(p) * HD + i1) = y1;
             }
         }
     }
     if (owner) {
+        const int voff = a.qd + a.kvd + a.g * HD;
         for (int i = tid; i < HD; i += NW * WAVE) {
-            const float v = act_ld<COH>(a.qkv + a.qd + a.kvd + a.g * HD + i);
+            float v = act_ld<COH>(a.qkv + voff + i);
+            if (a.bias) v += *gmem(a.bias + voff + i);
             vnew[i] = v;
             *gmem(a.vc + int64_t(p) * HD + i) = v;  // append v at slot p
         }

@@ -41,6 +41,12 @@ hipError_t launch_mv_t(const Weight& W, const float* x, const float* nw,
     int64_t blocks = 0;
     const MvLayout L = make_mv_layout(WT, W.cols, n_out, up_rows, 512, 8, &blocks);
     const size_t lds = mv_lds_bytes(L, MODE);
+    if (lds > 65536) {  // x of more than 16384 values: opt in to the larger LDS
+        const hipError_t r = hipFuncSetAttribute(
+            reinterpret_cast<const void*>(&matvec_kernel<WT, MODE, NORM>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+        if (r != hipSuccess) return r;
+    }
     DFK_LAUNCH((matvec_kernel<WT, MODE, NORM>), dim3(unsigned(blocks)),
                        dim3(512), lds, s, W.data, W.scales, L, x, nw, eps, out);
     return hipGetLastError();
@@ -114,7 +120,9 @@ attn_decode_kernel(AttnDecodeArgs a)
     it.qkv = a.qkv;
     it.q_norm = a.q_norm;
     it.k_norm = a.k_norm;
+    it.bias = a.bias;
     it.eps = a.eps;
+    it.adjacent = a.adjacent;
     it.cos_row = a.cos_t + int64_t(p) * (HD / 2);
     it.sin_row = a.sin_t + int64_t(p) * (HD / 2);
     it.kc = a.kc + int64_t(g) * a.max_ctx * HD;
@@ -385,7 +393,11 @@ hipError_t launch_attn_hd(const AttnDecodeArgs& a, dim3 grid, hipStream_t s)
     switch (a.n_heads / a.n_kv) {
     case 1: DFK_LAUNCH((attn_decode_kernel<HD, 1>), grid, dim3(256), 0, s, a); break;
     case 2: DFK_LAUNCH((attn_decode_kernel<HD, 2>), grid, dim3(256), 0, s, a); break;
+    case 3: DFK_LAUNCH((attn_decode_kernel<HD, 3>), grid, dim3(256), 0, s, a); break;
     case 4: DFK_LAUNCH((attn_decode_kernel<HD, 4>), grid, dim3(256), 0, s, a); break;
+    case 5: DFK_LAUNCH((attn_decode_kernel<HD, 5>), grid, dim3(256), 0, s, a); break;
+    case 6: DFK_LAUNCH((attn_decode_kernel<HD, 6>), grid, dim3(256), 0, s, a); break;
+    case 7: DFK_LAUNCH((attn_decode_kernel<HD, 7>), grid, dim3(256), 0, s, a); break;
     case 8: DFK_LAUNCH((attn_decode_kernel<HD, 8>), grid, dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
     }

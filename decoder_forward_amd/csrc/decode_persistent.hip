@@ -200,7 +200,9 @@ decode_step_kernel(const StepArgs* __restrict__ Ap, float* logits_out, int advan
             it.qkv = A.qkv;
             it.q_norm = Ly.q_norm;
             it.k_norm = Ly.k_norm;
+            it.bias = Ly.bias;
             it.eps = A.eps;
+            it.adjacent = A.adjacent;
             it.cos_row = A.cos_t + int64_t(p) * (HD / 2);
             it.sin_row = A.sin_t + int64_t(p) * (HD / 2);
             it.kc = Ly.kc + int64_t(g) * A.max_ctx * HD;
@@ -324,7 +326,11 @@ const void* pick(int wdtype, int odtype, int hd, int G)
     switch (G) {                                                          \
     case 1: return step_kernel_ptr<WT, WO, HD, 1>();                      \
     case 2: return step_kernel_ptr<WT, WO, HD, 2>();                      \
+    case 3: return step_kernel_ptr<WT, WO, HD, 3>();                      \
     case 4: return step_kernel_ptr<WT, WO, HD, 4>();                      \
+    case 5: return step_kernel_ptr<WT, WO, HD, 5>();                      \
+    case 6: return step_kernel_ptr<WT, WO, HD, 6>();                      \
+    case 7: return step_kernel_ptr<WT, WO, HD, 7>();                      \
     case 8: return step_kernel_ptr<WT, WO, HD, 8>();                      \
     }                                                                     \
     return nullptr;

@@ -108,7 +108,9 @@ struct AttnDecodeArgs {
     const float* qkv;          // [n_heads*hd | n_kv*hd | n_kv*hd]
     const float* q_norm;       // [hd] or null (llama)
     const float* k_norm;
+    const float* bias;         // [qd + 2 kvd] q|k|v bias (qwen2) or null
     float eps;
+    int adjacent;              // rope pairing: (2i, 2i+1) if set, else (i, i + hd/2)
     const float* cos_t;        // [max_ctx][hd/2]
     const float* sin_t;
     float* kc;                 // this layer's K cache [n_kv][max_ctx][hd]
@@ -144,6 +146,7 @@ struct StepLayer {
     const float* ffn_norm;
     const float* q_norm;                     // null for llama
     const float* k_norm;
+    const float* bias;                       // q|k|v bias (qwen2), else null
     float* kc;                               // layer K cache [n_kv][max_ctx][hd]
     float* vc;
 };
@@ -152,6 +155,7 @@ struct StepArgs {
     const StepLayer* layers;
     int n_layers, d, qd, kvd, F, V, hd, n_heads, n_kv, max_ctx;
     float eps;
+    int adjacent;                            // rope pairing, as in AttnDecodeArgs
     const void* embd;                        // token embedding (f16 or f32)
     int embd_dtype;
     const void* wout; const uint16_t* sout;  // logits matrix
@@ -217,7 +221,9 @@ struct QkPostArgs {
     const float* qkv;     // [S][qd | kvd | kvd] f32
     const float* q_norm;  // [hd] or null
     const float* k_norm;
+    const float* bias;    // [qd | kvd | kvd] bias (qwen2) or null
     float eps;
+    int adjacent;         // rope pairing, as in AttnDecodeArgs
     const float* cos_t;
     const float* sin_t;
     float* kc;            // layer K cache [n_kv][max_ctx][hd]

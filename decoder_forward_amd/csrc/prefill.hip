@@ -364,9 +364,9 @@ hipError_t launch_gemm_t(const GemmArgs& g, hipStream_t s)
 }
 
 // ---------------------------------------------------------------------------
-// Per row s (position p0 + s) and head: norm_heads (qwen3), RoPE at the
-// position, then q -> Q16[s][head][d] (f16, the attention's A operand) and
-// k (after RoPE), v -> the f32 KV cache at slot p0 + s.
+// Per row s (position p0 + s) and head: bias (qwen2), norm_heads (qwen3),
+// RoPE at the position, then q -> Q16[s][head][d] (f16, the attention's A
+// operand) and k (after RoPE), v (+ bias) -> the f32 KV cache at slot p0 + s.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(64)
 qk_post_rows_kernel(QkPostArgs a)
@@ -380,8 +380,9 @@ qk_post_rows_kernel(QkPostArgs a)
     const int pos = a.p0 + s;
     const bool is_q = h < a.n_heads;
     const int g = h - a.n_heads;
-    const float* src = a.qkv + int64_t(s) * (qd + 2 * kvd) + (is_q ? h * HD : qd + g * HD);
-    for (int i = lane; i < HD; i += WAVE) v[i] = src[i];
+    const int off = is_q ? h * HD : qd + g * HD;
+    const float* src = a.qkv + int64_t(s) * (qd + 2 * kvd) + off;
+    for (int i = lane; i < HD; i += WAVE) v[i] = a.bias ? src[i] + a.bias[off + i] : src[i];
     __syncthreads();
     const float* nw = is_q ? a.q_norm : a.k_norm;
     if (nw) {
@@ -395,9 +396,10 @@ qk_post_rows_kernel(QkPostArgs a)
     const float* cs = a.cos_t + int64_t(pos) * half;
     const float* sn = a.sin_t + int64_t(pos) * half;
     for (int i = lane; i < half; i += WAVE) {
-        const float x0 = v[i], x1 = v[i + half];
-        v[i] = fmaf(x0, cs[i], -x1 * sn[i]);
-        v[i + half] = fmaf(x0, sn[i], x1 * cs[i]);
+        const int i0 = a.adjacent ? 2 * i : i, i1 = a.adjacent ? 2 * i + 1 : i + half;
+        const float x0 = v[i0], x1 = v[i1];
+        v[i0] = fmaf(x0, cs[i], -x1 * sn[i]);
+        v[i1] = fmaf(x0, sn[i], x1 * cs[i]);
     }
     __syncthreads();
     if (is_q) {
@@ -405,10 +407,11 @@ qk_post_rows_kernel(QkPostArgs a)
         for (int i = lane; i < HD; i += WAVE) q[i] = f2h(v[i]);
     } else {
         const int64_t slot = (int64_t(g) * a.max_ctx + pos) * HD;
-        const float* vs = a.qkv + int64_t(s) * (qd + 2 * kvd) + qd + kvd + g * HD;
+        const int voff = qd + kvd + g * HD;
+        const float* vs = a.qkv + int64_t(s) * (qd + 2 * kvd) + voff;
         for (int i = lane; i < HD; i += WAVE) {
             a.kc[slot + i] = v[i];
-            a.vc[slot + i] = vs[i];
+            a.vc[slot + i] = a.bias ? vs[i] + a.bias[voff + i] : vs[i];
         }
     }
 }
@@ -563,7 +566,11 @@ hipError_t launch_attn_prefill_hd(const AttnPrefillArgs& a, hipStream_t s)
     switch (a.n_heads / a.n_kv) {
     case 1: DFK_LAUNCH((attn_prefill_kernel<HD, 1>), grid, dim3(64), 0, s, a); break;
     case 2: DFK_LAUNCH((attn_prefill_kernel<HD, 2>), grid, dim3(128), 0, s, a); break;
+    case 3: DFK_LAUNCH((attn_prefill_kernel<HD, 3>), grid, dim3(192), 0, s, a); break;
     case 4: DFK_LAUNCH((attn_prefill_kernel<HD, 4>), grid, dim3(256), 0, s, a); break;
+    case 5: DFK_LAUNCH((attn_prefill_kernel<HD, 5>), grid, dim3(320), 0, s, a); break;
+    case 6: DFK_LAUNCH((attn_prefill_kernel<HD, 6>), grid, dim3(384), 0, s, a); break;
+    case 7: DFK_LAUNCH((attn_prefill_kernel<HD, 7>), grid, dim3(448), 0, s, a); break;
     case 8: DFK_LAUNCH((attn_prefill_kernel<HD, 8>), grid, dim3(512), 0, s, a); break;
     default: return hipErrorInvalidValue;
     }

@@ -107,6 +107,7 @@ struct Layer {
     float* ffn_norm = nullptr;
     float* q_norm = nullptr;
     float* k_norm = nullptr;
+    float* bqkv = nullptr;     // qwen2: [q bias | k bias | v bias]
 };
 
 }  // namespace
@@ -219,12 +220,16 @@ bool cfg_fail(Fail* e, const char* field, const std::string& reason)
 bool validate_config(const df_config* c, Fail* e)
 {
     if (!c) { *e = {DF_ERR_INVALID_ARGUMENT, "config is NULL"}; return false; }
-    if (c->arch != DF_ARCH_LLAMA && c->arch != DF_ARCH_QWEN3)
-        return cfg_fail(e, "arch", fmt("= %d: expected 0 (llama) or 1 (qwen3)", c->arch));
+    if (c->arch != DF_ARCH_LLAMA && c->arch != DF_ARCH_QWEN3 && c->arch != DF_ARCH_QWEN2)
+        return cfg_fail(e, "arch", fmt("= %d: expected 0 (llama), 1 (qwen3) or 2 (qwen2)", c->arch));
+    if (c->rope_pairing != DF_ROPE_HALVES && c->rope_pairing != DF_ROPE_ADJACENT)
+        return cfg_fail(e, "rope_pairing", fmt("= %d: expected 0 (halves) or 1 (adjacent)",
+                                               c->rope_pairing));
     if (c->n_layers < 0 || c->n_layers > 4096)
         return cfg_fail(e, "n_layers", fmt("= %d: expected 0..4096", c->n_layers));
-    if (c->d_model <= 0 || c->d_model % 32 || c->d_model > 16384)
-        return cfg_fail(e, "d_model", fmt("= %d: expected a multiple of 32 in 32..16384", c->d_model));
+    if (c->d_model <= 0 || c->d_model % 32 || c->d_model > DF_MAX_WIDTH)
+        return cfg_fail(e, "d_model", fmt("= %d: expected a multiple of 32 in 32..%d", c->d_model,
+                                          DF_MAX_WIDTH));
     if (c->head_dim != 16 && c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128)
         return cfg_fail(e, "head_dim", fmt("= %d: expected 16, 32, 64 or 128", c->head_dim));
     if (c->n_kv_heads <= 0 || c->n_heads <= 0 || c->n_heads % c->n_kv_heads)
@@ -232,15 +237,16 @@ bool validate_config(const df_config* c, Fail* e)
                                           c->n_heads, c->n_kv_heads));
     {
         const int G = c->n_heads / c->n_kv_heads;
-        if (G != 1 && G != 2 && G != 4 && G != 8)
-            return cfg_fail(e, "n_heads", fmt("/ n_kv_heads = %d: expected 1, 2, 4 or 8 query heads "
-                                              "per KV head", G));
+        if (G > ATTN_MAX_GROUP)
+            return cfg_fail(e, "n_heads", fmt("/ n_kv_heads = %d: expected at most %d query heads "
+                                              "per KV head", G, ATTN_MAX_GROUP));
     }
-    if (int64_t(c->n_heads) * c->head_dim > 16384 || (c->n_heads * c->head_dim) % 32)
-        return cfg_fail(e, "n_heads", fmt("* head_dim = %lld: expected a multiple of 32 up to 16384",
-                                          (long long)c->n_heads * c->head_dim));
-    if (c->ffn_dim <= 0 || c->ffn_dim % 32 || c->ffn_dim > 16384)
-        return cfg_fail(e, "ffn_dim", fmt("= %d: expected a multiple of 32 in 32..16384", c->ffn_dim));
+    if (int64_t(c->n_heads) * c->head_dim > DF_MAX_WIDTH || (c->n_heads * c->head_dim) % 32)
+        return cfg_fail(e, "n_heads", fmt("* head_dim = %lld: expected a multiple of 32 up to %d",
+                                          (long long)c->n_heads * c->head_dim, DF_MAX_WIDTH));
+    if (c->ffn_dim <= 0 || c->ffn_dim % 32 || c->ffn_dim > DF_MAX_WIDTH)
+        return cfg_fail(e, "ffn_dim", fmt("= %d: expected a multiple of 32 in 32..%d", c->ffn_dim,
+                                          DF_MAX_WIDTH));
     if (c->vocab <= 0)
         return cfg_fail(e, "vocab", fmt("= %d: expected >= 1", c->vocab));
     if (c->max_ctx <= 0 || c->max_ctx > (1 << 20))
@@ -264,7 +270,12 @@ uint64_t expected_bytes(int dtype, int64_t rows, int64_t cols)
     return uint64_t(rows) * uint64_t(cols / 32) * 34;
 }
 
-enum Kind { K_EMBED, K_NORM, K_MATMUL };
+enum Kind { K_EMBED, K_NORM, K_MATMUL, K_BIAS };
+
+const char* arch_name(int a)
+{
+    return a == DF_ARCH_QWEN3 ? "qwen3" : a == DF_ARCH_QWEN2 ? "qwen2" : "llama";
+}
 
 struct Need {
     std::string name;
@@ -287,6 +298,11 @@ std::vector<Need> required_tensors(const df_config* c)
         v.push_back({b + "attn_q.weight", K_MATMUL, qd, d, true, L + " q matmul"});
         v.push_back({b + "attn_k.weight", K_MATMUL, kvd, d, true, L + " k matmul"});
         v.push_back({b + "attn_v.weight", K_MATMUL, kvd, d, true, L + " v matmul"});
+        if (c->arch == DF_ARCH_QWEN2) {
+            v.push_back({b + "attn_q.bias", K_BIAS, 1, qd, true, L + " add_bias q"});
+            v.push_back({b + "attn_k.bias", K_BIAS, 1, kvd, true, L + " add_bias k"});
+            v.push_back({b + "attn_v.bias", K_BIAS, 1, kvd, true, L + " add_bias v"});
+        }
         if (c->arch == DF_ARCH_QWEN3) {
             v.push_back({b + "attn_q_norm.weight", K_NORM, 1, hd, true, L + " norm_heads q"});
             v.push_back({b + "attn_k_norm.weight", K_NORM, 1, hd, true, L + " norm_heads k"});
@@ -319,7 +335,7 @@ bool validate_tensors(const df_config* c, const df_tensor* t, size_t n,
         if (it == by_name.end()) {
             *e = {DF_ERR_INVALID_ARGUMENT,
                   fmt("tensor '%s' is not part of the %s step list with %d layers", name.c_str(),
-                      c->arch == DF_ARCH_QWEN3 ? "qwen3" : "llama", c->n_layers)};
+                      arch_name(c->arch), c->n_layers)};
             return false;
         }
         if (found->count(name)) {
@@ -336,7 +352,7 @@ bool validate_tensors(const df_config* c, const df_tensor* t, size_t n,
         if (nd.kind != K_MATMUL && x.dtype == DF_Q8_32) {
             *e = {DF_ERR_UNSUPPORTED_OP,
                   fmt("tensor '%s' (%s): q8_32 is supported for matmul weights only; "
-                      "embeddings and norm weights are f32 or f16",
+                      "embeddings, norm weights and biases are f32 or f16",
                       name.c_str(), nd.required_by.c_str())};
             return false;
         }
@@ -470,11 +486,10 @@ bool upload_matrix(df_model* m, const std::vector<const df_tensor*>& parts,
     return true;
 }
 
-bool upload_norm(df_model* m, const df_tensor* t, float** out, Fail* e)
+// Convert one f32/f16 vector into f32 device memory at dst.
+bool upload_vector_into(df_model* m, const df_tensor* t, float* dst, Fail* e)
 {
     const int64_t n = t->rows * t->cols;
-    float* dst = static_cast<float*>(dev_alloc(m, size_t(n) * 4, t->name, e));
-    if (!dst) return false;
     const void* src = t->data;
     void* staging = nullptr;
     if (!t->on_device) {
@@ -492,9 +507,30 @@ bool upload_norm(df_model* m, const df_tensor* t, float** out, Fail* e)
         (void)hipFree(staging);
     }
     if (!check(r, t->name, e)) return false;
-    *out = dst;
     m->weight_bytes += n * 4;
     return true;
+}
+
+// Concatenate vectors into one f32 device vector.
+bool upload_vectors(df_model* m, const std::vector<const df_tensor*>& parts, float** out,
+                    const char* what, Fail* e)
+{
+    int64_t n = 0;
+    for (auto* t : parts) n += t->rows * t->cols;
+    float* dst = static_cast<float*>(dev_alloc(m, size_t(n) * 4, what, e));
+    if (!dst) return false;
+    int64_t off = 0;
+    for (auto* t : parts) {
+        if (!upload_vector_into(m, t, dst + off, e)) return false;
+        off += t->rows * t->cols;
+    }
+    *out = dst;
+    return true;
+}
+
+bool upload_norm(df_model* m, const df_tensor* t, float** out, Fail* e)
+{
+    return upload_vectors(m, {t}, out, t->name, e);
 }
 
 bool upload_embedding(df_model* m, const df_tensor* t, Weight* w, Fail* e)
@@ -515,6 +551,10 @@ bool build_model(df_model* m, const std::map<std::string, const df_tensor*>& T, 
         if (!upload_norm(m, get(b + "attn_norm.weight"), &L.attn_norm, e)) return false;
         if (!upload_matrix(m, {get(b + "attn_q.weight"), get(b + "attn_k.weight"),
                                get(b + "attn_v.weight")}, &L.wqkv, "q/k/v weights", e))
+            return false;
+        if (c.arch == DF_ARCH_QWEN2 &&
+            !upload_vectors(m, {get(b + "attn_q.bias"), get(b + "attn_k.bias"),
+                                get(b + "attn_v.bias")}, &L.bqkv, "q/k/v biases", e))
             return false;
         if (c.arch == DF_ARCH_QWEN3) {
             if (!upload_norm(m, get(b + "attn_q_norm.weight"), &L.q_norm, e)) return false;
@@ -613,6 +653,7 @@ bool setup_step(df_model* m, Fail* e)
     a.n_kv = c.n_kv_heads;
     a.max_ctx = c.max_ctx;
     a.eps = float(c.rms_eps);
+    a.adjacent = c.rope_pairing == DF_ROPE_ADJACENT;
     a.embd = m->embd.data;
     a.embd_dtype = m->embd.dtype;
     a.wout = m->out.data;
@@ -660,6 +701,7 @@ bool setup_step(df_model* m, Fail* e)
         s.wd = L.wd.data; s.sd = L.wd.scales;
         s.attn_norm = L.attn_norm;
         s.ffn_norm = L.ffn_norm;
+        s.bias = L.bqkv;
         s.q_norm = L.q_norm;
         s.k_norm = L.k_norm;
         s.kc = m->kc + size_t(l) * kv_layer;
@@ -745,7 +787,9 @@ hipError_t launch_class(df_model* m, const StepBufs& b, int kernel, int l, int g
         a.qkv = b.qkv;
         a.q_norm = L->q_norm;
         a.k_norm = L->k_norm;
+        a.bias = L->bqkv;
         a.eps = eps;
+        a.adjacent = c.rope_pairing == DF_ROPE_ADJACENT;
         a.cos_t = m->cos_t;
         a.sin_t = m->sin_t;
         a.kc = m->kc + size_t(l) * kv_layer;
@@ -939,6 +983,7 @@ df_status prefill(df_model* m, const int32_t* tokens, int32_t n, float* logits)
         if (r != hipSuccess) break;
         QkPostArgs qa{};
         qa.qkv = qkv; qa.q_norm = L.q_norm; qa.k_norm = L.k_norm; qa.eps = eps;
+        qa.bias = L.bqkv; qa.adjacent = c.rope_pairing == DF_ROPE_ADJACENT;
         qa.cos_t = m->cos_t; qa.sin_t = m->sin_t;
         qa.kc = m->kc + size_t(l) * kv_layer; qa.vc = m->vc + size_t(l) * kv_layer;
         qa.q16 = q16; qa.S = S; qa.p0 = p0; qa.n_heads = c.n_heads; qa.n_kv = c.n_kv_heads;

@@ -60,10 +60,27 @@ typedef int32_t df_status;
 #define DF_ERR_INVALID_ARGUMENT 10       /* NULL / out-of-range argument, bad token id */
 #define DF_ERR_DEVICE 11                 /* a HIP call failed after load */
 
-/* Architectures: the two step lists (llama 16 steps per layer, qwen3 18,
- * page "Local inference and architectures", "What is in effect right now"). */
+/* Architectures: the step lists of page "Local inference and
+ * architectures" ("What is in effect right now": llama 16 steps per layer,
+ * qwen3 18, qwen2 19). qwen3 adds norm_heads on q and k before rope (section
+ * "The format"); qwen2 adds a bias to each of the q, k and v matmul outputs
+ * (the three bias lines of the same section), tensors
+ * "blk.<i>.attn_{q,k,v}.bias", f32 or f16 vectors of n_heads*head_dim and
+ * n_kv_heads*head_dim values. */
 #define DF_ARCH_LLAMA 0
 #define DF_ARCH_QWEN3 1
+#define DF_ARCH_QWEN2 2
+
+/* RoPE pairing within a head (the pages name rope without fixing the
+ * pairing): DF_ROPE_HALVES rotates (t[i], t[i + head_dim/2]),
+ * DF_ROPE_ADJACENT rotates (t[2i], t[2i+1]); pair i turns by
+ * p * theta^(-2i/head_dim) either way. */
+/* Widest matmul input: a decode matvec keeps its whole f32 input vector in
+ * LDS (128 KiB at this width, of the 160 KiB a gfx950 work-group may use). */
+#define DF_MAX_WIDTH 32768
+
+#define DF_ROPE_HALVES 0
+#define DF_ROPE_ADJACENT 1
 
 /* Weight dtypes. DF_Q8_32: blocks of 32 consecutive int8 values along a row
  * with one f16 scale each; the host layout of one block is the scale
@@ -74,16 +91,16 @@ typedef int32_t df_status;
 #define DF_Q8_32 2
 
 typedef struct df_config {
-    int32_t arch;        /* DF_ARCH_LLAMA or DF_ARCH_QWEN3 */
+    int32_t arch;        /* DF_ARCH_LLAMA, DF_ARCH_QWEN3 or DF_ARCH_QWEN2 */
     int32_t n_layers;    /* >= 0 */
-    int32_t d_model;     /* multiple of 32, <= 16384 */
+    int32_t d_model;     /* multiple of 32, <= DF_MAX_WIDTH */
     int32_t n_heads;     /* query heads */
     int32_t n_kv_heads;  /* divides n_heads; n_heads / n_kv_heads <= 8 */
-    int32_t head_dim;    /* 16, 32, 64 or 128; n_heads * head_dim <= 16384 */
-    int32_t ffn_dim;     /* multiple of 32, <= 16384 */
+    int32_t head_dim;    /* 16, 32, 64 or 128; n_heads * head_dim <= DF_MAX_WIDTH */
+    int32_t ffn_dim;     /* multiple of 32, <= DF_MAX_WIDTH */
     int32_t vocab;       /* >= 1 */
     int32_t max_ctx;     /* KV capacity in positions, 1 .. 1048576 */
-    int32_t reserved;    /* set to 0 */
+    int32_t rope_pairing; /* DF_ROPE_HALVES (0) or DF_ROPE_ADJACENT */
     double rope_theta;   /* > 0; angle p * theta^(-2i/head_dim) */
     double rms_eps;      /* >= 0; inside the square root */
 } df_config;

@@ -72,6 +72,13 @@ CONFIGS = {
                         tied=False, wdtype="q8", seed=4, max_ctx=8320,
                         prompt_len=8192, decode_steps=128,
                         contexts=(1024, 8192)),
+    # qwen2-7B shape: 28 layers, d 3584, 28/4 heads of 128 (7 query heads
+    # per KV head), ffn 18944, vocab 152064, untied, q/k/v biases, f16
+    "qwen2_7b": dict(arch="qwen2", n_layers=28, d_model=3584, n_heads=28,
+                     n_kv_heads=4, head_dim=128, ffn_dim=18944, vocab=152064,
+                     rope_theta=1000000.0, rms_eps=1e-6, tied=False,
+                     wdtype="f16", seed=6, max_ctx=4224, prompt_len=4096,
+                     decode_steps=64),
     # qwen3-8B shape: 36 layers, d 4096, 32/8 heads of 128, ffn 12288,
     # vocab 151936, untied, per-head Q/K norm, f16
     "qwen3_8b": dict(arch="qwen3", n_layers=36, d_model=4096, n_heads=32,

@@ -83,11 +83,62 @@ def test_invalid_config_is_named(dfa, field, value, needle):
     assert needle in msg
 
 
-@pytest.mark.parametrize("nh,nkv", [(16, 1), (6, 2)])
+@pytest.mark.parametrize("nh,nkv", [(16, 1), (18, 2)])
 def test_unsupported_group_size(dfa, nh, nkv):
     cfg, W = tiny_table(n_heads=nh, n_kv_heads=nkv, head_dim=16, d_model=256)
     status, msg = load_rc(dfa, cfg, synth.make_weights(cfg))
     assert status == "INVALID_CONFIG" and "query heads" in msg
+
+
+@pytest.mark.parametrize("nh,nkv", [(6, 2), (14, 2), (10, 2)])
+def test_any_group_size_up_to_8_passes_validation(dfa, nh, nkv):
+    cfg, W = tiny_table(n_heads=nh, n_kv_heads=nkv, head_dim=16, d_model=256)
+    status, msg = load_rc(dfa, cfg, synth.make_weights(cfg))
+    assert status in ("OK", "BACKEND_INIT"), msg
+
+
+def test_invalid_rope_pairing_is_named(dfa):
+    cfg, W = tiny_table()
+    c = dfa.make_config(cfg)
+    c.rope_pairing = 2
+    h = C.c_void_p()
+    arr = (dfa.df_tensor * 1)()
+    rc = dfa.lib().df_load(C.byref(c), arr, 0, None, C.byref(h))
+    assert dfa.STATUS_NAMES[rc] == "INVALID_CONFIG"
+    assert b"rope_pairing" in dfa.lib().df_last_error(None)
+
+
+def test_qwen2_missing_bias_is_named(dfa):
+    cfg, W = tiny_table(arch="qwen2")
+    del W["blk.1.attn_v.bias"]
+    status, msg = load_rc(dfa, cfg, W)
+    assert status == "MISSING_TENSOR"
+    assert "blk.1.attn_v.bias" in msg and "add_bias v" in msg
+
+
+def test_qwen2_bias_shape_and_dtype_checked(dfa):
+    cfg, W = tiny_table(arch="qwen2")
+    W["blk.0.attn_k.bias"] = W["blk.0.attn_q.bias"]
+    status, msg = load_rc(dfa, cfg, W)
+    assert status == "SHAPE_MISMATCH" and "blk.0.attn_k.bias" in msg
+    cfg, W = tiny_table(arch="qwen2")
+    W["blk.0.attn_q.bias"] = np.zeros((1, 2 * 34), np.uint8)
+    status, msg = load_rc(dfa, cfg, W)
+    assert status == "UNSUPPORTED_OP" and "blk.0.attn_q.bias" in msg
+
+
+def test_bias_on_llama_rejected(dfa):
+    cfg, W = tiny_table(arch="llama")
+    W.update({k: v for k, v in synth.make_weights(synth.config("tiny", arch="qwen2")).items()
+              if k.endswith(".bias")})
+    status, msg = load_rc(dfa, cfg, W)
+    assert status == "INVALID_ARGUMENT" and ".bias" in msg and "llama" in msg
+
+
+def test_valid_qwen2_table_passes_validation(dfa):
+    cfg, W = tiny_table(arch="qwen2", rope_pairing="adjacent")
+    status, msg = load_rc(dfa, cfg, W)
+    assert status in ("OK", "BACKEND_INIT"), msg
 
 
 def test_missing_tensor_is_named(dfa):

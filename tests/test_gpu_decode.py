@@ -42,11 +42,16 @@ def gpu_teacher_forced(dfa, cfg, W, fed, max_ctx=None):
     return m, out
 
 
-@pytest.mark.parametrize("arch,wdtype", [("qwen3", "f32"), ("llama", "f32"),
-                                         ("qwen3", "f16"), ("llama", "q8")])
-def test_tiny_token_by_token_and_decode(dfa, arch, wdtype):
-    say(f"[tiny {arch} {wdtype}] 32-token prompt + 16 greedy steps")
-    cfg = synth.config("tiny", arch=arch, wdtype=wdtype)
+@pytest.mark.parametrize("arch,wdtype,over", [
+    ("qwen3", "f32", {}), ("llama", "f32", {}), ("qwen3", "f16", {}), ("llama", "q8", {}),
+    ("qwen2", "f32", {}), ("qwen2", "f16", dict(rope_pairing="adjacent")),
+    ("qwen2", "q8", dict(n_heads=6, n_kv_heads=2)),
+    ("llama", "f32", dict(rope_pairing="adjacent", n_heads=14, n_kv_heads=2)),
+    ("qwen3", "f16", dict(rope_pairing="adjacent", n_heads=10, n_kv_heads=2))],
+    ids=lambda v: "-".join(f"{k}{x}" for k, x in v.items()) if isinstance(v, dict) else str(v))
+def test_tiny_token_by_token_and_decode(dfa, arch, wdtype, over):
+    say(f"[tiny {arch} {wdtype} {over}] 32-token prompt + 16 greedy steps")
+    cfg = synth.config("tiny", arch=arch, wdtype=wdtype, **over)
     W = synth.make_weights(cfg)
     prompt = synth.make_prompt(cfg, cfg["prompt_len"])
     fed, ref = oracle_greedy(cfg, W, prompt, cfg["decode_steps"])

@@ -5,6 +5,8 @@ outputs the oracle can compute.
   to 4096 synthetic positions, then decode steps at p = 4096.. are compared
   (logits rel-L2 <= 1e-4) -- the bench's decode launch configuration.
 * the same shape with 8-bit blocks at contexts 1024 and 8192 (<= 1e-3).
+* qwen2-7B shape, f16, all 28 layers (q/k/v biases, 7 query heads per KV
+  head), decode at p = 4096 on a restored cache (<= 1e-4).
 * qwen3-8B shape, all 36 layers, one bulk prefill of 2048 tokens: against
   GPU token-by-token (<= 5e-3, greedy token identical), and layer 0's K / V
   cache rows at sampled positions against the oracle's step functions (a
@@ -76,6 +78,12 @@ def restored_decode(dfa, cfg, ctx, n_steps, tol):
 def test_llama_8b_f16_decode_at_4096(dfa):
     say("[llama-8B shape, 32 layers, f16] decode at p = 4096, 4097 on a restored cache")
     restored_decode(dfa, synth.config("llama_8b"), 4096, 2, 1e-4)
+
+
+def test_qwen2_7b_f16_decode_at_4096(dfa):
+    say("[qwen2-7B shape, 28 layers, f16, q/k/v biases, 7 heads per KV head] "
+        "decode at p = 4096, 4097 on a restored cache")
+    restored_decode(dfa, synth.config("qwen2_7b"), 4096, 2, 1e-4)
 
 
 @pytest.mark.parametrize("ctx", [1024, 8192])

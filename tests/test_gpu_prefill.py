@@ -60,10 +60,14 @@ def check_kv(m, om, cfg, n, tol=TOL):
             assert err <= tol, (layer, which, err)
 
 
-@pytest.mark.parametrize("arch", ["qwen3", "llama"])
-def test_tiny_f16_bulk_then_bulk_then_decode(dfa, arch):
-    say(f"[tiny {arch} f16] bulk 40 + bulk 7 (on top) + 6 decode steps")
-    cfg = synth.config("tiny", arch=arch, wdtype="f16", max_ctx=64)
+@pytest.mark.parametrize("arch,over", [
+    ("qwen3", {}), ("llama", {}), ("qwen2", {}),
+    ("qwen2", dict(rope_pairing="adjacent", n_heads=6, n_kv_heads=2)),
+    ("qwen3", dict(rope_pairing="adjacent", n_heads=14, n_kv_heads=2))],
+    ids=lambda v: "-".join(f"{k}{x}" for k, x in v.items()) if isinstance(v, dict) else str(v))
+def test_tiny_f16_bulk_then_bulk_then_decode(dfa, arch, over):
+    say(f"[tiny {arch} f16 {over}] bulk 40 + bulk 7 (on top) + 6 decode steps")
+    cfg = synth.config("tiny", arch=arch, wdtype="f16", max_ctx=64, **over)
     W = synth.make_weights(cfg)
     toks = synth.make_prompt(cfg, 47)
     om, ref = oracle_run(cfg, W, [toks[:40], toks[40:]], 64)
@@ -83,7 +87,7 @@ def test_tiny_f16_bulk_then_bulk_then_decode(dfa, arch):
     m.close()
 
 
-@pytest.mark.parametrize("arch", ["qwen3", "llama"])
+@pytest.mark.parametrize("arch", ["qwen3", "llama", "qwen2"])
 def test_tiny_q8_bulk_then_decode(dfa, arch):
     """8-bit block weights: the GEMMs dequantise the weight tiles to f16."""
     say(f"[tiny {arch} q8] bulk 40 (ragged K and N tiles) + 4 decode steps vs the oracle")
@@ -105,7 +109,8 @@ def test_tiny_q8_bulk_then_decode(dfa, arch):
 
 
 @pytest.mark.parametrize("name,S,vocab", [("qwen3_8b", 300, None), ("llama_8b", 200, 4096),
-                                          ("qwen3_0p6b", 137, None), ("llama_8b_q8", 160, 4096)])
+                                          ("qwen3_0p6b", 137, None), ("llama_8b_q8", 160, 4096),
+                                          ("qwen2_7b", 150, 4096)])
 def test_one_layer_real_shape_bulk(dfa, name, S, vocab):
     over = dict(n_layers=1, max_ctx=S + 8)
     if vocab:

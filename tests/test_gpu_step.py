@@ -4,7 +4,8 @@ DF_FLAG_PERSISTENT_STEP) on the GPU.
 The step kernel runs where the weights are f16 or 8-bit blocks and
 head_dim is 64 or 128. These cases use small shapes the oracle finishes in
 seconds but that still cover every template the kernel has: head_dim 64 and
-128, query heads per KV head 1, 2, 4 and 8, both architectures, f16 and
+128, query heads per KV head 1, 2, 3, 4, 7 and 8, the three architectures
+and both rope pairings, f16 and
 8-bit weights with an f16 or an 8-bit logits matrix, a model dimension that
 is not a whole number of 512-value chunks, a ragged vocabulary, and contexts
 long enough for many attention splits. Bars as for the other decode tests:
@@ -42,14 +43,18 @@ def small(arch, wdtype, hd, n_kv, tied=True, **over):
     return synth.config("tiny", **base)
 
 
-CASES = [("qwen3", "f16", 64, 8, True), ("llama", "f16", 64, 4, True),
-         ("qwen3", "f16", 128, 2, True), ("llama", "f16", 128, 1, False),
-         ("qwen3", "q8", 128, 4, False), ("llama", "q8", 64, 2, True)]
+CASES = [("qwen3", "f16", 64, 8, True, {}), ("llama", "f16", 64, 4, True, {}),
+         ("qwen3", "f16", 128, 2, True, {}), ("llama", "f16", 128, 1, False, {}),
+         ("qwen3", "q8", 128, 4, False, {}), ("llama", "q8", 64, 2, True, {}),
+         ("qwen2", "f16", 128, 1, False, dict(n_heads=7)),
+         ("qwen2", "q8", 64, 2, True, dict(n_heads=6, rope_pairing="adjacent"))]
 
 
-@pytest.mark.parametrize("arch,wdtype,hd,n_kv,tied", CASES)
-def test_step_kernel_teacher_forced(dfa, arch, wdtype, hd, n_kv, tied):
-    cfg = small(arch, wdtype, hd, n_kv, tied)
+@pytest.mark.parametrize("arch,wdtype,hd,n_kv,tied,over", CASES,
+                         ids=lambda v: "-".join(f"{k}{x}" for k, x in v.items())
+                         if isinstance(v, dict) else str(v))
+def test_step_kernel_teacher_forced(dfa, arch, wdtype, hd, n_kv, tied, over):
+    cfg = small(arch, wdtype, hd, n_kv, tied, **over)
     G = cfg["n_heads"] // n_kv
     say(f"[{arch} {wdtype} hd {hd} G {G} tied {tied}] 24-token prompt + 12 greedy steps")
     W = synth.make_weights(cfg)
