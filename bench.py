@@ -183,6 +183,57 @@ def cpu_baseline(cfg: dict, ctx: int) -> dict:
                        f"scaled to {cfg['n_layers']} layers; cpu {cpu}")}
 
 
+def concurrent_sessions(m, cfg, ctx, max_ctx, first, args):
+    """N conversations on the model's weights (df_session), each with the
+    same restored context, decoding args.steps greedy tokens at once from N
+    host threads (one stream each). Aggregate tokens/s over the wall time
+    from the common start to the last stream's end."""
+    import threading
+    import numpy as np
+    import torch
+    import decoder_forward_amd as dfa
+    import synth
+    n = args.sessions
+    sess = [m.session(max_ctx) for _ in range(n)]
+    for layer in range(cfg["n_layers"]):
+        K, V = synth.make_kv_rows_device(cfg, layer, ctx)
+        K, V = K.cpu().numpy(), V.cpu().numpy()
+        for s in sess:
+            s.write_kv(layer, 0, 0, K, ctx)
+            s.write_kv(layer, 1, 0, V, ctx)
+    outs = [torch.empty(args.steps, dtype=torch.int32, device=m.device) for _ in sess]
+    for s, o in zip(sess, outs):  # warm each session's step graph
+        dfa.df_generate(s.h, first, 2, o, s.logits)
+    torch.cuda.synchronize()
+    for s in sess:
+        s.write_kv(0, 0, 0, np.zeros((cfg["n_kv_heads"], 0, cfg["head_dim"]), np.float32), ctx)
+    go = threading.Barrier(n + 1)
+
+    def run(k):
+        go.wait()
+        dfa.df_generate(sess[k].h, first, args.steps, outs[k], sess[k].logits)
+        torch.cuda.synchronize(m.device)
+
+    th = [threading.Thread(target=run, args=(k,)) for k in range(n)]
+    for t in th:
+        t.start()
+    go.wait()
+    t0 = time.perf_counter()
+    for t in th:
+        t.join()
+    wall = time.perf_counter() - t0
+    same = all(torch.equal(outs[0], o) for o in outs[1:])
+    for s in sess:
+        s.close()
+    agg = n * args.steps / wall
+    log(f"[bench] {n} sessions at once: {agg:.1f} tok/s aggregate, "
+        f"{wall / args.steps * 1e3:.3f} ms per step each (wall); identical tokens: {same}")
+    return {"n": n, "aggregate_tokens_per_s": round(agg, 1),
+            "ms_per_step_each": round(wall / args.steps * 1e3, 4),
+            "identical_tokens": bool(same),
+            "timing": "host wall clock from a common start to the last thread's device sync"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -197,6 +248,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--persistent-step", action="store_true",
                     help="one persistent launch per step instead of one per operation class")
+    ap.add_argument("--sessions", type=int, default=0, metavar="N",
+                    help="also time N conversations (df_session) decoding at once, "
+                         "one host thread and stream each, same context")
     ap.add_argument("--copy-probe", type=int, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("DIR", "KERNEL"),
@@ -298,6 +352,8 @@ def main():
     gu_gbps = gu_bytes / (gu["mean_us"] * 1e-6) / 1e9
     log(f"[bench] kernels: {json.dumps(kernels)}")
 
+    sessions = concurrent_sessions(m, cfg, ctx, max_ctx, first, args) if args.sessions > 0 else None
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline (bounded sample)")
@@ -349,6 +405,7 @@ def main():
                        "HIP events on the library's stream"),
         },
         "kernels": kernels,
+        "sessions": sessions,
         "cpu_baseline": cpu,
         "memory": {"weight_bytes": t["weight_bytes"], "kv_bytes": t["kv_bytes"],
                    "activation_pool_bytes": t["pool_bytes"]},

@@ -37,7 +37,7 @@ DF_F32, DF_F16, DF_Q8_32 = 0, 1, 2
 EXPORTS = ("df_load", "df_forward", "df_generate", "df_reset_kv_cache",
            "df_free", "df_last_error", "df_get_timings", "df_kv_length",
            "df_argmax", "df_read_kv", "df_write_kv", "df_stream",
-           "df_profile", "df_profile_read", "df_time_kernel")
+           "df_profile", "df_profile_read", "df_time_kernel", "df_session")
 KERNELS = {"embed": 0, "qkv": 1, "attn": 2, "o": 3, "gate_up": 4, "down": 5,
            "logits": 6, "argmax": 7, "attn_merge": 8, "step": 9}
 # df_options.flags: every decode step as one persistent launch (opt-in).
@@ -94,6 +94,7 @@ def lib() -> C.CDLL:
     L = C.CDLL(LIB_PATH)
     vp, i32, P = C.c_void_p, C.c_int32, C.POINTER
     L.df_load.argtypes = [P(df_config), P(df_tensor), C.c_size_t, P(df_options), P(vp)]
+    L.df_session.argtypes = [vp, i32, P(df_options), P(vp)]
     L.df_forward.argtypes = [vp, P(i32), i32, vp]
     L.df_generate.argtypes = [vp, i32, i32, vp, vp]
     L.df_reset_kv_cache.argtypes = [vp]
@@ -174,6 +175,16 @@ def df_load(cfg: dict, weights: dict, stream=None, device: int = 0,
     rc = lib().df_load(C.byref(c), arr, len(names), C.byref(opt), C.byref(h))
     _check(rc, None)
     return h
+
+
+def df_session(h, max_ctx: int, stream=None):
+    """Another conversation on the loaded model h: its own KV cache of
+    max_ctx positions, the model's weights. Returns a handle."""
+    opt = df_options(stream, 0, 0)
+    out = C.c_void_p()
+    rc = lib().df_session(h, max_ctx, C.byref(opt), C.byref(out))
+    _check(rc, None)
+    return out
 
 
 def df_forward(h, tokens, logits=None) -> None:
@@ -267,8 +278,8 @@ class Model:
     first and makes torch's current stream wait for it afterwards, so torch
     code before and after sees the results in order."""
 
-    def __init__(self, cfg: dict, weights: dict, max_ctx: int | None = None,
-                 device: int = 0, persistent_step: bool = False):
+    def __init__(self, cfg: dict, weights: dict | None, max_ctx: int | None = None,
+                 device: int = 0, persistent_step: bool = False, _base=None):
         import torch
         self._torch = torch
         self.cfg = dict(cfg)
@@ -277,11 +288,20 @@ class Model:
         self.device = torch.device("cuda", device)
         self.stream = torch.cuda.Stream(self.device)
         self.h = None
-        self.h = df_load(self.cfg, weights, stream=self.stream.cuda_stream,
-                         device=device,
-                         flags=DF_FLAG_PERSISTENT_STEP if persistent_step else 0)
+        if _base is not None:
+            self.h = df_session(_base.h, self.cfg["max_ctx"], stream=self.stream.cuda_stream)
+        else:
+            self.h = df_load(self.cfg, weights, stream=self.stream.cuda_stream,
+                             device=device,
+                             flags=DF_FLAG_PERSISTENT_STEP if persistent_step else 0)
         self.logits = torch.empty(self.cfg["vocab"], dtype=torch.float32,
                                   device=self.device)
+
+    def session(self, max_ctx: int | None = None) -> "Model":
+        """A new conversation on these weights with its own KV cache and
+        stream (df_session)."""
+        return Model(self.cfg, None, max_ctx=max_ctx if max_ctx is not None else self.cfg["max_ctx"],
+                     device=self.device.index, _base=self)
 
     def _enter(self):
         self.stream.wait_stream(self._torch.cuda.current_stream(self.device))

@@ -10,6 +10,7 @@
 // reads the f32 KV cache and rounds K and V to f16 in LDS.
 #include "kernels.h"
 
+#include <atomic>
 #include <type_traits>
 
 namespace dfk {
@@ -344,12 +345,12 @@ template <int BM, int BN, int MODE, bool WQ8>
 hipError_t launch_gemm_q(const GemmArgs& g, hipStream_t s)
 {
     constexpr size_t lds = gemm_lds_bytes<BM, BN>();
-    static bool attr_set = false;
-    if (!attr_set) {
+    static std::atomic<bool> attr_set{false};  // sessions may launch from several threads
+    if (!attr_set.load(std::memory_order_acquire)) {
         const hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<BM, BN, MODE, WQ8>),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
         if (r != hipSuccess) return r;
-        attr_set = true;
+        attr_set.store(true, std::memory_order_release);
     }
     constexpr int ncols = (MODE == GEMM_SWIGLU_F16) ? BN / 2 : BN;
     const int blocks = ((g.N + ncols - 1) / ncols) * ((g.M + BM - 1) / BM);

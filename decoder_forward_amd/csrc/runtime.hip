@@ -19,6 +19,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <memory>
 #include <string>
 #include <utility>
 #include <vector>
@@ -101,6 +102,20 @@ private:
     size_t total_ = 0;
 };
 
+// Device memory of the weights, the position caches and the zero block:
+// shared by a model and every session opened on it, freed when the last of
+// them is freed.
+struct WeightStore {
+    int device = 0;
+    std::vector<void*> allocs;
+    ~WeightStore()
+    {
+        if (allocs.empty()) return;
+        (void)hipSetDevice(device);
+        for (void* p : allocs) (void)hipFree(p);
+    }
+};
+
 struct Layer {
     Weight wqkv, wo, wgu, wd;  // [q;k;v], o, [gate;up], down
     float* attn_norm = nullptr;
@@ -121,8 +136,11 @@ struct df_model {
     std::atomic<int> busy{0};
     int32_t kv_len = 0;
 
-    std::vector<void*> allocs;  // every long-lived device allocation
+    std::vector<void*> allocs;  // this conversation's device allocations
+    std::shared_ptr<WeightStore> wstore;  // weights, shared with sessions
+    std::vector<void*>* alloc_to = nullptr;  // where dev_alloc records (null: allocs)
     int64_t weight_bytes = 0, kv_bytes = 0;
+    int32_t rope_rows = 0;  // positions the cos/sin table covers
 
     Weight embd, out;
     float* out_norm = nullptr;
@@ -183,7 +201,7 @@ void* dev_alloc(df_model* m, size_t bytes, const char* what, Fail* err)
                 fmt("hipMalloc of %zu bytes for %s failed", bytes, what)};
         return nullptr;
     }
-    m->allocs.push_back(p);
+    (m->alloc_to ? *m->alloc_to : m->allocs).push_back(p);
     return p;
 }
 
@@ -205,6 +223,7 @@ void release(df_model* m)
     if (m->ev1) (void)hipEventDestroy(m->ev1);
     if (m->own_stream && m->stream) (void)hipStreamDestroy(m->stream);
     m->stream = nullptr;
+    m->wstore.reset();
 }
 
 // ---------------------------------------------------------------------------
@@ -539,7 +558,7 @@ bool upload_embedding(df_model* m, const df_tensor* t, Weight* w, Fail* e)
     return upload_matrix(m, parts, w, t->name, e);
 }
 
-bool build_model(df_model* m, const std::map<std::string, const df_tensor*>& T, Fail* e)
+bool build_weights(df_model* m, const std::map<std::string, const df_tensor*>& T, Fail* e)
 {
     const df_config& c = m->cfg;
     auto get = [&](const std::string& n) { return T.at(n); };
@@ -577,18 +596,11 @@ bool build_model(df_model* m, const std::map<std::string, const df_tensor*>& T, 
         m->out = m->embd;
     }
 
-    // KV cache sized to max context (section "Memory lifecycle", "KV cache").
-    const int64_t hd = c.head_dim;
-    const size_t kv_elems = size_t(c.n_layers) * size_t(c.n_kv_heads) * size_t(c.max_ctx) * size_t(hd);
-    m->kc = static_cast<float*>(dev_alloc(m, kv_elems * 4, "K cache", e));
-    if (!m->kc) return false;
-    m->vc = static_cast<float*>(dev_alloc(m, kv_elems * 4, "V cache", e));
-    if (!m->vc) return false;
-    m->kv_bytes = int64_t(kv_elems) * 8;
-
     // cos/sin position cache, computed in f64 and rounded to f32 (section
     // "Memory lifecycle", "Position caches").
+    const int64_t hd = c.head_dim;
     const int64_t half = hd / 2;
+    m->rope_rows = c.max_ctx;
     std::vector<float> cs(size_t(c.max_ctx * half)), sn(size_t(c.max_ctx * half));
     for (int64_t p = 0; p < c.max_ctx; ++p)
         for (int64_t i = 0; i < half; ++i) {
@@ -607,7 +619,25 @@ bool build_model(df_model* m, const std::map<std::string, const df_tensor*>& T, 
                "rope sin upload", e))
         return false;
 
-    // Decode state, attention partials and counters.
+    m->zeros = static_cast<uint16_t*>(dev_alloc(m, 256, "zero block", e));
+    if (!m->zeros) return false;
+    if (!check(hipMemsetAsync(m->zeros, 0, 256, m->stream), "zero block init", e)) return false;
+    return check(hipStreamSynchronize(m->stream), "upload", e);
+}
+
+// One conversation's device state (section "Memory lifecycle": the KV cache
+// is per conversation, sized to its max context): the KV cache, the decode
+// state, attention partials, argmax result and generated-token buffer.
+bool build_conversation(df_model* m, Fail* e)
+{
+    const df_config& c = m->cfg;
+    const int64_t hd = c.head_dim;
+    const size_t kv_elems = size_t(c.n_layers) * size_t(c.n_kv_heads) * size_t(c.max_ctx) * size_t(hd);
+    m->kc = static_cast<float*>(dev_alloc(m, kv_elems * 4, "K cache", e));
+    if (!m->kc) return false;
+    m->vc = static_cast<float*>(dev_alloc(m, kv_elems * 4, "V cache", e));
+    if (!m->vc) return false;
+    m->kv_bytes = int64_t(kv_elems) * 8;
     m->state = static_cast<DevState*>(dev_alloc(m, sizeof(DevState), "decode state", e));
     if (!m->state) return false;
     const int G = c.n_heads / c.n_kv_heads;
@@ -616,9 +646,6 @@ bool build_model(df_model* m, const std::map<std::string, const df_tensor*>& T, 
     if (!m->attn_part) return false;
     m->argmax_out = static_cast<int*>(dev_alloc(m, 4, "argmax result", e));
     if (!m->argmax_out) return false;
-    m->zeros = static_cast<uint16_t*>(dev_alloc(m, 256, "zero block", e));
-    if (!m->zeros) return false;
-    if (!check(hipMemsetAsync(m->zeros, 0, 256, m->stream), "zero block init", e)) return false;
     m->gen_tokens = static_cast<int*>(dev_alloc(m, size_t(c.max_ctx) * 4, "generated tokens", e));
     if (!m->gen_tokens) return false;
     if (!check(hipMemsetAsync(m->state, 0, sizeof(DevState), m->stream), "state init", e)) return false;
@@ -1115,8 +1142,82 @@ df_status df_load(const df_config* cfg, const df_tensor* tensors, size_t n_tenso
         return DF_ERR_BACKEND_INIT;
     }
     m->flags = opt ? opt->flags : 0;
-    if (!build_model(m, found, &e) ||
+    m->wstore = std::make_shared<WeightStore>();
+    m->wstore->device = dev;
+    m->alloc_to = &m->wstore->allocs;
+    const bool weights_ok = build_weights(m, found, &e);
+    m->alloc_to = nullptr;
+    if (!weights_ok || !build_conversation(m, &e) ||
         ((m->flags & DF_FLAG_PERSISTENT_STEP) && !setup_step(m, &e))) {
+        release(m);
+        delete m;
+        g_load_error = e.msg;
+        return e.code;
+    }
+    m->load_ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t_start).count();
+    *out = m;
+    return DF_OK;
+}
+
+df_status df_session(const df_model* base, int32_t max_ctx, const df_options* opt, df_model** out)
+{
+    const auto t_start = std::chrono::steady_clock::now();
+    g_load_error.clear();
+    if (!out) {
+        g_load_error = "df_session: out is NULL";
+        return DF_ERR_INVALID_ARGUMENT;
+    }
+    *out = nullptr;
+    if (!base) {
+        g_load_error = "df_session: model is NULL";
+        return DF_ERR_INVALID_ARGUMENT;
+    }
+    if (max_ctx < 1 || max_ctx > base->rope_rows) {
+        g_load_error = fmt("df_session: max_ctx = %d: expected 1..%d (the positions the model's "
+                           "cos/sin table covers)", max_ctx, base->rope_rows);
+        return DF_ERR_INVALID_ARGUMENT;
+    }
+    if (opt && opt->flags) {
+        g_load_error = fmt("df_session: option flags 0x%x: sessions take none (the persistent "
+                           "step is per model)", unsigned(opt->flags));
+        return DF_ERR_INVALID_ARGUMENT;
+    }
+    if (hipSetDevice(base->device) != hipSuccess) {
+        (void)hipGetLastError();
+        g_load_error = fmt("df_session: hipSetDevice(%d) failed", base->device);
+        return DF_ERR_DEVICE;
+    }
+    df_model* m = new (std::nothrow) df_model();
+    if (!m) {
+        g_load_error = "host allocation of the session failed";
+        return DF_ERR_OUT_OF_MEMORY;
+    }
+    m->cfg = base->cfg;
+    m->cfg.max_ctx = max_ctx;
+    m->device = base->device;
+    m->wstore = base->wstore;
+    m->weight_bytes = base->weight_bytes;
+    m->rope_rows = base->rope_rows;
+    m->embd = base->embd;
+    m->out = base->out;
+    m->out_norm = base->out_norm;
+    m->layers = base->layers;
+    m->cos_t = base->cos_t;
+    m->sin_t = base->sin_t;
+    m->zeros = base->zeros;
+    Fail e{DF_OK, ""};
+    bool ok = true;
+    if (opt && opt->stream) {
+        m->stream = static_cast<hipStream_t>(opt->stream);
+    } else {
+        ok = check(hipStreamCreateWithFlags(&m->stream, hipStreamNonBlocking), "session stream", &e,
+                   DF_ERR_DEVICE);
+        m->own_stream = ok;
+    }
+    ok = ok && check(hipEventCreate(&m->ev0), "session events", &e, DF_ERR_DEVICE) &&
+         check(hipEventCreate(&m->ev1), "session events", &e, DF_ERR_DEVICE) &&
+         build_conversation(m, &e);
+    if (!ok) {
         release(m);
         delete m;
         g_load_error = e.msg;

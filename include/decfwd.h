@@ -161,6 +161,22 @@ typedef struct df_model df_model;
 df_status df_load(const df_config* cfg, const df_tensor* tensors,
                   size_t n_tensors, const df_options* opt, df_model** out);
 
+/* Open another conversation on a loaded model (page "Execution contract",
+ * "Concurrency": each conversation has its own KV cache, and several share
+ * one loaded model). The session shares the model's device weights and
+ * cos/sin table and gets its own KV cache of max_ctx positions (1 .. the
+ * model's max_ctx), decode state, activation pool and stream (opt->stream,
+ * or one the library makes; opt->device is ignored: the model's device is
+ * used; opt->flags must be 0). *out is a df_model handle on which every
+ * other call works as on a loaded model; it starts empty (kv_len 0). Forwards
+ * on different handles of one model may run concurrently from different
+ * threads; one handle still takes one forward at a time (DF_ERR_BUSY). The
+ * weights stay allocated until the model and all its sessions are freed,
+ * in any order, each with df_free. On error *out = NULL and
+ * df_last_error(NULL) says why. */
+df_status df_session(const df_model* model, int32_t max_ctx, const df_options* opt,
+                     df_model** out);
+
 /* Append n tokens (host array of ids in [0, vocab)) at positions kv_len ..
  * kv_len+n-1 and write the logits of the last position, vocab f32 values,
  * to logits_dev (device memory, caller-owned; NULL skips the logits).

@@ -211,3 +211,12 @@ def test_null_handles(dfa):
     n = C.c_int32()
     assert L.df_kv_length(None, C.byref(n)) == 10
     assert L.df_stream(None) is None
+
+
+def test_session_argument_checks_before_any_device_call(dfa):
+    out = C.c_void_p(1)
+    rc = dfa.lib().df_session(None, 16, None, C.byref(out))
+    assert dfa.STATUS_NAMES[rc] == "INVALID_ARGUMENT" and not out.value
+    assert "model is NULL" in dfa.df_last_error(None)
+    rc = dfa.lib().df_session(None, 16, None, None)
+    assert dfa.STATUS_NAMES[rc] == "INVALID_ARGUMENT"
