@@ -19,21 +19,23 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liboracle.so")
 
 F32, F16, Q8 = 0, 1, 2
-LLAMA, QWEN3, QWEN2 = 0, 1, 2
-ARCHS = {"llama": LLAMA, "qwen3": QWEN3, "qwen2": QWEN2}
+LLAMA, QWEN3, QWEN2, GEMMA3 = 0, 1, 2, 3
+ARCHS = {"llama": LLAMA, "qwen3": QWEN3, "qwen2": QWEN2, "gemma3": GEMMA3}
 ROPE_PAIRINGS = {"halves": 0, "adjacent": 1}
 # Per-layer tensors in the oracle's slot order (GGUF names after "blk.{i}.").
 SLOTS = ("attn_norm.weight", "attn_q.weight", "attn_k.weight",
          "attn_v.weight", "attn_q_norm.weight", "attn_k_norm.weight",
          "attn_output.weight", "ffn_norm.weight", "ffn_gate.weight",
          "ffn_up.weight", "ffn_down.weight", "attn_q.bias", "attn_k.bias",
-         "attn_v.bias")
+         "attn_v.bias", "post_attention_norm.weight", "post_ffw_norm.weight")
 
 MUTATIONS = {
     "none": 0, "norm_after_rope": 1, "rope_interleaved": 2,
     "no_attn_residual": 3, "scale_1_over_hd": 4, "gqa_modulo": 5,
     "eps_outside": 6, "exclude_self": 7, "silu_on_up": 8,
     "rope_pos_plus1": 9, "matvec_transpose": 10, "k_bias_after_rope": 11,
+    "gelu_erf": 12, "window_plus1": 13, "no_post_attn_norm": 14,
+    "global_theta": 15,
 }
 
 
@@ -43,7 +45,9 @@ class Config(C.Structure):
                 ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
                 ("ffn_dim", C.c_int32), ("vocab", C.c_int32),
                 ("max_ctx", C.c_int32), ("rope_pairing", C.c_int32),
-                ("rope_theta", C.c_double), ("rms_eps", C.c_double)]
+                ("rope_theta", C.c_double), ("rms_eps", C.c_double),
+                ("sliding_window", C.c_int32), ("window_pattern", C.c_int32),
+                ("rope_theta_local", C.c_double)]
 
 
 class Tensor(C.Structure):
@@ -74,6 +78,8 @@ def lib():
         L.orc_add_bias.argtypes = [fp, T, i64]
         L.orc_attention.argtypes = [fp, i32, i32, i32, fp, fp, i64, i32, fp]
         L.orc_silu.argtypes = [fp, i64]
+        L.orc_gelu_tanh.argtypes = [fp, i64]
+        L.orc_scale.argtypes = [fp, i64, C.c_float]
         L.orc_mul.argtypes = [fp, fp, i64]
         L.orc_create.argtypes = [C.POINTER(Config), T, T, T, T]
         L.orc_create.restype = vp
@@ -213,6 +219,18 @@ def silu(g: np.ndarray) -> np.ndarray:
     return g
 
 
+def gelu_tanh(g: np.ndarray) -> np.ndarray:
+    g = np.array(g, np.float32, copy=True, order="C")
+    lib().orc_gelu_tanh(_fp(g), g.size)
+    return g
+
+
+def scale(x: np.ndarray, s: float) -> np.ndarray:
+    x = np.array(x, np.float32, copy=True, order="C")
+    lib().orc_scale(_fp(x), x.size, C.c_float(s))
+    return x
+
+
 def mul(g: np.ndarray, u: np.ndarray) -> np.ndarray:
     g = np.array(g, np.float32, copy=True, order="C")
     u = np.ascontiguousarray(u, np.float32)
@@ -243,7 +261,9 @@ class Model:
                            c["n_kv_heads"], c["head_dim"], c["ffn_dim"],
                            c["vocab"], c["max_ctx"],
                            ROPE_PAIRINGS[c.get("rope_pairing", "halves")],
-                           float(c["rope_theta"]), float(c["rms_eps"]))
+                           float(c["rope_theta"]), float(c["rms_eps"]),
+                           int(c.get("sliding_window", 0)), int(c.get("window_pattern", 0)),
+                           float(c.get("rope_theta_local", 0.0)))
         nl = c["n_layers"]
         layers = (Tensor * max(1, nl * len(SLOTS)))()
         for i in range(nl):

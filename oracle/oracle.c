@@ -298,6 +298,27 @@ void orc_silu(float* g, int64_t n)
     }
 }
 
+/* gelu_tanh (section "The operations": the tanh approximation, not the erf
+ * form), in place: g = g/2 * (1 + tanh(sqrt(2/pi) * (g + 0.044715 g^3))). */
+void orc_gelu_tanh(float* g, int64_t n)
+{
+    const double c = sqrt(2.0 / acos(-1.0));
+    for (int64_t i = 0; i < n; ++i) {
+        double z = g[i];
+        if (g_mutation == ORC_MUT_GELU_ERF)
+            g[i] = (float)(0.5 * z * (1.0 + erf(z / sqrt(2.0))));
+        else
+            g[i] = (float)(0.5 * z * (1.0 + tanh(c * (z + 0.044715 * z * z * z))));
+    }
+}
+
+/* scale (section "The operations"), in place: x = x * s, one f32 rounding
+ * of the exact product. */
+void orc_scale(float* x, int64_t n, float s)
+{
+    for (int64_t i = 0; i < n; ++i) x[i] = (float)((double)x[i] * (double)s);
+}
+
 /* mul, in place: g = g * u (one f32 rounding). */
 void orc_mul(float* g, const float* u, int64_t n)
 {
@@ -323,6 +344,8 @@ struct orc_model {
     float* vc;
     float* cos_t; /* [max_ctx][hd/2] */
     float* sin_t;
+    float* cos_l; /* local layers' table (rope_theta_local) */
+    float* sin_l;
     int32_t n_past;
     float *x, *h, *q, *k, *v, *a, *o, *g, *u, *dn, *y;
     char trace[TRACE_CAP];
@@ -350,8 +373,11 @@ orc_model* orc_create(const orc_config* cfg, const orc_tensor* token_embd,
         cfg->n_kv_heads <= 0 || cfg->n_heads % cfg->n_kv_heads ||
         cfg->head_dim <= 0 || cfg->head_dim % 2 || cfg->ffn_dim <= 0 ||
         cfg->vocab <= 0 || cfg->max_ctx <= 0 ||
-        (cfg->arch != ORC_LLAMA && cfg->arch != ORC_QWEN3 && cfg->arch != ORC_QWEN2) ||
-        (cfg->rope_pairing != ORC_ROPE_HALVES && cfg->rope_pairing != ORC_ROPE_ADJACENT))
+        (cfg->arch != ORC_LLAMA && cfg->arch != ORC_QWEN3 && cfg->arch != ORC_QWEN2 &&
+         cfg->arch != ORC_GEMMA3) ||
+        (cfg->rope_pairing != ORC_ROPE_HALVES && cfg->rope_pairing != ORC_ROPE_ADJACENT) ||
+        cfg->sliding_window < 0 || (cfg->sliding_window > 0 && cfg->window_pattern < 1) ||
+        cfg->rope_theta_local < 0)
         return NULL;
     orc_model* m = (orc_model*)calloc(1, sizeof(orc_model));
     if (!m) return NULL;
@@ -369,6 +395,8 @@ orc_model* orc_create(const orc_config* cfg, const orc_tensor* token_embd,
     m->vc = (float*)calloc((size_t)(kv_elems ? kv_elems : 1), sizeof(float));
     m->cos_t = (float*)malloc(sizeof(float) * (size_t)cfg->max_ctx * (size_t)(hd / 2));
     m->sin_t = (float*)malloc(sizeof(float) * (size_t)cfg->max_ctx * (size_t)(hd / 2));
+    m->cos_l = (float*)malloc(sizeof(float) * (size_t)cfg->max_ctx * (size_t)(hd / 2));
+    m->sin_l = (float*)malloc(sizeof(float) * (size_t)cfg->max_ctx * (size_t)(hd / 2));
     const int64_t qd = (int64_t)cfg->n_heads * hd, kvd = (int64_t)cfg->n_kv_heads * hd;
     m->x = (float*)malloc(sizeof(float) * (size_t)d);
     m->h = (float*)malloc(sizeof(float) * (size_t)d);
@@ -381,13 +409,17 @@ orc_model* orc_create(const orc_config* cfg, const orc_tensor* token_embd,
     m->dn = (float*)malloc(sizeof(float) * (size_t)d);
     m->g = (float*)malloc(sizeof(float) * (size_t)cfg->ffn_dim);
     m->u = (float*)malloc(sizeof(float) * (size_t)cfg->ffn_dim);
-    if (!m->layers || !m->kc || !m->vc || !m->cos_t || !m->sin_t || !m->x ||
+    if (!m->layers || !m->kc || !m->vc || !m->cos_t || !m->sin_t || !m->cos_l ||
+        !m->sin_l || !m->x ||
         !m->h || !m->y || !m->q || !m->a || !m->k || !m->v || !m->o ||
         !m->dn || !m->g || !m->u) {
         orc_destroy(m);
         return NULL;
     }
     orc_rope_table(cfg->max_ctx, cfg->head_dim, cfg->rope_theta, m->cos_t, m->sin_t);
+    orc_rope_table(cfg->max_ctx, cfg->head_dim,
+                   cfg->rope_theta_local > 0 ? cfg->rope_theta_local : cfg->rope_theta,
+                   m->cos_l, m->sin_l);
     return m;
 }
 
@@ -395,6 +427,7 @@ void orc_destroy(orc_model* m)
 {
     if (!m) return;
     free(m->layers); free(m->kc); free(m->vc); free(m->cos_t); free(m->sin_t);
+    free(m->cos_l); free(m->sin_l);
     free(m->x); free(m->h); free(m->y); free(m->q); free(m->a); free(m->k);
     free(m->v); free(m->o); free(m->dn); free(m->g); free(m->u);
     free(m);
@@ -432,8 +465,7 @@ static void forward_one(orc_model* m, int32_t tok, float* logits)
     const int32_t half = hd / 2;
     int32_t rp = (g_mutation == ORC_MUT_ROPE_POS_PLUS1) ? p + 1 : p;
     if (rp >= c->max_ctx) rp = c->max_ctx - 1;
-    const float* cos_row = m->cos_t + (int64_t)rp * half;
-    const float* sin_row = m->sin_t + (int64_t)rp * half;
+    const int gemma = (c->arch == ORC_GEMMA3);
     float tmp[4096];
     float* hbuf = hd <= 4096 ? tmp : NULL;
     char sec = '|';
@@ -441,9 +473,19 @@ static void forward_one(orc_model* m, int32_t tok, float* logits)
     trace_reset(m);
     trace_op(m, "embed", sec);
     orc_embed(&m->token_embd, tok, d, m->x);
+    if (gemma) {
+        trace_op(m, "scale", ',');
+        orc_scale(m->x, d, (float)sqrt((double)d));
+    }
 
     for (int32_t l = 0; l < c->n_layers; ++l) {
         const orc_tensor* w = m->layers + (int64_t)l * ORC_NSLOT;
+        /* local layer: attends through the window, rotates with the local
+         * theta; the pattern's every P-th layer is global. */
+        const int local = c->sliding_window > 0 && (l + 1) % c->window_pattern != 0;
+        const int local_theta = local && g_mutation != ORC_MUT_GLOBAL_THETA;
+        const float* cos_row = (local_theta ? m->cos_l : m->cos_t) + (int64_t)rp * half;
+        const float* sin_row = (local_theta ? m->sin_l : m->sin_t) + (int64_t)rp * half;
         sec = '|';
         trace_op(m, "rms_norm", sec); sec = ',';
         orc_rmsnorm(m->x, &w[ORC_ATTN_NORM], d, eps, m->h);
@@ -458,7 +500,7 @@ static void forward_one(orc_model* m, int32_t tok, float* logits)
         trace_op(m, "matmul", sec);
         orc_matvec(&w[ORC_ATTN_V], kvd, d, m->h, m->v);
         if (bias) { trace_op(m, "add_bias", sec); orc_add_bias(m->v, &w[ORC_ATTN_V_BIAS], kvd); }
-        const int qk_norm = (c->arch == ORC_QWEN3);
+        const int qk_norm = (c->arch == ORC_QWEN3 || gemma);
         const int norm_first = (g_mutation != ORC_MUT_NORM_AFTER_ROPE);
         if (qk_norm && norm_first) {
             trace_op(m, "norm_heads", sec);
@@ -485,11 +527,23 @@ static void forward_one(orc_model* m, int32_t tok, float* logits)
         }
         trace_op(m, "attention", sec);
         int32_t n_pos = (g_mutation == ORC_MUT_EXCLUDE_SELF) ? p : p + 1;
-        orc_attention(m->q, nh, nkv, hd, kv_row(m, m->kc, l, 0, 0),
-                      kv_row(m, m->vc, l, 0, 0), (int64_t)c->max_ctx * hd,
-                      n_pos, m->a);
+        int32_t lo = 0;  /* first position inside the window */
+        if (local) {
+            const int32_t W = c->sliding_window + (g_mutation == ORC_MUT_WINDOW_PLUS1 ? 1 : 0);
+            lo = p - W + 1 > 0 ? p - W + 1 : 0;
+        }
+        orc_attention(m->q, nh, nkv, hd, kv_row(m, m->kc, l, 0, lo),
+                      kv_row(m, m->vc, l, 0, lo), (int64_t)c->max_ctx * hd,
+                      n_pos - lo, m->a);
         trace_op(m, "matmul", sec);
         orc_matvec(&w[ORC_ATTN_OUTPUT], d, qd, m->a, m->o);
+        if (gemma) {
+            trace_op(m, "rms_norm", sec);
+            if (g_mutation != ORC_MUT_NO_POST_ATTN_NORM) {
+                orc_rmsnorm(m->o, &w[ORC_POST_ATTN_NORM], d, eps, m->y);
+                memcpy(m->o, m->y, sizeof(float) * (size_t)d);
+            }
+        }
         trace_op(m, "add", sec);
         if (g_mutation == ORC_MUT_NO_ATTN_RESIDUAL)
             memcpy(m->x, m->o, sizeof(float) * (size_t)d);
@@ -500,13 +554,16 @@ static void forward_one(orc_model* m, int32_t tok, float* logits)
         orc_rmsnorm(m->x, &w[ORC_FFN_NORM], d, eps, m->h);
         trace_op(m, "matmul", sec);
         orc_matvec(&w[ORC_FFN_GATE], F, d, m->h, m->g);
-        if (g_mutation != ORC_MUT_SILU_ON_UP) {
+        if (gemma) {
+            trace_op(m, "gelu_tanh", sec);
+            orc_gelu_tanh(m->g, F);
+        } else if (g_mutation != ORC_MUT_SILU_ON_UP) {
             trace_op(m, "silu", sec);
             orc_silu(m->g, F);
         }
         trace_op(m, "matmul", sec);
         orc_matvec(&w[ORC_FFN_UP], F, d, m->h, m->u);
-        if (g_mutation == ORC_MUT_SILU_ON_UP) {
+        if (!gemma && g_mutation == ORC_MUT_SILU_ON_UP) {
             trace_op(m, "silu", sec);
             orc_silu(m->u, F);
         }
@@ -514,6 +571,11 @@ static void forward_one(orc_model* m, int32_t tok, float* logits)
         orc_mul(m->g, m->u, F);
         trace_op(m, "matmul", sec);
         orc_matvec(&w[ORC_FFN_DOWN], d, F, m->g, m->dn);
+        if (gemma) {
+            trace_op(m, "rms_norm", sec);
+            orc_rmsnorm(m->dn, &w[ORC_POST_FFN_NORM], d, eps, m->y);
+            memcpy(m->dn, m->y, sizeof(float) * (size_t)d);
+        }
         trace_op(m, "add", sec);
         add_inplace(m->x, m->dn, d);
     }

@@ -5,15 +5,22 @@
  * calls this code; only the tests, the package's smoke check and the
  * benchmark's CPU-baseline leg load it. It shares no code with the GPU path.
  *
- * What it computes: the per-layer step list of a llama / qwen3 / qwen2
- * decoder as the architecture-definition file lays it out (page "Local
- * inference and architectures", section "The format": prologue embed; block
+ * What it computes: the per-layer step list of a llama / qwen3 / qwen2 /
+ * gemma3-style decoder as the architecture-definition file lays it out
+ * (page "Local inference and architectures", section "The format": prologue
+ * embed; block
  * rms_norm, q/k/v matmul (each followed by add_bias in qwen2, whose
  * definition differs from llama's by those three lines, section "Adding an
  * architecture"), norm_heads q/k (qwen3 only), rope q/k, attention, o matmul,
  * add, rms_norm, gate matmul, silu, up matmul, mul, down matmul, add;
  * epilogue rms_norm, last, logits matmul with the output weight or, if that
- * is absent, the token embedding). Multiplication is in f32 on f32 values
+ * is absent, the token embedding). gemma3 (20 steps per layer, section
+ * "What is in effect right now"; gelu_tanh, section "The operations"; a
+ * window pattern, section "Rules") is read as: prologue embed, scale by
+ * sqrt(d_model); block rms_norm, q/k/v matmul, norm_heads q/k, rope q/k,
+ * attention (through a sliding window on the pattern's local layers), o
+ * matmul, rms_norm of o, add, rms_norm, gate matmul, gelu_tanh, up matmul,
+ * mul, down matmul, rms_norm of down, add. Multiplication is in f32 on f32 values
  * (same page, section "Choosing the engine": the engine multiplies in f32
  * rather than quantising activations). Every dot product is formed from
  * exact f32×f32 products accumulated in f64 and rounded once to f32, so the
@@ -36,6 +43,12 @@
  *  - attention: causal over positions 0..p including p, scale 1/sqrt(hd),
  *    grouped-query head j reads KV head j / (n_heads / n_kv_heads).
  *  - K is cached after RoPE, V as computed.
+ *  - sliding window W (gemma3's local layers): position p attends to the
+ *    positions t with p - W < t <= p; with window_pattern P, layer l is
+ *    global when (l + 1) % P == 0 and local otherwise; local layers rotate
+ *    with rope_theta_local, global ones with rope_theta.
+ *  - gelu_tanh(x) = x/2 * (1 + tanh(sqrt(2/pi) * (x + 0.044715 x^3))).
+ *  - scale: x_i = x_i * s with s = f32(sqrt(d_model)), one rounding.
  *  - 8-bit blocks: 32 int8 along K with one f16 scale, w = scale * q.
  */
 #ifndef DECFWD_ORACLE_H
@@ -48,7 +61,7 @@ extern "C" {
 #endif
 
 enum { ORC_F32 = 0, ORC_F16 = 1, ORC_Q8 = 2 };
-enum { ORC_LLAMA = 0, ORC_QWEN3 = 1, ORC_QWEN2 = 2 };
+enum { ORC_LLAMA = 0, ORC_QWEN3 = 1, ORC_QWEN2 = 2, ORC_GEMMA3 = 3 };
 enum { ORC_ROPE_HALVES = 0, ORC_ROPE_ADJACENT = 1 };
 
 enum {
@@ -64,7 +77,7 @@ enum {
     ORC_ATTN_NORM = 0, ORC_ATTN_Q, ORC_ATTN_K, ORC_ATTN_V, ORC_ATTN_Q_NORM,
     ORC_ATTN_K_NORM, ORC_ATTN_OUTPUT, ORC_FFN_NORM, ORC_FFN_GATE,
     ORC_FFN_UP, ORC_FFN_DOWN, ORC_ATTN_Q_BIAS, ORC_ATTN_K_BIAS,
-    ORC_ATTN_V_BIAS, ORC_NSLOT
+    ORC_ATTN_V_BIAS, ORC_POST_ATTN_NORM, ORC_POST_FFN_NORM, ORC_NSLOT
 };
 
 /* Planted mistakes, used only by tests that prove the pins catch them. */
@@ -80,7 +93,11 @@ enum {
     ORC_MUT_SILU_ON_UP = 8,       /* silu(up) * gate */
     ORC_MUT_ROPE_POS_PLUS1 = 9,   /* rotate by p+1 */
     ORC_MUT_MATVEC_TRANSPOSE = 10, /* y = W^T h on square weights */
-    ORC_MUT_K_BIAS_AFTER_ROPE = 11 /* qwen2's k bias added after rope */
+    ORC_MUT_K_BIAS_AFTER_ROPE = 11, /* qwen2's k bias added after rope */
+    ORC_MUT_GELU_ERF = 12,         /* erf gelu where gelu_tanh is asked for */
+    ORC_MUT_WINDOW_PLUS1 = 13,     /* the window one position wider */
+    ORC_MUT_NO_POST_ATTN_NORM = 14, /* o added without its rms_norm */
+    ORC_MUT_GLOBAL_THETA = 15      /* local layers rotate with rope_theta */
 };
 
 typedef struct {
@@ -89,6 +106,9 @@ typedef struct {
     int32_t max_ctx;
     int32_t rope_pairing;  /* ORC_ROPE_HALVES or ORC_ROPE_ADJACENT */
     double rope_theta, rms_eps;
+    int32_t sliding_window; /* 0: every layer attends to all positions */
+    int32_t window_pattern; /* >= 1 when sliding_window > 0 */
+    double rope_theta_local; /* theta of the local layers; 0: rope_theta */
 } orc_config;
 
 /* A weight as the caller holds it. f32 / f16: [rows][cols] row-major.
@@ -124,11 +144,15 @@ void orc_attention(const float* q, int32_t n_heads, int32_t n_kv, int32_t hd,
                    const float* K, const float* V, int64_t head_stride,
                    int32_t n_pos, float* out);
 void orc_silu(float* g, int64_t n);
+/* gelu_tanh in place (f64 inside, one rounding). */
+void orc_gelu_tanh(float* g, int64_t n);
+/* x_i = f32(x_i * s) for i < n. */
+void orc_scale(float* x, int64_t n, float s);
 void orc_mul(float* g, const float* u, int64_t n);
 
 /* The model. `layers` holds n_layers * ORC_NSLOT tensors; slots an
- * architecture does not use (q/k norm outside qwen3, biases outside qwen2)
- * are ignored. `output` with data == NULL means tied weights. */
+ * architecture does not use (q/k norm outside qwen3 and gemma3, biases
+ * outside qwen2, post norms outside gemma3) are ignored. `output` with data == NULL means tied weights. */
 orc_model* orc_create(const orc_config* cfg, const orc_tensor* token_embd,
                       const orc_tensor* output_norm, const orc_tensor* output,
                       const orc_tensor* layers);

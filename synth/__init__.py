@@ -79,6 +79,22 @@ CONFIGS = {
                      rope_theta=1000000.0, rms_eps=1e-6, tied=False,
                      wdtype="f16", seed=6, max_ctx=4224, prompt_len=4096,
                      decode_steps=64),
+    # gemma3-style tiny model: 2 layers (a local layer with a window of 8
+    # positions, then a global one), d 64, 4/2 heads of 16, ffn 128, vocab
+    # 256, tied, f32
+    "tiny_gemma3": dict(arch="gemma3", n_layers=2, d_model=64, n_heads=4, n_kv_heads=2,
+                        head_dim=16, ffn_dim=128, vocab=256, rope_theta=1000000.0,
+                        rope_theta_local=10000.0, sliding_window=8, window_pattern=2,
+                        rms_eps=1e-6, tied=True, wdtype="f32", seed=7, max_ctx=48,
+                        prompt_len=32, decode_steps=16),
+    # gemma3-4B shape: 34 layers, d 2560, 8/4 heads of 256, ffn 10240, vocab
+    # 262208, tied; five local layers (window 1024, theta 1e4) per global
+    # one (theta 1e6); post-attention and post-FFN norms, gelu_tanh; f16
+    "gemma3_4b": dict(arch="gemma3", n_layers=34, d_model=2560, n_heads=8, n_kv_heads=4,
+                      head_dim=256, ffn_dim=10240, vocab=262208, rope_theta=1000000.0,
+                      rope_theta_local=10000.0, sliding_window=1024, window_pattern=6,
+                      rms_eps=1e-6, tied=True, wdtype="f16", seed=8, max_ctx=4224,
+                      prompt_len=4096, decode_steps=64),
     # qwen3-8B shape: 36 layers, d 4096, 32/8 heads of 128, ffn 12288,
     # vocab 151936, untied, per-head Q/K norm, f16
     "qwen3_8b": dict(arch="qwen3", n_layers=36, d_model=4096, n_heads=32,
@@ -91,7 +107,7 @@ CONFIGS = {
 LAYER_SLOTS = ("attn_norm", "attn_q", "attn_k", "attn_v", "attn_q_norm",
                "attn_k_norm", "attn_output", "ffn_norm", "ffn_gate",
                "ffn_up", "ffn_down", "attn_q.bias", "attn_k.bias",
-               "attn_v.bias")
+               "attn_v.bias", "post_attention_norm", "post_ffw_norm")
 
 
 def config(name: str, **overrides) -> dict:
@@ -134,7 +150,7 @@ def tensor_specs(cfg: dict) -> list[tuple[str, str, int, int]]:
             specs += [(b + "attn_q.bias", "bias", 1, qd),
                       (b + "attn_k.bias", "bias", 1, kvd),
                       (b + "attn_v.bias", "bias", 1, kvd)]
-        if cfg["arch"] == "qwen3":
+        if cfg["arch"] in ("qwen3", "gemma3"):
             specs += [(b + "attn_q_norm.weight", "norm", 1, hd),
                       (b + "attn_k_norm.weight", "norm", 1, hd)]
         specs += [(b + "attn_output.weight", "matmul", d, qd),
@@ -142,6 +158,9 @@ def tensor_specs(cfg: dict) -> list[tuple[str, str, int, int]]:
                   (b + "ffn_gate.weight", "matmul", F, d),
                   (b + "ffn_up.weight", "matmul", F, d),
                   (b + "ffn_down.weight", "matmul", d, F)]
+        if cfg["arch"] == "gemma3":
+            specs += [(b + "post_attention_norm.weight", "norm", 1, d),
+                      (b + "post_ffw_norm.weight", "norm", 1, d)]
     specs.append(("output_norm.weight", "norm", 1, d))
     if not cfg["tied"]:
         specs.append(("output.weight", "matmul", V, d))

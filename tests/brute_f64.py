@@ -9,7 +9,10 @@ Follows the step list of page "Local inference and architectures", section
 "The format"; readings of the open points are the same as the oracle's
 (rotate-half RoPE pairs unless the config asks for adjacent ones, eps inside
 the root, scale 1/sqrt(hd), GQA head j on KV head j // group, qwen2's biases
-added right after their matmuls).
+added right after their matmuls; gemma3: embedding times f32(sqrt(d)),
+q/k head norms, an rms_norm on the o and down outputs before each residual
+add, gelu_tanh, and on the pattern's local layers a window of W positions
+with the local RoPE theta).
 """
 from __future__ import annotations
 
@@ -64,9 +67,17 @@ def forward_all(cfg: dict, W: dict, tokens) -> np.ndarray:
     pos = np.arange(S)
     E = W["token_embd.weight"].astype(np.float64)
     X = E[tokens]
+    gemma = cfg["arch"] == "gemma3"
+    if gemma:
+        X = X * float(np.float32(np.sqrt(d)))
     mask = np.triu(np.ones((S, S), bool), k=1)  # True where t > s
+    Wn = cfg.get("sliding_window", 0)
+    far = (pos[:, None] - pos[None, :]) >= Wn if Wn else np.zeros((S, S), bool)
     for i in range(cfg["n_layers"]):
         b = f"blk.{i}."
+        local = Wn > 0 and (i + 1) % cfg["window_pattern"] != 0
+        th = cfg.get("rope_theta_local") or theta if local else theta
+        lmask = mask | far if local else mask
         H = rms(X, W[b + "attn_norm.weight"], eps)
         Q = H @ dequant(W[b + "attn_q.weight"], d).T
         Kx = H @ dequant(W[b + "attn_k.weight"], d).T
@@ -78,27 +89,37 @@ def forward_all(cfg: dict, W: dict, tokens) -> np.ndarray:
         Q = Q.reshape(S, nh, hd)
         Kx = Kx.reshape(S, nkv, hd)
         Vx = Vx.reshape(S, nkv, hd)
-        if cfg["arch"] == "qwen3":
+        if cfg["arch"] in ("qwen3", "gemma3"):
             Q = rms(Q, W[b + "attn_q_norm.weight"], eps)
             Kx = rms(Kx, W[b + "attn_k_norm.weight"], eps)
         pairing = cfg.get("rope_pairing", "halves")
-        Q = rope_complex(Q, pos, theta, pairing)
-        Kx = rope_complex(Kx, pos, theta, pairing)
+        Q = rope_complex(Q, pos, th, pairing)
+        Kx = rope_complex(Kx, pos, th, pairing)
         A = np.empty((S, nh, hd))
         for j in range(nh):
             g = j // group
             sc = Q[:, j, :] @ Kx[:, g, :].T / np.sqrt(hd)
-            sc[mask] = -np.inf
+            sc[lmask] = -np.inf
             sc = sc - sc.max(axis=1, keepdims=True)
             P = np.exp(sc)
             P /= P.sum(axis=1, keepdims=True)
             A[:, j, :] = P @ Vx[:, g, :]
-        X = X + A.reshape(S, nh * hd) @ dequant(W[b + "attn_output.weight"], nh * hd).T
+        O = A.reshape(S, nh * hd) @ dequant(W[b + "attn_output.weight"], nh * hd).T
+        if gemma:
+            O = rms(O, W[b + "post_attention_norm.weight"], eps)
+        X = X + O
         H = rms(X, W[b + "ffn_norm.weight"], eps)
         G = H @ dequant(W[b + "ffn_gate.weight"], d).T
         U = H @ dequant(W[b + "ffn_up.weight"], d).T
-        M = G / (1.0 + np.exp(-G)) * U
-        X = X + M @ dequant(W[b + "ffn_down.weight"], F).T
+        if gemma:
+            c = np.sqrt(2.0 / np.pi)
+            M = 0.5 * G * (1.0 + np.tanh(c * (G + 0.044715 * G ** 3))) * U
+        else:
+            M = G / (1.0 + np.exp(-G)) * U
+        Dn = M @ dequant(W[b + "ffn_down.weight"], F).T
+        if gemma:
+            Dn = rms(Dn, W[b + "post_ffw_norm.weight"], eps)
+        X = X + Dn
     Y = rms(X, W["output_norm.weight"], eps)
     Wout = W["output.weight"] if "output.weight" in W else W["token_embd.weight"]
     return Y @ dequant(Wout, d).T

@@ -30,7 +30,8 @@ def run_token_by_token(cfg, W, toks):
 
 
 def tiny(**kw):
-    cfg = synth.config("tiny", **kw)
+    base = "tiny_gemma3" if kw.get("arch") == "gemma3" else "tiny"
+    cfg = synth.config(base, **kw)
     return cfg, synth.make_weights(cfg)
 
 
@@ -39,7 +40,8 @@ def tiny(**kw):
     ("qwen3", "f16", "halves"), ("llama", "q8", "halves"),
     ("qwen2", "f32", "halves"), ("qwen2", "f16", "adjacent"),
     ("qwen2", "q8", "halves"), ("llama", "f32", "adjacent"),
-    ("qwen3", "f32", "adjacent")])
+    ("qwen3", "f32", "adjacent"), ("gemma3", "f32", "halves"),
+    ("gemma3", "f16", "halves"), ("gemma3", "q8", "adjacent")])
 def test_tiny_matches_f64_brute_force_every_step(arch, wdtype, pairing):
     cfg, W = tiny(arch=arch, wdtype=wdtype, rope_pairing=pairing)
     toks = synth.make_prompt(cfg, 40)
@@ -115,7 +117,7 @@ def golden_lists():
     return ops, steps
 
 
-@pytest.mark.parametrize("arch", ["qwen3", "llama", "qwen2"])
+@pytest.mark.parametrize("arch", ["qwen3", "llama", "qwen2", "gemma3"])
 def test_step_list_matches_the_printed_definition(arch):
     gold, steps = golden_lists()
     cfg, W = tiny(arch=arch)
@@ -182,6 +184,58 @@ def test_rope_adjacent_is_halves_on_permuted_lanes():
         if p:
             assert not np.array_equal(
                 adj, oracle.rope(t.copy(), hd, cos[p], sin[p]))
+
+
+def test_window_wider_than_the_context_is_no_window_bitwise():
+    # A window that covers every position leaves the causal mask as it is;
+    # with one theta for all layers the two models are the same bits.
+    cfg, W = tiny(arch="gemma3")
+    cfg["rope_theta_local"] = cfg["rope_theta"]
+    toks = synth.make_prompt(cfg, 20)
+    a = run_token_by_token(dict(cfg, sliding_window=1000), W, toks)
+    b = run_token_by_token(dict(cfg, sliding_window=0), W, toks)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    c = run_token_by_token(cfg, W, toks)  # window 8 over 20 tokens: differs
+    assert rel_l2(c[-1], b[-1]) > 1e-3
+
+
+def test_window_of_one_sees_only_itself():
+    # Window 1 on every layer: each attention weight is exactly 1 on the
+    # position's own V, so the last logits depend on the last token only.
+    cfg, W = tiny(arch="gemma3")
+    cfg.update(sliding_window=1, window_pattern=cfg["n_layers"] + 1)
+    toks = synth.make_prompt(cfg, 9)
+    a = run_token_by_token(cfg, W, toks)[-1]
+    b = run_token_by_token(cfg, W, toks[-1:])[-1]
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_gelu_tanh_pins():
+    x = np.linspace(-6, 6, 2001).astype(np.float32)
+    g = oracle.gelu_tanh(x).astype(np.float64)
+    gm = oracle.gelu_tanh(-x).astype(np.float64)
+    assert oracle.gelu_tanh(np.zeros(1, np.float32))[0] == 0.0
+    # tanh is odd, so gelu_tanh(x) - gelu_tanh(-x) = x
+    assert np.max(np.abs(g - gm - x) / np.maximum(1, np.abs(x))) < 4e-7
+    big = oracle.gelu_tanh(np.array([12.0, -12.0], np.float32))
+    assert big[0] == np.float32(12.0) and abs(big[1]) < 1e-30
+    # the tanh form is within about 1e-3 of the erf form and is not it
+    from math import erf
+    ge = np.array([0.5 * v * (1 + erf(v / np.sqrt(2.0))) for v in x.astype(np.float64)])
+    dev = np.max(np.abs(g - ge))
+    assert 1e-4 < dev < 1e-3, dev
+    # one value against the formula evaluated by hand: x = 1
+    # 0.5 * (1 + tanh(0.7978845608 * 1.044715)) = 0.8411919906
+    assert abs(oracle.gelu_tanh(np.ones(1, np.float32))[0] - 0.8411919906) < 1e-7
+
+
+def test_scale_is_one_rounding():
+    x = np.array([1.0, -3.0, 1e-3, 3.0e37], np.float32)
+    assert np.array_equal(oracle.scale(x, 4.0), x * np.float32(4.0))
+    s = np.float32(np.sqrt(2560.0))
+    y = np.array([0.3, -1.7, 2.2e-5], np.float32)
+    want = (y.astype(np.float64) * np.float64(s)).astype(np.float32)
+    assert np.array_equal(oracle.scale(y, float(s)), want)
 
 
 def test_norm_heads_before_rope_matters():
@@ -290,6 +344,15 @@ def _one_hot_fails():
     return not np.array_equal(oracle.matvec(W, h), W[:, 3])
 
 
+def _gelu_fails():
+    # the tanh form sits 1e-4..1e-3 away from the erf form near |x| = 2
+    x = np.linspace(-4, 4, 801).astype(np.float32)
+    from math import erf
+    ge = np.array([0.5 * v * (1 + erf(v / np.sqrt(2.0))) for v in x.astype(np.float64)])
+    dev = np.max(np.abs(oracle.gelu_tanh(x).astype(np.float64) - ge))
+    return not (1e-4 < dev < 1e-3)
+
+
 def _kv_row_fails():
     # K cached at position 0 of layer 0 is the unrotated k of token 0 (RoPE
     # at position 0 is the identity). A constant position offset leaves the
@@ -309,9 +372,9 @@ def test_each_planted_mistake_is_caught(mutation):
     oracle.set_mutation(mutation)
     try:
         caught = (_rmsnorm_closed_form_fails() or _one_hot_fails()
-                  or _kv_row_fails()
+                  or _kv_row_fails() or _gelu_fails()
                   or _brute_tiny_fails("qwen3") or _brute_tiny_fails("llama")
-                  or _brute_tiny_fails("qwen2"))
+                  or _brute_tiny_fails("qwen2") or _brute_tiny_fails("gemma3"))
     finally:
         oracle.set_mutation("none")
     assert caught, mutation
@@ -321,6 +384,8 @@ def test_pins_pass_without_mistakes():
     assert not _rmsnorm_closed_form_fails()
     assert not _one_hot_fails()
     assert not _kv_row_fails()
+    assert not _gelu_fails()
     assert not _brute_tiny_fails("qwen3")
     assert not _brute_tiny_fails("llama")
     assert not _brute_tiny_fails("qwen2")
+    assert not _brute_tiny_fails("gemma3")
