@@ -41,8 +41,9 @@ def log(*a):
 def step_bytes(cfg: dict, p: int) -> int:
     """Algorithmic HBM bytes of one decode step at position p: every matmul
     weight once (f16, or 8-bit values + f16 scales), the norm weights and
-    biases as held on the device (f32), one embedding row, the KV rows 0..p-1 read and row p
-    written (f32), and the logits written."""
+    biases as held on the device (f32), one embedding row, the KV rows 0..p-1
+    (within the window on a sliding-window layer) read and row p written
+    (f32), and the logits written."""
     d, F, V, L = cfg["d_model"], cfg["ffn_dim"], cfg["vocab"], cfg["n_layers"]
     hd = cfg["head_dim"]
     qd, kvd = cfg["n_heads"] * hd, cfg["n_kv_heads"] * hd
@@ -50,12 +51,17 @@ def step_bytes(cfg: dict, p: int) -> int:
     mat = L * per_layer + V * d  # lm head (untied)
     wbytes = mat * 2 if cfg["wdtype"] == "f16" else mat + mat // 32 * 2
     norms = (L * 2 * d + d) * 4
-    if cfg["arch"] == "qwen3":
+    if cfg["arch"] in ("qwen3", "gemma3"):
         norms += L * 2 * hd * 4
+    if cfg["arch"] == "gemma3":  # rms_norm weights of the o and down outputs
+        norms += L * 2 * d * 4
     if cfg["arch"] == "qwen2":  # q/k/v biases, f32 on the device
         norms += L * (qd + 2 * kvd) * 4
-    kv_tok = L * 2 * kvd * 4
-    return wbytes + norms + d * 2 + (p + 1) * kv_tok + V * 4
+    # KV rows read: positions 0..p, or the last `sliding_window` of them on a
+    # local layer
+    W, P = cfg.get("sliding_window", 0), cfg.get("window_pattern", 1)
+    rows = sum(min(p + 1, W) if W and (i + 1) % P else p + 1 for i in range(L))
+    return wbytes + norms + d * 2 + rows * 2 * kvd * 4 + V * 4
 
 
 def gate_up_launch_bytes(cfg: dict) -> int:
@@ -241,7 +247,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--context", type=int, default=4096)
     ap.add_argument("--workload", default="llama_8b",
-                    choices=["llama_8b", "llama_8b_q8", "qwen3_8b", "qwen3_0p6b", "qwen2_7b"])
+                    choices=["llama_8b", "llama_8b_q8", "qwen3_8b", "qwen3_0p6b", "qwen2_7b",
+                             "gemma3_4b"])
     ap.add_argument("--context-from", default="restore", choices=["prefill", "restore"],
                     help="build the context by bulk prefill (default) or by writing "
                          "synthetic KV rows")

@@ -27,8 +27,9 @@ STATUS_NAMES = {
     7: "INVALID_CONFIG", 8: "CONTEXT_FULL", 9: "BUSY", 10: "INVALID_ARGUMENT",
     11: "DEVICE",
 }
-DF_ARCH_LLAMA, DF_ARCH_QWEN3, DF_ARCH_QWEN2 = 0, 1, 2
-ARCHS = {"llama": DF_ARCH_LLAMA, "qwen3": DF_ARCH_QWEN3, "qwen2": DF_ARCH_QWEN2}
+DF_ARCH_LLAMA, DF_ARCH_QWEN3, DF_ARCH_QWEN2, DF_ARCH_GEMMA3 = 0, 1, 2, 3
+ARCHS = {"llama": DF_ARCH_LLAMA, "qwen3": DF_ARCH_QWEN3, "qwen2": DF_ARCH_QWEN2,
+         "gemma3": DF_ARCH_GEMMA3}
 DF_ROPE_HALVES, DF_ROPE_ADJACENT = 0, 1
 ROPE_PAIRINGS = {"halves": DF_ROPE_HALVES, "adjacent": DF_ROPE_ADJACENT}
 DF_F32, DF_F16, DF_Q8_32 = 0, 1, 2
@@ -57,7 +58,9 @@ class df_config(C.Structure):
                 ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
                 ("ffn_dim", C.c_int32), ("vocab", C.c_int32),
                 ("max_ctx", C.c_int32), ("rope_pairing", C.c_int32),
-                ("rope_theta", C.c_double), ("rms_eps", C.c_double)]
+                ("rope_theta", C.c_double), ("rms_eps", C.c_double),
+                ("sliding_window", C.c_int32), ("window_pattern", C.c_int32),
+                ("rope_theta_local", C.c_double)]
 
 
 class df_tensor(C.Structure):
@@ -131,7 +134,9 @@ def make_config(cfg: dict, max_ctx: int | None = None) -> df_config:
                      cfg["n_kv_heads"], cfg["head_dim"], cfg["ffn_dim"],
                      cfg["vocab"], max_ctx if max_ctx is not None else cfg["max_ctx"],
                      ROPE_PAIRINGS[cfg.get("rope_pairing", "halves")],
-                     float(cfg["rope_theta"]), float(cfg["rms_eps"]))
+                     float(cfg["rope_theta"]), float(cfg["rms_eps"]),
+                     int(cfg.get("sliding_window", 0)), int(cfg.get("window_pattern", 0)),
+                     float(cfg.get("rope_theta_local", 0.0)))
 
 
 def _tensor_entry(name: str, a, keep: list) -> df_tensor:

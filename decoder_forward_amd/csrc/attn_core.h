@@ -110,42 +110,61 @@ __device__ void attn_core(const AttnItem& a, float* lds, int tid)
     load(0, ka, va);
 
     // q of the group's heads (and, for the owner, this step's k): one wave
-    // per vector, lane i < hd/2 holding rope pair i, elements (i0, i1);
-    // bias (qwen2), norm_heads (qwen3), then rope, then into LDS.
+    // per vector, lane l holding rope pairs l, l + 64, ... (< hd/2), pair i
+    // being elements (i0, i1); bias (qwen2), norm_heads, then rope, then
+    // into LDS.
+    constexpr int PPL = (HALF + WAVE - 1) / WAVE;  // rope pairs per lane
     const int nv = G + (owner ? 1 : 0);
-    const int i0 = a.adjacent ? 2 * lane : lane;
-    const int i1 = a.adjacent ? 2 * lane + 1 : lane + HALF;
     for (int j = w; j < nv; j += NW) {
         const int off = j < G ? (a.g * G + j) * HD : a.qd + a.g * HD;
         const float* src = a.qkv + off;
-        float x0 = 0.f, x1 = 0.f;
-        if (lane < HALF) {
-            x0 = act_ld<COH>(src + i0);
-            x1 = act_ld<COH>(src + i1);
-            if (a.bias) {
-                x0 += *gmem(a.bias + off + i0);
-                x1 += *gmem(a.bias + off + i1);
+        float x0[PPL], x1[PPL];
+        int i0[PPL], i1[PPL];
+#pragma unroll
+        for (int r = 0; r < PPL; ++r) {
+            const int i = lane + r * WAVE;
+            i0[r] = a.adjacent ? 2 * i : i;
+            i1[r] = a.adjacent ? 2 * i + 1 : i + HALF;
+            x0[r] = 0.f;
+            x1[r] = 0.f;
+            if (i < HALF) {
+                x0[r] = act_ld<COH>(src + i0[r]);
+                x1[r] = act_ld<COH>(src + i1[r]);
+                if (a.bias) {
+                    x0[r] += *gmem(a.bias + off + i0[r]);
+                    x1[r] += *gmem(a.bias + off + i1[r]);
+                }
             }
         }
         if (a.q_norm) {
-            const float ss = wave_sum(fmaf(x0, x0, x1 * x1));
-            const float r = 1.0f / sqrtf(ss / static_cast<float>(HD) + a.eps);
-            if (lane < HALF) {
-                const float* nw = j < G ? a.q_norm : a.k_norm;
-                x0 = *gmem(nw + i0) * (x0 * r);
-                x1 = *gmem(nw + i1) * (x1 * r);
+            float ss = 0.f;
+#pragma unroll
+            for (int r = 0; r < PPL; ++r) ss += fmaf(x0[r], x0[r], x1[r] * x1[r]);
+            ss = wave_sum(ss);
+            const float rs = 1.0f / sqrtf(ss / static_cast<float>(HD) + a.eps);
+            const float* nw = j < G ? a.q_norm : a.k_norm;
+#pragma unroll
+            for (int r = 0; r < PPL; ++r) {
+                if (lane + r * WAVE < HALF) {
+                    x0[r] = *gmem(nw + i0[r]) * (x0[r] * rs);
+                    x1[r] = *gmem(nw + i1[r]) * (x1[r] * rs);
+                }
             }
         }
-        if (lane < HALF) {
-            const float c = *gmem(a.cos_row + lane), s = *gmem(a.sin_row + lane);
-            const float y0 = fmaf(x0, c, -x1 * s);
-            const float y1 = fmaf(x0, s, x1 * c);
-            float* dst = j < G ? qs + j * HD : knew;
-            dst[i0] = y0;
-            dst[i1] = y1;
-            if (j == G) {  // append k at slot p
-                *gmem(a.kc + int64_t(p) * HD + i0) = y0;
-                *gmem(a.kc + int64_t(p) * HD + i1) = y1;
+        float* dst = j < G ? qs + j * HD : knew;
+#pragma unroll
+        for (int r = 0; r < PPL; ++r) {
+            const int i = lane + r * WAVE;
+            if (i < HALF) {
+                const float c = *gmem(a.cos_row + i), s = *gmem(a.sin_row + i);
+                const float y0 = fmaf(x0[r], c, -x1[r] * s);
+                const float y1 = fmaf(x0[r], s, x1[r] * c);
+                dst[i0[r]] = y0;
+                dst[i1[r]] = y1;
+                if (j == G) {  // append k at slot p
+                    *gmem(a.kc + int64_t(p) * HD + i0[r]) = y0;
+                    *gmem(a.kc + int64_t(p) * HD + i1[r]) = y1;
+                }
             }
         }
     }

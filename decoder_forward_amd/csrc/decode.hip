@@ -36,10 +36,11 @@ matvec_kernel(const void* __restrict__ W, const uint16_t* __restrict__ scales, M
 template <int WT, int MODE, bool NORM>
 hipError_t launch_mv_t(const Weight& W, const float* x, const float* nw,
                        float eps, int64_t n_out, int64_t up_rows, float* out,
-                       hipStream_t s)
+                       hipStream_t s, int act)
 {
     int64_t blocks = 0;
-    const MvLayout L = make_mv_layout(WT, W.cols, n_out, up_rows, 512, 8, &blocks);
+    MvLayout L = make_mv_layout(WT, W.cols, n_out, up_rows, 512, 8, &blocks);
+    L.act = act;
     const size_t lds = mv_lds_bytes(L, MODE);
     if (lds > 65536) {  // x of more than 16384 values: opt in to the larger LDS
         const hipError_t r = hipFuncSetAttribute(
@@ -55,19 +56,19 @@ hipError_t launch_mv_t(const Weight& W, const float* x, const float* nw,
 template <int WT>
 hipError_t launch_mv_w(const Weight& W, int mode, const float* x,
                        const float* nw, float eps, int64_t n_out,
-                       int64_t up_rows, float* out, hipStream_t s)
+                       int64_t up_rows, float* out, hipStream_t s, int act)
 {
     const bool norm = nw != nullptr;
     switch (mode) {
     case MV_STORE:
-        return norm ? launch_mv_t<WT, MV_STORE, true>(W, x, nw, eps, n_out, up_rows, out, s)
-                    : launch_mv_t<WT, MV_STORE, false>(W, x, nw, eps, n_out, up_rows, out, s);
+        return norm ? launch_mv_t<WT, MV_STORE, true>(W, x, nw, eps, n_out, up_rows, out, s, act)
+                    : launch_mv_t<WT, MV_STORE, false>(W, x, nw, eps, n_out, up_rows, out, s, act);
     case MV_RESID:
-        return norm ? launch_mv_t<WT, MV_RESID, true>(W, x, nw, eps, n_out, up_rows, out, s)
-                    : launch_mv_t<WT, MV_RESID, false>(W, x, nw, eps, n_out, up_rows, out, s);
+        return norm ? launch_mv_t<WT, MV_RESID, true>(W, x, nw, eps, n_out, up_rows, out, s, act)
+                    : launch_mv_t<WT, MV_RESID, false>(W, x, nw, eps, n_out, up_rows, out, s, act);
     case MV_SWIGLU:
-        return norm ? launch_mv_t<WT, MV_SWIGLU, true>(W, x, nw, eps, n_out, up_rows, out, s)
-                    : launch_mv_t<WT, MV_SWIGLU, false>(W, x, nw, eps, n_out, up_rows, out, s);
+        return norm ? launch_mv_t<WT, MV_SWIGLU, true>(W, x, nw, eps, n_out, up_rows, out, s, act)
+                    : launch_mv_t<WT, MV_SWIGLU, false>(W, x, nw, eps, n_out, up_rows, out, s, act);
     }
     return hipErrorInvalidValue;
 }
@@ -79,7 +80,7 @@ template <int WT>
 __global__ void embed_kernel(const void* __restrict__ E, int64_t d,
                              const int* __restrict__ tokens,
                              const int* __restrict__ state_tok,
-                             float* __restrict__ x)
+                             float* __restrict__ x, float scale)
 {
     const int row = blockIdx.x;
     const int t = tokens ? tokens[row] : *state_tok;
@@ -87,7 +88,44 @@ __global__ void embed_kernel(const void* __restrict__ E, int64_t d,
         float v;
         if constexpr (WT == W_F32) v = static_cast<const float*>(E)[int64_t(t) * d + i];
         else v = f16_bits_to_f32(static_cast<const uint16_t*>(E)[int64_t(t) * d + i]);
-        x[int64_t(row) * d + i] = v;
+        x[int64_t(row) * d + i] = v * scale;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// rms_norm of a matmul output added to the residual stream (gemma3's norms
+// after o and after down): x[row] += w . t[row] / sqrt(mean(t[row]^2) + eps).
+// One block per row; the row is held in registers between the two passes.
+// ---------------------------------------------------------------------------
+constexpr int NA_THREADS = 1024;
+constexpr int NA_PER_THREAD = (MAX_WIDTH + NA_THREADS - 1) / NA_THREADS;
+
+__global__ void __launch_bounds__(NA_THREADS)
+norm_add_rows_kernel(float* __restrict__ x, const float* __restrict__ t,
+                     const float* __restrict__ w, int d, float eps)
+{
+    __shared__ float red[NA_THREADS / WAVE];
+    const int64_t row = blockIdx.x;
+    const float* tr = t + row * d;
+    float* xr = x + row * d;
+    float v[NA_PER_THREAD];
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < NA_PER_THREAD; ++i) {
+        const int k = threadIdx.x + i * NA_THREADS;
+        v[i] = k < d ? tr[k] : 0.f;
+        ss = fmaf(v[i], v[i], ss);
+    }
+    ss = wave_sum(ss);
+    if ((threadIdx.x & (WAVE - 1)) == 0) red[threadIdx.x / WAVE] = ss;
+    __syncthreads();
+    float tot = 0.f;
+    for (int i = 0; i < NA_THREADS / WAVE; ++i) tot += red[i];
+    const float r = 1.0f / sqrtf(tot / static_cast<float>(d) + eps);
+#pragma unroll
+    for (int i = 0; i < NA_PER_THREAD; ++i) {
+        const int k = threadIdx.x + i * NA_THREADS;
+        if (k < d) xr[k] += w[k] * (v[i] * r);
     }
 }
 
@@ -103,16 +141,20 @@ __global__ void embed_kernel(const void* __restrict__ E, int64_t d,
 // softmax over its rows. One work-group per head writes the output itself;
 // otherwise each writes its (acc, max, sum) partial for the merge kernel.
 // ---------------------------------------------------------------------------
+template <int HD>
+constexpr int attn_waves() { return HD >= 256 ? 8 : 4; }
+
 template <int HD, int G>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(64 * attn_waves<HD>())
 attn_decode_kernel(AttnDecodeArgs a)
 {
-    constexpr int NW = 4;
+    constexpr int NW = attn_waves<HD>();
     __shared__ float lds[attn_core_lds_floats<HD, G, NW>()];
     const int split = blockIdx.x;
     const int g = blockIdx.y;
     const int p = *gmem(a.state_pos);
-    const int tiles = (p + 1 + ATTN_T - 1) / ATTN_T;
+    const int lo = attn_first_pos(p, a.window);
+    const int tiles = (p + 1 - lo + ATTN_T - 1) / ATTN_T;
     const int tpw = (tiles + ATTN_MAX_SPLIT - 1) / ATTN_MAX_SPLIT;  // tiles per work-group
     const int n_active = (tiles + tpw - 1) / tpw;
     if (split >= n_active) return;
@@ -131,8 +173,8 @@ attn_decode_kernel(AttnDecodeArgs a)
     it.kvd = a.n_kv * HD;
     it.g = g;
     it.p = p;
-    it.pos0 = split * tpw * ATTN_T;
-    it.pos1 = min(p + 1, (split + 1) * tpw * ATTN_T);
+    it.pos0 = lo + split * tpw * ATTN_T;
+    it.pos1 = min(p + 1, lo + (split + 1) * tpw * ATTN_T);
     it.out = n_active == 1 ? a.out : nullptr;
     it.part = a.part + (int64_t(g) * ATTN_MAX_SPLIT + split) * attn_part_stride(G, HD);
     attn_core<HD, G, NW, ATTN_T / (NW * 4), false, false>(it, lds, threadIdx.x);
@@ -157,7 +199,7 @@ attn_combine_kernel(AttnDecodeArgs a)
     const int g = hq / G, j = hq % G;
     const int tid = threadIdx.x;
     const int p = *a.state_pos;
-    const int tiles = (p + 1 + T - 1) / T;
+    const int tiles = (p + 1 - attn_first_pos(p, a.window) + T - 1) / T;
     const int tpw = (tiles + ATTN_MAX_SPLIT - 1) / ATTN_MAX_SPLIT;
     const int n_active = (tiles + tpw - 1) / tpw;
     if (n_active == 1) return;  // the split kernel wrote the output itself
@@ -363,27 +405,27 @@ size_t mv_lds_bytes(const MvLayout& L, int mode)
 
 hipError_t launch_matvec(const Weight& W, int mode, const float* x,
                          const float* norm_w, float eps, int64_t n_out,
-                         int64_t up_rows, float* out, hipStream_t s)
+                         int64_t up_rows, float* out, hipStream_t s, int act)
 {
     if (n_out <= 0) return hipSuccess;
     switch (W.dtype) {
-    case W_F32: return launch_mv_w<W_F32>(W, mode, x, norm_w, eps, n_out, up_rows, out, s);
-    case W_F16: return launch_mv_w<W_F16>(W, mode, x, norm_w, eps, n_out, up_rows, out, s);
-    case W_Q8: return launch_mv_w<W_Q8>(W, mode, x, norm_w, eps, n_out, up_rows, out, s);
+    case W_F32: return launch_mv_w<W_F32>(W, mode, x, norm_w, eps, n_out, up_rows, out, s, act);
+    case W_F16: return launch_mv_w<W_F16>(W, mode, x, norm_w, eps, n_out, up_rows, out, s, act);
+    case W_Q8: return launch_mv_w<W_Q8>(W, mode, x, norm_w, eps, n_out, up_rows, out, s, act);
     }
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_embed(const Weight& E, const int* tokens_dev,
                         const int* state_tok, int n_rows, float* x,
-                        hipStream_t s)
+                        hipStream_t s, float scale)
 {
     if (E.dtype == W_F32)
         DFK_LAUNCH(embed_kernel<W_F32>, dim3(n_rows), dim3(256), 0, s,
-                           E.data, E.cols, tokens_dev, state_tok, x);
+                           E.data, E.cols, tokens_dev, state_tok, x, scale);
     else
         DFK_LAUNCH(embed_kernel<W_F16>, dim3(n_rows), dim3(256), 0, s,
-                           E.data, E.cols, tokens_dev, state_tok, x);
+                           E.data, E.cols, tokens_dev, state_tok, x, scale);
     return hipGetLastError();
 }
 
@@ -391,14 +433,14 @@ template <int HD>
 hipError_t launch_attn_hd(const AttnDecodeArgs& a, dim3 grid, hipStream_t s)
 {
     switch (a.n_heads / a.n_kv) {
-    case 1: DFK_LAUNCH((attn_decode_kernel<HD, 1>), grid, dim3(256), 0, s, a); break;
-    case 2: DFK_LAUNCH((attn_decode_kernel<HD, 2>), grid, dim3(256), 0, s, a); break;
-    case 3: DFK_LAUNCH((attn_decode_kernel<HD, 3>), grid, dim3(256), 0, s, a); break;
-    case 4: DFK_LAUNCH((attn_decode_kernel<HD, 4>), grid, dim3(256), 0, s, a); break;
-    case 5: DFK_LAUNCH((attn_decode_kernel<HD, 5>), grid, dim3(256), 0, s, a); break;
-    case 6: DFK_LAUNCH((attn_decode_kernel<HD, 6>), grid, dim3(256), 0, s, a); break;
-    case 7: DFK_LAUNCH((attn_decode_kernel<HD, 7>), grid, dim3(256), 0, s, a); break;
-    case 8: DFK_LAUNCH((attn_decode_kernel<HD, 8>), grid, dim3(256), 0, s, a); break;
+    case 1: DFK_LAUNCH((attn_decode_kernel<HD, 1>), grid, dim3(64 * attn_waves<HD>()), 0, s, a); break;
+    case 2: DFK_LAUNCH((attn_decode_kernel<HD, 2>), grid, dim3(64 * attn_waves<HD>()), 0, s, a); break;
+    case 3: DFK_LAUNCH((attn_decode_kernel<HD, 3>), grid, dim3(64 * attn_waves<HD>()), 0, s, a); break;
+    case 4: DFK_LAUNCH((attn_decode_kernel<HD, 4>), grid, dim3(64 * attn_waves<HD>()), 0, s, a); break;
+    case 5: DFK_LAUNCH((attn_decode_kernel<HD, 5>), grid, dim3(64 * attn_waves<HD>()), 0, s, a); break;
+    case 6: DFK_LAUNCH((attn_decode_kernel<HD, 6>), grid, dim3(64 * attn_waves<HD>()), 0, s, a); break;
+    case 7: DFK_LAUNCH((attn_decode_kernel<HD, 7>), grid, dim3(64 * attn_waves<HD>()), 0, s, a); break;
+    case 8: DFK_LAUNCH((attn_decode_kernel<HD, 8>), grid, dim3(64 * attn_waves<HD>()), 0, s, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -412,6 +454,7 @@ hipError_t launch_attn_decode(const AttnDecodeArgs& a, hipStream_t s)
     case 32: return launch_attn_hd<32>(a, grid, s);
     case 64: return launch_attn_hd<64>(a, grid, s);
     case 128: return launch_attn_hd<128>(a, grid, s);
+    case 256: return launch_attn_hd<256>(a, grid, s);
     }
     return hipErrorInvalidValue;
 }
@@ -424,8 +467,18 @@ hipError_t launch_attn_combine(const AttnDecodeArgs& a, hipStream_t s)
     case 32: DFK_LAUNCH(attn_combine_kernel<32>, grid, dim3(128), 0, s, a); break;
     case 64: DFK_LAUNCH(attn_combine_kernel<64>, grid, dim3(256), 0, s, a); break;
     case 128: DFK_LAUNCH(attn_combine_kernel<128>, grid, dim3(512), 0, s, a); break;
+    case 256: DFK_LAUNCH(attn_combine_kernel<256>, grid, dim3(1024), 0, s, a); break;
     default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_norm_add_rows(float* x, const float* t, const float* w, int rows, int d,
+                                float eps, hipStream_t s)
+{
+    if (rows <= 0) return hipSuccess;
+    if (d > MAX_WIDTH) return hipErrorInvalidValue;
+    DFK_LAUNCH(norm_add_rows_kernel, dim3(rows), dim3(NA_THREADS), 0, s, x, t, w, d, eps);
     return hipGetLastError();
 }
 

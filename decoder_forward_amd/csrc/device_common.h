@@ -56,6 +56,7 @@ __device__ inline float f16_bits_to_f32(uint16_t b)
     return static_cast<float>(__builtin_bit_cast(_Float16, b));
 }
 
+
 // Cross-work-group hand-off without cache-wide fences. Values another
 // work-group will read are stored with relaxed agent-scope atomics (written
 // through to the coherence point, bypassing the per-XCD L2), every wave waits
@@ -398,7 +399,7 @@ __device__ inline void mv_finish(const uint16_t* scales, const void* W, const Mv
         if constexpr (MODE == MV_SWIGLU) {
             const float g = acc[0] * r;
             const float u = acc[1] * r;
-            act_st<COH>(out + unit, (g / (1.0f + expf(-g))) * u);
+            act_st<COH>(out + unit, gate_act(g, L.act) * u);
         } else if constexpr (MODE == MV_RESID) {
             act_st<COH>(out + unit, act_ld<COH>(out + unit) + acc[0] * r);
         } else {

@@ -22,7 +22,7 @@ LaunchTiming& launch_timing();
 #define DFK_LAUNCH(kernel, grid, block, lds, stream, ...)                                      \
     do {                                                                                      \
         ::dfk::LaunchTiming& lt_ = ::dfk::launch_timing();                                    \
-        if (lt_.start)                                                                        \
+        if (lt_.start || lt_.stop)                                                            \
             hipExtLaunchKernelGGL(kernel, grid, block, lds, stream, lt_.start, lt_.stop, 0u,  \
                                   __VA_ARGS__);                                               \
         else                                                                                  \
@@ -30,6 +30,9 @@ LaunchTiming& launch_timing();
     } while (0)
 
 enum WType { W_F32 = 0, W_F16 = 1, W_Q8 = 2 };
+
+// Widest activation row a kernel handles (d_model, ffn_dim, n_heads*hd).
+constexpr int MAX_WIDTH = 32768;
 
 // A device matrix [rows][cols] (y = W h). f32 / f16: `data` holds the
 // values row-major. Q8: `data` holds the int8 values row-major and `scales`
@@ -44,10 +47,23 @@ struct Weight {
 // Epilogues of the decode matvec.
 //   MV_STORE : out[n]  = r * (W (x . w))[n]
 //   MV_RESID : out[n] += r * (W (x . w))[n]            (residual add)
-//   MV_SWIGLU: out[f]  = silu(r (W (x . w))[f]) * r (W (x . w))[f + up_rows]
+//   MV_SWIGLU: out[f]  = act(r (W (x . w))[f]) * r (W (x . w))[f + up_rows]
 // where (x . w) is x times the norm weight and r = 1/sqrt(mean(x^2) + eps)
-// when a norm weight is given, else x and r = 1.
+// when a norm weight is given, else x and r = 1; act is silu or gelu_tanh.
 enum MatvecMode { MV_STORE = 0, MV_RESID = 1, MV_SWIGLU = 2 };
+// Gate activation of the gated FFN.
+enum GateAct { ACT_SILU = 0, ACT_GELU_TANH = 1 };
+// Gate activation of the gated FFN (GateAct): silu(g) = g / (1 + e^-g), or
+// gelu_tanh(g) = g/2 (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3))), the tanh
+// form of gelu (page "Local inference and architectures", "The operations").
+__device__ inline float gate_act(float g, int act)
+{
+    if (act == ACT_GELU_TANH) {
+        constexpr float k = 0.7978845608028654f;  // sqrt(2/pi)
+        return 0.5f * g * (1.0f + tanhf(k * fmaf(0.044715f * g, g * g, g)));
+    }
+    return g / (1.0f + expf(-g));
+}
 
 // Work layout of a decode matvec over a grid of blocks of waves (see
 // device_common.h): units per block, K slices per unit, chunks per slice,
@@ -58,6 +74,7 @@ struct MvLayout {
     int log_s;
     int cps;
     int ipw;
+    int act = ACT_SILU;  // MV_SWIGLU's gate activation
 };
 // Layout for at most max_blocks blocks of nwaves waves; *blocks gets the
 // blocks it uses.
@@ -88,21 +105,34 @@ constexpr int ATTN_MAX_SPLIT = 128;
 inline constexpr int attn_part_stride(int G, int hd) { return G * hd + ((2 * G + 3) & ~3); }
 constexpr int ATTN_MAX_GROUP = 8;
 
-// Work-groups per KV head that decode attention uses at position p.
-inline int attn_splits(int p)
+// First position decode attention reads at position p: 0, or inside a
+// sliding window of `window` positions, p - window + 1.
+__host__ __device__ inline int attn_first_pos(int p, int window)
 {
-    const int tiles = (p + 1 + ATTN_T - 1) / ATTN_T;
+    return window > 0 && p - window + 1 > 0 ? p - window + 1 : 0;
+}
+// Work-groups per KV head that decode attention uses at position p.
+inline int attn_splits(int p, int window = 0)
+{
+    const int tiles = (p + 1 - attn_first_pos(p, window) + ATTN_T - 1) / ATTN_T;
     const int tpw = (tiles + ATTN_MAX_SPLIT - 1) / ATTN_MAX_SPLIT;
     return (tiles + tpw - 1) / tpw;
 }
 
 hipError_t launch_matvec(const Weight& W, int mode, const float* x,
                          const float* norm_w, float eps, int64_t n_out,
-                         int64_t up_rows, float* out, hipStream_t s);
+                         int64_t up_rows, float* out, hipStream_t s,
+                         int act = ACT_SILU);
 
+// x[row] = f32(E[token]) * scale.
 hipError_t launch_embed(const Weight& E, const int* tokens_dev,
                         const int* state_tok, int n_rows, float* x,
-                        hipStream_t s);
+                        hipStream_t s, float scale = 1.0f);
+
+// x[row] += w . t[row] / sqrt(mean(t[row]^2) + eps) for `rows` rows of d
+// floats: an rms_norm of a matmul output added to the residual stream.
+hipError_t launch_norm_add_rows(float* x, const float* t, const float* w, int rows, int d,
+                                float eps, hipStream_t s);
 
 struct AttnDecodeArgs {
     const float* qkv;          // [n_heads*hd | n_kv*hd | n_kv*hd]
@@ -111,6 +141,7 @@ struct AttnDecodeArgs {
     const float* bias;         // [qd + 2 kvd] q|k|v bias (qwen2) or null
     float eps;
     int adjacent;              // rope pairing: (2i, 2i+1) if set, else (i, i + hd/2)
+    int window;                // > 0: attend to positions p - window < t <= p only
     const float* cos_t;        // [max_ctx][hd/2]
     const float* sin_t;
     float* kc;                 // this layer's K cache [n_kv][max_ctx][hd]
@@ -198,7 +229,7 @@ enum GemmMode {
     GEMM_STORE_F32 = 0,   // C f32  = A B^T
     GEMM_ADD_F32 = 1,     // C f32 += A B^T (residual)
     GEMM_STORE_F16 = 2,   // C f16  = A B^T
-    GEMM_SWIGLU_F16 = 3,  // C f16 [M][N] = silu(A Bg^T) * (A Bu^T); Bu = B + up_rows rows
+    GEMM_SWIGLU_F16 = 3,  // C f16 [M][N] = act(A Bg^T) * (A Bu^T); Bu = B + up_rows rows
 };
 struct GemmArgs {
     const uint16_t* A;
@@ -214,6 +245,7 @@ struct GemmArgs {
     // f16 scale of every 32 values [N][ldb / 32]; B rows are dequantised to
     // f16 (scale * q) on their way into LDS. Null for f16 weights.
     const uint16_t* Bsc;
+    int act;                   // GEMM_SWIGLU_F16's gate activation (GateAct)
 };
 hipError_t launch_gemm(const GemmArgs& g, int mode, hipStream_t s);
 
@@ -239,6 +271,7 @@ struct AttnPrefillArgs {
     const float* vc;
     uint16_t* out16;      // [S][n_heads * hd] f16
     int S, p0, n_heads, n_kv, head_dim, max_ctx;
+    int window;           // > 0: each query sees the keys p - window < t <= p only
 };
 hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t s);
 

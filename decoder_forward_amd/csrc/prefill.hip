@@ -323,7 +323,7 @@ gemm_kernel(GemmArgs g)
                     if (f < g.N) {
                         const float gt = acc[mi][ni][i];
                         const float up = acc[mi][ni + 1][i];
-                        static_cast<uint16_t*>(g.C)[int64_t(r) * g.ldc + f] = f2h((gt / (1.0f + expf(-gt))) * up);
+                        static_cast<uint16_t*>(g.C)[int64_t(r) * g.ldc + f] = f2h(gate_act(gt, g.act) * up);
                     }
                 }
             } else {
@@ -474,7 +474,10 @@ attn_prefill_kernel(AttnPrefillArgs a)
     const int s_last = min(a.S, s0 + 16) - 1;
     const int n_keys = a.p0 + s_last + 1;
     const int tiles = (n_keys + TK - 1) / TK;
-    for (int kt = 0; kt < tiles; ++kt) {
+    // With a window, keys before the first query row's window are skipped
+    // whole tiles at a time and masked inside the first tile used.
+    const int key_lo = a.window > 0 ? max(0, a.p0 + s0 - a.window + 1) : 0;
+    for (int kt = key_lo / TK; kt < tiles; ++kt) {
         const int t0 = kt * TK;
         // K tile (row-major, zero-padded depth): 4 halves per 8-byte store,
         // consecutive threads on consecutive addresses.
@@ -517,8 +520,9 @@ attn_prefill_kernel(AttnPrefillArgs a)
         for (int i = 0; i < 4; ++i) {
             const int qpos = a.p0 + s0 + (l >> 4) * 4 + i;
             float x0 = sc[0][i] * scale, x1 = sc[1][i] * scale;
-            if (t0 + (l & 15) > qpos) x0 = -INFINITY;
-            if (t0 + 16 + (l & 15) > qpos) x1 = -INFINITY;
+            const int kmin = a.window > 0 ? qpos - a.window + 1 : 0;  // first key in the window
+            if (t0 + (l & 15) > qpos || t0 + (l & 15) < kmin) x0 = -INFINITY;
+            if (t0 + 16 + (l & 15) > qpos || t0 + 16 + (l & 15) < kmin) x1 = -INFINITY;
             const float mt = row16_max(fmaxf(x0, x1));
             const float mn = fmaxf(m[i], mt);
             const float p0v = (x0 == -INFINITY) ? 0.f : expf(x0 - mn);
@@ -616,6 +620,7 @@ hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t s)
     case 32: return launch_attn_prefill_hd<32>(a, s);
     case 64: return launch_attn_prefill_hd<64>(a, s);
     case 128: return launch_attn_prefill_hd<128>(a, s);
+    case 256: return launch_attn_prefill_hd<256>(a, s);
     }
     return hipErrorInvalidValue;
 }

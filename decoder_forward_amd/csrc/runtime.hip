@@ -12,6 +12,8 @@
 
 #include "../../include/decfwd.h"
 
+static_assert(dfk::MAX_WIDTH == DF_MAX_WIDTH, "kernel width limit matches the header");
+
 #include <atomic>
 #include <chrono>
 #include <cmath>
@@ -123,6 +125,9 @@ struct Layer {
     float* q_norm = nullptr;
     float* k_norm = nullptr;
     float* bqkv = nullptr;     // qwen2: [q bias | k bias | v bias]
+    float* post_attn_norm = nullptr;  // gemma3: rms_norm of o before the add
+    float* post_ffn_norm = nullptr;   // gemma3: rms_norm of down before the add
+    bool local = false;        // attends through the sliding window, local rope theta
 };
 
 }  // namespace
@@ -149,6 +154,8 @@ struct df_model {
     float* vc = nullptr;
     float* cos_t = nullptr;  // [max_ctx][hd/2]
     float* sin_t = nullptr;
+    float* cos_l = nullptr;  // local layers' table (rope_theta_local), else cos_t
+    float* sin_l = nullptr;
     DevState* state = nullptr;
     float* attn_part = nullptr;
     int* argmax_out = nullptr;
@@ -239,8 +246,18 @@ bool cfg_fail(Fail* e, const char* field, const std::string& reason)
 bool validate_config(const df_config* c, Fail* e)
 {
     if (!c) { *e = {DF_ERR_INVALID_ARGUMENT, "config is NULL"}; return false; }
-    if (c->arch != DF_ARCH_LLAMA && c->arch != DF_ARCH_QWEN3 && c->arch != DF_ARCH_QWEN2)
-        return cfg_fail(e, "arch", fmt("= %d: expected 0 (llama), 1 (qwen3) or 2 (qwen2)", c->arch));
+    if (c->arch != DF_ARCH_LLAMA && c->arch != DF_ARCH_QWEN3 && c->arch != DF_ARCH_QWEN2 &&
+        c->arch != DF_ARCH_GEMMA3)
+        return cfg_fail(e, "arch", fmt("= %d: expected 0 (llama), 1 (qwen3), 2 (qwen2) or 3 (gemma3)",
+                                       c->arch));
+    if (c->sliding_window < 0)
+        return cfg_fail(e, "sliding_window", fmt("= %d: expected >= 0", c->sliding_window));
+    if (c->sliding_window > 0 && c->window_pattern < 1)
+        return cfg_fail(e, "window_pattern", fmt("= %d: expected >= 1 with a sliding window",
+                                                 c->window_pattern));
+    if (!(c->rope_theta_local >= 0) || !std::isfinite(c->rope_theta_local))
+        return cfg_fail(e, "rope_theta_local", fmt("= %g: expected a finite value >= 0 (0: rope_theta)",
+                                                   c->rope_theta_local));
     if (c->rope_pairing != DF_ROPE_HALVES && c->rope_pairing != DF_ROPE_ADJACENT)
         return cfg_fail(e, "rope_pairing", fmt("= %d: expected 0 (halves) or 1 (adjacent)",
                                                c->rope_pairing));
@@ -249,8 +266,9 @@ bool validate_config(const df_config* c, Fail* e)
     if (c->d_model <= 0 || c->d_model % 32 || c->d_model > DF_MAX_WIDTH)
         return cfg_fail(e, "d_model", fmt("= %d: expected a multiple of 32 in 32..%d", c->d_model,
                                           DF_MAX_WIDTH));
-    if (c->head_dim != 16 && c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128)
-        return cfg_fail(e, "head_dim", fmt("= %d: expected 16, 32, 64 or 128", c->head_dim));
+    if (c->head_dim != 16 && c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128 &&
+        c->head_dim != 256)
+        return cfg_fail(e, "head_dim", fmt("= %d: expected 16, 32, 64, 128 or 256", c->head_dim));
     if (c->n_kv_heads <= 0 || c->n_heads <= 0 || c->n_heads % c->n_kv_heads)
         return cfg_fail(e, "n_heads", fmt("= %d with n_kv_heads = %d: n_kv_heads must divide n_heads",
                                           c->n_heads, c->n_kv_heads));
@@ -291,9 +309,16 @@ uint64_t expected_bytes(int dtype, int64_t rows, int64_t cols)
 
 enum Kind { K_EMBED, K_NORM, K_MATMUL, K_BIAS };
 
+// gemma3's embedding scale (the "scale" step after embed): f32(sqrt(d_model)).
+float embed_scale(const df_config& c)
+{
+    return c.arch == DF_ARCH_GEMMA3 ? float(std::sqrt(double(c.d_model))) : 1.0f;
+}
+
 const char* arch_name(int a)
 {
-    return a == DF_ARCH_QWEN3 ? "qwen3" : a == DF_ARCH_QWEN2 ? "qwen2" : "llama";
+    return a == DF_ARCH_QWEN3 ? "qwen3" : a == DF_ARCH_QWEN2 ? "qwen2"
+         : a == DF_ARCH_GEMMA3 ? "gemma3" : "llama";
 }
 
 struct Need {
@@ -322,9 +347,13 @@ std::vector<Need> required_tensors(const df_config* c)
             v.push_back({b + "attn_k.bias", K_BIAS, 1, kvd, true, L + " add_bias k"});
             v.push_back({b + "attn_v.bias", K_BIAS, 1, kvd, true, L + " add_bias v"});
         }
-        if (c->arch == DF_ARCH_QWEN3) {
+        if (c->arch == DF_ARCH_QWEN3 || c->arch == DF_ARCH_GEMMA3) {
             v.push_back({b + "attn_q_norm.weight", K_NORM, 1, hd, true, L + " norm_heads q"});
             v.push_back({b + "attn_k_norm.weight", K_NORM, 1, hd, true, L + " norm_heads k"});
+        }
+        if (c->arch == DF_ARCH_GEMMA3) {
+            v.push_back({b + "post_attention_norm.weight", K_NORM, 1, d, true, L + " rms_norm of o"});
+            v.push_back({b + "post_ffw_norm.weight", K_NORM, 1, d, true, L + " rms_norm of down"});
         }
         v.push_back({b + "attn_output.weight", K_MATMUL, d, qd, true, L + " o matmul"});
         v.push_back({b + "ffn_norm.weight", K_NORM, 1, d, true, L + " rms_norm (ffn)"});
@@ -575,10 +604,15 @@ bool build_weights(df_model* m, const std::map<std::string, const df_tensor*>& T
             !upload_vectors(m, {get(b + "attn_q.bias"), get(b + "attn_k.bias"),
                                 get(b + "attn_v.bias")}, &L.bqkv, "q/k/v biases", e))
             return false;
-        if (c.arch == DF_ARCH_QWEN3) {
+        if (c.arch == DF_ARCH_QWEN3 || c.arch == DF_ARCH_GEMMA3) {
             if (!upload_norm(m, get(b + "attn_q_norm.weight"), &L.q_norm, e)) return false;
             if (!upload_norm(m, get(b + "attn_k_norm.weight"), &L.k_norm, e)) return false;
         }
+        if (c.arch == DF_ARCH_GEMMA3) {
+            if (!upload_norm(m, get(b + "post_attention_norm.weight"), &L.post_attn_norm, e)) return false;
+            if (!upload_norm(m, get(b + "post_ffw_norm.weight"), &L.post_ffn_norm, e)) return false;
+        }
+        L.local = c.sliding_window > 0 && (i + 1) % c.window_pattern != 0;
         if (!upload_matrix(m, {get(b + "attn_output.weight")}, &L.wo, "o weight", e)) return false;
         if (!upload_norm(m, get(b + "ffn_norm.weight"), &L.ffn_norm, e)) return false;
         if (!upload_matrix(m, {get(b + "ffn_gate.weight"), get(b + "ffn_up.weight")}, &L.wgu,
@@ -618,6 +652,28 @@ bool build_weights(df_model* m, const std::map<std::string, const df_tensor*>& T
     if (!check(hipMemcpyAsync(m->sin_t, sn.data(), sn.size() * 4, hipMemcpyHostToDevice, m->stream),
                "rope sin upload", e))
         return false;
+    m->cos_l = m->cos_t;
+    m->sin_l = m->sin_t;
+    if (c.sliding_window > 0 && c.rope_theta_local > 0 && c.rope_theta_local != c.rope_theta) {
+        // the local layers' table, built the same way with their theta; the
+        // host vectors are refilled only after the first upload has finished
+        if (!check(hipStreamSynchronize(m->stream), "rope upload", e)) return false;
+        for (int64_t p = 0; p < c.max_ctx; ++p)
+            for (int64_t i = 0; i < half; ++i) {
+                const double ang = double(p) * std::pow(c.rope_theta_local, -2.0 * double(i) / double(hd));
+                cs[size_t(p * half + i)] = float(std::cos(ang));
+                sn[size_t(p * half + i)] = float(std::sin(ang));
+            }
+        m->cos_l = static_cast<float*>(dev_alloc(m, cs.size() * 4, "local rope cos", e));
+        if (!m->cos_l) return false;
+        m->sin_l = static_cast<float*>(dev_alloc(m, sn.size() * 4, "local rope sin", e));
+        if (!m->sin_l) return false;
+        if (!check(hipMemcpyAsync(m->cos_l, cs.data(), cs.size() * 4, hipMemcpyHostToDevice, m->stream),
+                   "local rope cos upload", e) ||
+            !check(hipMemcpyAsync(m->sin_l, sn.data(), sn.size() * 4, hipMemcpyHostToDevice, m->stream),
+                   "local rope sin upload", e))
+            return false;
+    }
 
     m->zeros = static_cast<uint16_t*>(dev_alloc(m, 256, "zero block", e));
     if (!m->zeros) return false;
@@ -661,6 +717,10 @@ bool setup_step(df_model* m, Fail* e)
 {
     const df_config& c = m->cfg;
     if (c.n_layers == 0) return true;
+    // The step kernel covers the llama / qwen3 / qwen2 step lists with full
+    // attention; gemma3's extra norms, gelu_tanh and windows run as separate
+    // launches.
+    if (c.arch == DF_ARCH_GEMMA3 || c.sliding_window > 0) return true;
     hipDeviceProp_t prop;
     if (!check(hipGetDeviceProperties(&prop, m->device), "device properties", e)) return false;
     const int nb = prop.multiProcessorCount;
@@ -759,6 +819,7 @@ bool setup_step(df_model* m, Fail* e)
 // ---------------------------------------------------------------------------
 struct StepBufs {
     float *x, *qkv, *att, *mid;
+    float* tmp;  // gemma3: o / down output before its rms_norm (d floats)
 };
 
 bool step_buffers(df_model* m, StepBufs* b, Fail* e)
@@ -769,6 +830,11 @@ bool step_buffers(df_model* m, StepBufs* b, Fail* e)
     b->qkv = static_cast<float*>(m->pool.alloc((qd + 2 * kvd) * 4, USAGE_DEVICE, e));
     b->att = static_cast<float*>(m->pool.alloc(qd * 4, USAGE_DEVICE, e));
     b->mid = static_cast<float*>(m->pool.alloc(size_t(c.ffn_dim) * 4, USAGE_DEVICE, e));
+    b->tmp = nullptr;
+    if (c.arch == DF_ARCH_GEMMA3) {
+        b->tmp = static_cast<float*>(m->pool.alloc(size_t(c.d_model) * 4 + 4, USAGE_DEVICE, e));
+        if (!b->tmp) return false;
+    }
     return b->x && b->qkv && b->att && b->mid;
 }
 
@@ -817,8 +883,9 @@ hipError_t launch_class(df_model* m, const StepBufs& b, int kernel, int l, int g
         a.bias = L->bqkv;
         a.eps = eps;
         a.adjacent = c.rope_pairing == DF_ROPE_ADJACENT;
-        a.cos_t = m->cos_t;
-        a.sin_t = m->sin_t;
+        a.cos_t = L->local ? m->cos_l : m->cos_t;
+        a.sin_t = L->local ? m->sin_l : m->sin_t;
+        a.window = L->local ? c.sliding_window : 0;
         a.kc = m->kc + size_t(l) * kv_layer;
         a.vc = m->vc + size_t(l) * kv_layer;
         a.max_ctx = c.max_ctx;
@@ -830,15 +897,33 @@ hipError_t launch_class(df_model* m, const StepBufs& b, int kernel, int l, int g
         a.out = b.att;
         a.grid_splits = grid_splits;
     }
+    const bool gemma = c.arch == DF_ARCH_GEMMA3;
+    // gemma3: the matmul output goes to tmp and its rms_norm is added to x
+    // by a second launch; both count as one launch of the class.
+    auto norm_added = [&](const Weight& W, const float* in, const float* post_w) {
+        const LaunchTiming saved = launch_timing();
+        launch_timing() = LaunchTiming{saved.start, nullptr};
+        hipError_t r = launch_matvec(W, MV_STORE, in, nullptr, eps, c.d_model, 0, b.tmp, m->stream);
+        launch_timing() = LaunchTiming{nullptr, saved.stop};
+        if (r == hipSuccess) r = launch_norm_add_rows(b.x, b.tmp, post_w, 1, c.d_model, eps, m->stream);
+        launch_timing() = saved;
+        return r;
+    };
     switch (kernel) {
-    case DF_K_EMBED: return launch_embed(m->embd, nullptr, &m->state->tok, 1, b.x, m->stream);
+    case DF_K_EMBED:
+        return launch_embed(m->embd, nullptr, &m->state->tok, 1, b.x, m->stream, embed_scale(c));
     case DF_K_QKV: return launch_matvec(L->wqkv, MV_STORE, b.x, L->attn_norm, eps, qd + 2 * kvd, 0, b.qkv, m->stream);
     case DF_K_ATTN: return launch_attn_decode(a, m->stream);
     case DF_K_ATTN_MERGE: return launch_attn_combine(a, m->stream);
-    case DF_K_O: return launch_matvec(L->wo, MV_RESID, b.att, nullptr, eps, c.d_model, 0, b.x, m->stream);
+    case DF_K_O:
+        if (gemma) return norm_added(L->wo, b.att, L->post_attn_norm);
+        return launch_matvec(L->wo, MV_RESID, b.att, nullptr, eps, c.d_model, 0, b.x, m->stream);
     case DF_K_GATE_UP:
-        return launch_matvec(L->wgu, MV_SWIGLU, b.x, L->ffn_norm, eps, c.ffn_dim, c.ffn_dim, b.mid, m->stream);
-    case DF_K_DOWN: return launch_matvec(L->wd, MV_RESID, b.mid, nullptr, eps, c.d_model, 0, b.x, m->stream);
+        return launch_matvec(L->wgu, MV_SWIGLU, b.x, L->ffn_norm, eps, c.ffn_dim, c.ffn_dim, b.mid, m->stream,
+                             gemma ? ACT_GELU_TANH : ACT_SILU);
+    case DF_K_DOWN:
+        if (gemma) return norm_added(L->wd, b.mid, L->post_ffn_norm);
+        return launch_matvec(L->wd, MV_RESID, b.mid, nullptr, eps, c.d_model, 0, b.x, m->stream);
     case DF_K_LOGITS: return launch_matvec(m->out, MV_STORE, b.x, m->out_norm, eps, c.vocab, 0, logits, m->stream);
     }
     return hipErrorInvalidValue;
@@ -992,10 +1077,14 @@ df_status prefill(df_model* m, const int32_t* tokens, int32_t n, float* logits)
     uint16_t* att16 = static_cast<uint16_t*>(A(size_t(S) * qd * 2));
     uint16_t* mid16 = static_cast<uint16_t*>(A(size_t(S) * F * 2));
     int* toks = static_cast<int*>(A(size_t(S) * 4));
-    if (!x || !h16 || !qkv || !q16 || !att16 || !mid16 || !toks) return set_err(m, e.code, e.msg);
+    const bool gemma = c.arch == DF_ARCH_GEMMA3;
+    // gemma3: o / down outputs before their rms_norm
+    float* tmp = gemma ? static_cast<float*>(A(size_t(S) * d * 4)) : nullptr;
+    if (!x || !h16 || !qkv || !q16 || !att16 || !mid16 || !toks || (gemma && !tmp))
+        return set_err(m, e.code, e.msg);
     const size_t kv_layer = size_t(c.n_kv_heads) * size_t(c.max_ctx) * size_t(hd);
     hipError_t r = hipMemcpyAsync(toks, tokens, size_t(S) * 4, hipMemcpyHostToDevice, m->stream);
-    if (r == hipSuccess) r = launch_embed(m->embd, toks, nullptr, S, x, m->stream);
+    if (r == hipSuccess) r = launch_embed(m->embd, toks, nullptr, S, x, m->stream, embed_scale(c));
     for (int l = 0; l < c.n_layers && r == hipSuccess; ++l) {
         const Layer& L = m->layers[size_t(l)];
         r = launch_rmsnorm_rows(x, L.attn_norm, S, d, eps, h16, m->stream);
@@ -1011,7 +1100,7 @@ df_status prefill(df_model* m, const int32_t* tokens, int32_t n, float* logits)
         QkPostArgs qa{};
         qa.qkv = qkv; qa.q_norm = L.q_norm; qa.k_norm = L.k_norm; qa.eps = eps;
         qa.bias = L.bqkv; qa.adjacent = c.rope_pairing == DF_ROPE_ADJACENT;
-        qa.cos_t = m->cos_t; qa.sin_t = m->sin_t;
+        qa.cos_t = L.local ? m->cos_l : m->cos_t; qa.sin_t = L.local ? m->sin_l : m->sin_t;
         qa.kc = m->kc + size_t(l) * kv_layer; qa.vc = m->vc + size_t(l) * kv_layer;
         qa.q16 = q16; qa.S = S; qa.p0 = p0; qa.n_heads = c.n_heads; qa.n_kv = c.n_kv_heads;
         qa.head_dim = hd; qa.max_ctx = c.max_ctx;
@@ -1021,14 +1110,16 @@ df_status prefill(df_model* m, const int32_t* tokens, int32_t n, float* logits)
         aa.q16 = q16; aa.kc = qa.kc; aa.vc = qa.vc; aa.out16 = att16;
         aa.S = S; aa.p0 = p0; aa.n_heads = c.n_heads; aa.n_kv = c.n_kv_heads;
         aa.head_dim = hd; aa.max_ctx = c.max_ctx;
+        aa.window = L.local ? c.sliding_window : 0;
         r = launch_attn_prefill(aa, m->stream);
         if (r != hipSuccess) break;
         g = GemmArgs{};
         g.zeros = m->zeros;
         g.A = att16; g.lda = qd;
         g.B = static_cast<const uint16_t*>(L.wo.data); g.ldb = qd; g.Bsc = L.wo.scales;
-        g.C = x; g.ldc = d; g.M = S; g.N = d; g.K = qd;
-        r = launch_gemm(g, GEMM_ADD_F32, m->stream);
+        g.C = gemma ? tmp : x; g.ldc = d; g.M = S; g.N = d; g.K = qd;
+        r = launch_gemm(g, gemma ? GEMM_STORE_F32 : GEMM_ADD_F32, m->stream);
+        if (r == hipSuccess && gemma) r = launch_norm_add_rows(x, tmp, L.post_attn_norm, S, d, eps, m->stream);
         if (r != hipSuccess) break;
         r = launch_rmsnorm_rows(x, L.ffn_norm, S, d, eps, h16, m->stream);
         if (r != hipSuccess) break;
@@ -1037,14 +1128,16 @@ df_status prefill(df_model* m, const int32_t* tokens, int32_t n, float* logits)
         g.A = h16; g.lda = d;
         g.B = static_cast<const uint16_t*>(L.wgu.data); g.ldb = d; g.Bsc = L.wgu.scales;
         g.C = mid16; g.ldc = F; g.M = S; g.N = F; g.K = d; g.up_rows = F;
+        g.act = gemma ? ACT_GELU_TANH : ACT_SILU;
         r = launch_gemm(g, GEMM_SWIGLU_F16, m->stream);
         if (r != hipSuccess) break;
         g = GemmArgs{};
         g.zeros = m->zeros;
         g.A = mid16; g.lda = F;
         g.B = static_cast<const uint16_t*>(L.wd.data); g.ldb = F; g.Bsc = L.wd.scales;
-        g.C = x; g.ldc = d; g.M = S; g.N = d; g.K = F;
-        r = launch_gemm(g, GEMM_ADD_F32, m->stream);
+        g.C = gemma ? tmp : x; g.ldc = d; g.M = S; g.N = d; g.K = F;
+        r = launch_gemm(g, gemma ? GEMM_STORE_F32 : GEMM_ADD_F32, m->stream);
+        if (r == hipSuccess && gemma) r = launch_norm_add_rows(x, tmp, L.post_ffn_norm, S, d, eps, m->stream);
     }
     if (r == hipSuccess && logits)
         r = launch_matvec(m->out, MV_STORE, x + size_t(S - 1) * d, m->out_norm, eps, c.vocab, 0,
@@ -1204,6 +1297,8 @@ df_status df_session(const df_model* base, int32_t max_ctx, const df_options* op
     m->layers = base->layers;
     m->cos_t = base->cos_t;
     m->sin_t = base->sin_t;
+    m->cos_l = base->cos_l;
+    m->sin_l = base->sin_l;
     m->zeros = base->zeros;
     Fail e{DF_OK, ""};
     bool ok = true;

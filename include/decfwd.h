@@ -70,6 +70,15 @@ typedef int32_t df_status;
 #define DF_ARCH_LLAMA 0
 #define DF_ARCH_QWEN3 1
 #define DF_ARCH_QWEN2 2
+/* gemma3 (20 steps per layer, page "Local inference and architectures",
+ * "What is in effect right now"; gelu_tanh, "The operations"; a window
+ * pattern, "Rules"). Read as: the embedding scaled by f32(sqrt(d_model));
+ * per layer rms_norm, q/k/v matmul, norm_heads q and k, rope, attention
+ * (through the sliding window on the pattern's local layers), o matmul,
+ * rms_norm of o ("blk.<i>.post_attention_norm.weight"), add, rms_norm, gate
+ * matmul, gelu_tanh, up matmul, mul, down matmul, rms_norm of down
+ * ("blk.<i>.post_ffw_norm.weight"), add. */
+#define DF_ARCH_GEMMA3 3
 
 /* RoPE pairing within a head (the pages name rope without fixing the
  * pairing): DF_ROPE_HALVES rotates (t[i], t[i + head_dim/2]),
@@ -91,18 +100,26 @@ typedef int32_t df_status;
 #define DF_Q8_32 2
 
 typedef struct df_config {
-    int32_t arch;        /* DF_ARCH_LLAMA, DF_ARCH_QWEN3 or DF_ARCH_QWEN2 */
+    int32_t arch;        /* DF_ARCH_LLAMA, DF_ARCH_QWEN3, DF_ARCH_QWEN2 or DF_ARCH_GEMMA3 */
     int32_t n_layers;    /* >= 0 */
     int32_t d_model;     /* multiple of 32, <= DF_MAX_WIDTH */
     int32_t n_heads;     /* query heads */
     int32_t n_kv_heads;  /* divides n_heads; n_heads / n_kv_heads <= 8 */
-    int32_t head_dim;    /* 16, 32, 64 or 128; n_heads * head_dim <= DF_MAX_WIDTH */
+    int32_t head_dim;    /* 16, 32, 64, 128 or 256; n_heads * head_dim <= DF_MAX_WIDTH */
     int32_t ffn_dim;     /* multiple of 32, <= DF_MAX_WIDTH */
     int32_t vocab;       /* >= 1 */
     int32_t max_ctx;     /* KV capacity in positions, 1 .. 1048576 */
     int32_t rope_pairing; /* DF_ROPE_HALVES (0) or DF_ROPE_ADJACENT */
     double rope_theta;   /* > 0; angle p * theta^(-2i/head_dim) */
     double rms_eps;      /* >= 0; inside the square root */
+    /* Sliding-window attention (any arch): with sliding_window W > 0, layer
+     * i is local when (i + 1) % window_pattern != 0 and its position p then
+     * attends to the positions p - W < t <= p only, rotating with
+     * rope_theta_local (0: rope_theta); the other layers are global. W = 0:
+     * every layer global. */
+    int32_t sliding_window;  /* >= 0 */
+    int32_t window_pattern;  /* >= 1 when sliding_window > 0 */
+    double rope_theta_local; /* >= 0 */
 } df_config;
 
 /* One weight. name is the GGUF name ("token_embd.weight",

@@ -7,6 +7,8 @@ outputs the oracle can compute.
 * the same shape with 8-bit blocks at contexts 1024 and 8192 (<= 1e-3).
 * qwen2-7B shape, f16, all 28 layers (q/k/v biases, 7 query heads per KV
   head), decode at p = 4096 on a restored cache (<= 1e-4).
+* gemma3-4B shape, f16, all 34 layers (head_dim 256, sliding windows of
+  1024 on the local layers), decode at p = 4096 on a restored cache.
 * qwen3-8B shape, all 36 layers, one bulk prefill of 2048 tokens: against
   GPU token-by-token (<= 5e-3, greedy token identical), and layer 0's K / V
   cache rows at sampled positions against the oracle's step functions (a
@@ -84,6 +86,12 @@ def test_qwen2_7b_f16_decode_at_4096(dfa):
     say("[qwen2-7B shape, 28 layers, f16, q/k/v biases, 7 heads per KV head] "
         "decode at p = 4096, 4097 on a restored cache")
     restored_decode(dfa, synth.config("qwen2_7b"), 4096, 2, 1e-4)
+
+
+def test_gemma3_4b_f16_decode_at_4096(dfa):
+    say("[gemma3-4B shape, 34 layers, f16, head_dim 256, windows of 1024 on 5 of 6 layers] "
+        "decode at p = 4096, 4097 on a restored cache")
+    restored_decode(dfa, synth.config("gemma3_4b"), 4096, 2, 1e-4)
 
 
 @pytest.mark.parametrize("ctx", [1024, 8192])
