@@ -77,7 +77,7 @@ def gate_up_launch_bytes(cfg: dict) -> int:
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_matvec_llama8b_traffic.txt")
 TRAFFIC_SOURCES = [os.path.join(ROOT, "decoder_forward_amd", "csrc", f)
-                   for f in ("device_common.h", "decode.hip")]
+                   for f in ("device_common.h", "decode.hip", "kernels.h")]
 
 
 def kernel_source_hash() -> str:
