@@ -189,6 +189,36 @@ def cpu_baseline(cfg: dict, ctx: int) -> dict:
                        f"scaled to {cfg['n_layers']} layers; cpu {cpu}")}
 
 
+PEAK_MFMA_F16_TFLOPS = 2500.0
+
+
+def prefill_classes(dfa, m, cfg, S):
+    """Per-layer device time of each bulk-prefill launch class at S rows
+    (df_time_prefill: every layer's launches once, back to back between HIP
+    events) and the algorithmic flops of its GEMM (2 S N K; the causal
+    attention 2 S^2 hd n_heads, QK^T and PV over the lower triangle), then
+    the MFMA roofline of the dominant class, the gate/up GEMM. Runs after
+    decode timing: it overwrites cache rows 0..S-1."""
+    d, F, hd = cfg["d_model"], cfg["ffn_dim"], cfg["head_dim"]
+    qd, kvd = cfg["n_heads"] * hd, cfg["n_kv_heads"] * hd
+    flops = {"qkv": 2 * S * (qd + 2 * kvd) * d, "attn": 2 * S * S * hd * cfg["n_heads"],
+             "o": 2 * S * d * qd, "gate_up": 2 * S * 2 * F * d, "down": 2 * S * d * F}
+    out = {}
+    for k in ("qkv", "attn", "o", "gate_up", "down"):
+        us = dfa.df_time_prefill(m.h, k, S, reps=1)
+        out[k] = {"mean_us_per_layer": round(us, 1), "tflops": round(flops[k] / (us * 1e-6) / 1e12, 1),
+                  "mfma_frac": round(flops[k] / (us * 1e-6) / 1e12 / PEAK_MFMA_F16_TFLOPS, 4)}
+    log(f"[bench] prefill classes at S={S}: {json.dumps(out)}")
+    g = out["gate_up"]
+    roof = {"bound": "mfma", "kernel": "prefill gate/up GEMM (f16 MFMA, silu * up epilogue)",
+            "achieved": g["tflops"], "peak": PEAK_MFMA_F16_TFLOPS, "unit": "TFLOP/s",
+            "frac": g["mfma_frac"], "flops_per_launch": flops["gate_up"],
+            "mean_launch_us": g["mean_us_per_layer"],
+            "timing": f"one launch per layer for all {cfg['n_layers']} layers back to back at S={S}, "
+                      "HIP events on the library's stream (includes the row rms_norm launch)"}
+    return out, roof
+
+
 def concurrent_sessions(m, cfg, ctx, max_ctx, first, args):
     """N conversations on the model's weights (df_session), each with the
     same restored context, decoding args.steps greedy tokens at once from N
@@ -249,9 +279,9 @@ def main():
     ap.add_argument("--workload", default="llama_8b",
                     choices=["llama_8b", "llama_8b_q8", "qwen3_8b", "qwen3_0p6b", "qwen2_7b",
                              "gemma3_4b"])
-    ap.add_argument("--context-from", default="restore", choices=["prefill", "restore"],
-                    help="build the context by bulk prefill (default) or by writing "
-                         "synthetic KV rows")
+    ap.add_argument("--context-from", default="prefill", choices=["prefill", "restore"],
+                    help="build the context by bulk prefill of a uniform-random prompt "
+                         "(default, timed) or by writing synthetic KV rows")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--persistent-step", action="store_true",
                     help="one persistent launch per step instead of one per operation class")
@@ -303,10 +333,11 @@ def main():
         t = time.perf_counter()
         m.forward(prompt, logits=True)
         torch.cuda.synchronize()
-        prefill_s = time.perf_counter() - t
+        prefill_wall = time.perf_counter() - t
+        prefill_s = m.timings()["last_prefill_ms"] / 1e3  # HIP events around the launches
         prefill_tps = ctx / prefill_s
-        log(f"[bench] bulk prefill of {ctx} tokens: {prefill_s * 1e3:.1f} ms "
-            f"({prefill_tps:.0f} tokens/s)")
+        log(f"[bench] bulk prefill of {ctx} tokens: {prefill_s * 1e3:.1f} ms device, "
+            f"{prefill_wall * 1e3:.1f} ms wall ({prefill_tps:.0f} tokens/s)")
     else:
         for layer in range(cfg["n_layers"]):
             K, V = synth.make_kv_rows_device(cfg, layer, ctx)
@@ -354,6 +385,7 @@ def main():
         kernels[k] = {"launches_per_step": n, "mean_us": round(us, 2),
                       "ms_per_step": round(us * n / 1e3, 4)}
     rewind()
+    prefill_kernels, pf_roof = prefill_classes(dfa, m, cfg, ctx) if args.context_from == "prefill" else ({}, None)
     gu = kernels["gate_up"]
     gu_bytes = gate_up_launch_bytes(cfg)
     gu_gbps = gu_bytes / (gu["mean_us"] * 1e-6) / 1e9
@@ -412,6 +444,8 @@ def main():
                        "HIP events on the library's stream"),
         },
         "kernels": kernels,
+        "prefill_roofline": pf_roof,
+        "prefill_kernels": prefill_kernels,
         "sessions": sessions,
         "cpu_baseline": cpu,
         "memory": {"weight_bytes": t["weight_bytes"], "kv_bytes": t["kv_bytes"],

@@ -38,9 +38,11 @@ DF_F32, DF_F16, DF_Q8_32 = 0, 1, 2
 EXPORTS = ("df_load", "df_forward", "df_generate", "df_reset_kv_cache",
            "df_free", "df_last_error", "df_get_timings", "df_kv_length",
            "df_argmax", "df_read_kv", "df_write_kv", "df_stream",
-           "df_profile", "df_profile_read", "df_time_kernel", "df_session")
+           "df_profile", "df_profile_read", "df_time_kernel", "df_session",
+           "df_time_prefill")
 KERNELS = {"embed": 0, "qkv": 1, "attn": 2, "o": 3, "gate_up": 4, "down": 5,
            "logits": 6, "argmax": 7, "attn_merge": 8, "step": 9}
+PREFILL_KERNELS = {"qkv": 10, "attn": 11, "o": 12, "gate_up": 13, "down": 14}
 # df_options.flags: every decode step as one persistent launch (opt-in).
 DF_FLAG_PERSISTENT_STEP = 1
 
@@ -115,6 +117,7 @@ def lib() -> C.CDLL:
     L.df_profile.argtypes = [vp, i32, i32]
     L.df_profile_read.argtypes = [vp, i32, P(C.c_int64), P(C.c_double)]
     L.df_time_kernel.argtypes = [vp, i32, i32, P(C.c_double)]
+    L.df_time_prefill.argtypes = [vp, i32, i32, i32, P(C.c_double)]
     for name in EXPORTS:
         if name not in ("df_free", "df_last_error", "df_stream"):
             getattr(L, name).restype = i32
@@ -265,6 +268,14 @@ def df_time_kernel(h, kernel: str, reps: int = 8) -> float:
     """Mean microseconds of one launch of a kernel class, back-to-back replay."""
     us = C.c_double()
     _check(lib().df_time_kernel(h, KERNELS[kernel], reps, C.byref(us)), h)
+    return us.value
+
+
+def df_time_prefill(h, kernel: str, rows: int, reps: int = 2) -> float:
+    """Mean microseconds of one layer's launches of a bulk-prefill class for
+    `rows` rows (overwrites cache rows 0..rows-1)."""
+    us = C.c_double()
+    _check(lib().df_time_prefill(h, PREFILL_KERNELS[kernel], rows, reps, C.byref(us)), h)
     return us.value
 
 

@@ -18,6 +18,10 @@
 // At the end the waves' states meet in LDS and are merged with weights
 // exp(m_w - M) in wave order.
 //
+// The softmax runs in base 2: q is multiplied once by log2(e)/sqrt(hd), so
+// a dot product is s_t * log2(e) and e^{s_t - M} = 2^{s'_t - M'} (one
+// v_exp_f32 per weight); maxima M are kept in these base-2 units.
+//
 // Result: with `out` set (the item covers every row) the normalised output
 // of the G heads; otherwise the partial (sum_t e^{s_t - M} v_t, M, sum_t
 // e^{s_t - M}) per head, merged across items by attn_merge_group.
@@ -179,18 +183,19 @@ __device__ void attn_core(const AttnItem& a, float* lds, int tid)
     }
     __syncthreads();
 
+    // log2(e) / sqrt(hd): scores in base-2 units
+    const float qscale = 1.4426950408889634f / sqrtf(static_cast<float>(HD));
     float q[G][DPL], acc[G][DPL], m[G], l[G];
 #pragma unroll
     for (int j = 0; j < G; ++j) {
 #pragma unroll
         for (int d = 0; d < DPL; ++d) {
-            q[j][d] = qs[j * HD + ds + d];
+            q[j][d] = qs[j * HD + ds + d] * qscale;
             acc[j][d] = 0.f;
         }
         m[j] = -INFINITY;
         l[j] = 0.f;
     }
-    const float scale = 1.0f / sqrtf(static_cast<float>(HD));
 
     auto consume = [&](int s, float (&kk)[ITER][DPL], float (&vv)[ITER][DPL]) {
 #pragma unroll
@@ -210,19 +215,19 @@ __device__ void attn_core(const AttnItem& a, float* lds, int tid)
 #pragma unroll
                 for (int d = 0; d < DPL; ++d) x = fmaf(q[j][d], kk[it][d], x);
                 x = row16_sum(x);
-                sc[it] = row_of(s, it) < a.pos1 ? x * scale : -INFINITY;
+                sc[it] = row_of(s, it) < a.pos1 ? x : -INFINITY;
                 mt = fmaxf(mt, sc[it]);
             }
             mt = fmaxf(fmaxf(lane_value(mt, 0), lane_value(mt, 16)),
                        fmaxf(lane_value(mt, 32), lane_value(mt, 48)));
             const float mn = fmaxf(m[j], mt);
-            const float resc = m[j] == -INFINITY ? 0.f : expf(m[j] - mn);
+            const float resc = m[j] == -INFINITY ? 0.f : exp2_fast(m[j] - mn);
             float ps = 0.f;
 #pragma unroll
             for (int d = 0; d < DPL; ++d) acc[j][d] *= resc;
 #pragma unroll
             for (int it = 0; it < ITER; ++it) {
-                const float pr = sc[it] == -INFINITY ? 0.f : expf(sc[it] - mn);
+                const float pr = sc[it] == -INFINITY ? 0.f : exp2_fast(sc[it] - mn);
                 ps += pr;
 #pragma unroll
                 for (int d = 0; d < DPL; ++d) acc[j][d] = fmaf(pr, vv[it][d], acc[j][d]);
@@ -276,7 +281,7 @@ __device__ void attn_core(const AttnItem& a, float* lds, int tid)
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww) {
             const float mw = sm[ww * G + j];
-            const float f = mw == -INFINITY ? 0.f : expf(mw - M);
+            const float f = mw == -INFINITY ? 0.f : exp2_fast(mw - M);
             v = fmaf(f, red[(ww * G + j) * HD + d], v);
             L = fmaf(f, sl[ww * G + j], L);
         }
@@ -336,7 +341,7 @@ __device__ void attn_merge_group(const float* part_g, int n_items, float* out, f
             for (int b = 0; b < CB; ++b) {
                 const int c = c0 + b * P;
                 if (c < n_items) {
-                    const float f = expf(ms[c * G + j] - M);
+                    const float f = exp2_fast(ms[c * G + j] - M);
                     v.x = fmaf(f, x[b].x, v.x);
                     v.y = fmaf(f, x[b].y, v.y);
                     v.z = fmaf(f, x[b].z, v.z);

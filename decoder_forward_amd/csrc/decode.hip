@@ -181,7 +181,7 @@ attn_decode_kernel(AttnDecodeArgs a)
 }
 
 // Merge of the split partials of one query head (launched after the split
-// kernel, so its stores are visible): weights exp(m_c - M), total sum, and
+// kernel, so its stores are visible): weights 2^(m_c - M) (base-2 maxima), total sum, and
 // the weighted sum of the accumulators in split order. Four groups of HD
 // threads take every fourth split; their sums meet in LDS in fixed order.
 template <int HD>
@@ -216,7 +216,7 @@ attn_combine_kernel(AttnDecodeArgs a)
         M = wave_max(M);
         float L = 0.f;
         for (int c = tid; c < n_active; c += WAVE) {
-            const float e = expf(w[c] - M);
+            const float e = exp2_fast(w[c] - M);  // maxima in base-2 units
             w[c] = e;
             L = fmaf(lsum[c], e, L);
         }

@@ -56,6 +56,10 @@ __device__ inline float f16_bits_to_f32(uint16_t b)
     return static_cast<float>(__builtin_bit_cast(_Float16, b));
 }
 
+// 2^x on the hardware exponential (v_exp_f32); softmax weights only, where
+// results below the normal range may flush to zero.
+__device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
 
 // Cross-work-group hand-off without cache-wide fences. Values another
 // work-group will read are stored with relaxed agent-scope atomics (written

@@ -446,7 +446,9 @@ attn_prefill_kernel(AttnPrefillArgs a)
     const int w = tid >> 6;
     const int j = g * G + w;  // query head
     const int s0 = qb * 16;
-    const float scale = 1.0f / sqrtf(static_cast<float>(HD));
+    // scores in base-2 units (log2(e) / sqrt(hd)), so that each softmax
+    // weight is one hardware exp2
+    const float scale = 1.4426950408889634f / sqrtf(static_cast<float>(HD));
     const int64_t head_base = int64_t(g) * a.max_ctx * HD;
 
     // Q fragments: A[q = l%16][d = kq*32 + (l/16)*8 + i].
@@ -525,10 +527,10 @@ attn_prefill_kernel(AttnPrefillArgs a)
             if (t0 + 16 + (l & 15) > qpos || t0 + 16 + (l & 15) < kmin) x1 = -INFINITY;
             const float mt = row16_max(fmaxf(x0, x1));
             const float mn = fmaxf(m[i], mt);
-            const float p0v = (x0 == -INFINITY) ? 0.f : expf(x0 - mn);
-            const float p1v = (x1 == -INFINITY) ? 0.f : expf(x1 - mn);
+            const float p0v = (x0 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x0 - mn);
+            const float p1v = (x1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x1 - mn);
             const float rs = row16_sum(p0v + p1v);
-            alpha[i] = (m[i] == -INFINITY) ? 0.f : expf(m[i] - mn);
+            alpha[i] = (m[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[i] - mn);
             lsum[i] = lsum[i] * alpha[i] + rs;
             m[i] = mn;
             Ps[w][(l >> 4) * 4 + i][l & 15] = _Float16(p0v);

@@ -1060,88 +1060,126 @@ bool bulk_supported(const df_model* m)
     return m->cfg.n_layers == 0 || m->layers[0].wqkv.dtype == W_F16 || m->layers[0].wqkv.dtype == W_Q8;
 }
 
+// Bulk prefill activations for S rows.
+struct PfBufs {
+    float* x;          // [S][d] residual stream
+    uint16_t* h16;     // [S][d] normed rows, f16
+    float* qkv;        // [S][qd + 2 kvd]
+    uint16_t* q16;     // [S][qd] q after rope, f16
+    uint16_t* att16;   // [S][qd] attention output, f16
+    uint16_t* mid16;   // [S][F] gated FFN activation, f16
+    float* tmp;        // gemma3: [S][d] o / down outputs before their rms_norm
+    int* toks;         // [S]
+};
+
+bool pf_buffers(df_model* m, int S, PfBufs* b, Fail* e)
+{
+    const df_config& c = m->cfg;
+    const size_t d = size_t(c.d_model), F = size_t(c.ffn_dim);
+    const size_t qd = size_t(c.n_heads) * c.head_dim, kvd = size_t(c.n_kv_heads) * c.head_dim;
+    auto A = [&](size_t bytes) { return m->pool.alloc(bytes, USAGE_DEVICE, e); };
+    b->x = static_cast<float*>(A(size_t(S) * d * 4));
+    b->h16 = static_cast<uint16_t*>(A(size_t(S) * d * 2));
+    b->qkv = static_cast<float*>(A(size_t(S) * (qd + 2 * kvd) * 4));
+    b->q16 = static_cast<uint16_t*>(A(size_t(S) * qd * 2));
+    b->att16 = static_cast<uint16_t*>(A(size_t(S) * qd * 2));
+    b->mid16 = static_cast<uint16_t*>(A(size_t(S) * F * 2));
+    b->toks = static_cast<int*>(A(size_t(S) * 4));
+    b->tmp = c.arch == DF_ARCH_GEMMA3 ? static_cast<float*>(A(size_t(S) * d * 4)) : nullptr;
+    return b->x && b->h16 && b->qkv && b->q16 && b->att16 && b->mid16 && b->toks &&
+           (c.arch != DF_ARCH_GEMMA3 || b->tmp);
+}
+
+// The bulk-prefill launches of layer l for S rows at positions p0.., one
+// class at a time (the classes in step-list order):
+//   DF_K_PF_QKV     rms_norm rows -> f16, q/k/v GEMM
+//   DF_K_PF_ATTN    bias + norm_heads + rope + KV append, causal attention
+//   DF_K_PF_O       o GEMM + residual add (gemma3: + rms_norm of o)
+//   DF_K_PF_GATE_UP rms_norm rows -> f16, gate/up GEMM + gate activation * up
+//   DF_K_PF_DOWN    down GEMM + residual add (gemma3: + rms_norm of down)
+hipError_t pf_launch(df_model* m, const PfBufs& b, int kernel, int l, int S, int p0)
+{
+    const df_config& c = m->cfg;
+    const Layer& L = m->layers[size_t(l)];
+    const int d = c.d_model, hd = c.head_dim, F = c.ffn_dim;
+    const int qd = c.n_heads * hd, kvd = c.n_kv_heads * hd;
+    const float eps = float(c.rms_eps);
+    const bool gemma = c.arch == DF_ARCH_GEMMA3;
+    const size_t kv_layer = size_t(c.n_kv_heads) * size_t(c.max_ctx) * size_t(hd);
+    GemmArgs g{};
+    g.zeros = m->zeros;
+    g.M = S;
+    hipError_t r = hipSuccess;
+    switch (kernel) {
+    case DF_K_PF_QKV:
+        r = launch_rmsnorm_rows(b.x, L.attn_norm, S, d, eps, b.h16, m->stream);
+        g.A = b.h16; g.lda = d;
+        g.B = static_cast<const uint16_t*>(L.wqkv.data); g.ldb = d; g.Bsc = L.wqkv.scales;
+        g.C = b.qkv; g.ldc = qd + 2 * kvd; g.N = qd + 2 * kvd; g.K = d;
+        if (r == hipSuccess) r = launch_gemm(g, GEMM_STORE_F32, m->stream);
+        return r;
+    case DF_K_PF_ATTN: {
+        QkPostArgs qa{};
+        qa.qkv = b.qkv; qa.q_norm = L.q_norm; qa.k_norm = L.k_norm; qa.eps = eps;
+        qa.bias = L.bqkv; qa.adjacent = c.rope_pairing == DF_ROPE_ADJACENT;
+        qa.cos_t = L.local ? m->cos_l : m->cos_t; qa.sin_t = L.local ? m->sin_l : m->sin_t;
+        qa.kc = m->kc + size_t(l) * kv_layer; qa.vc = m->vc + size_t(l) * kv_layer;
+        qa.q16 = b.q16; qa.S = S; qa.p0 = p0; qa.n_heads = c.n_heads; qa.n_kv = c.n_kv_heads;
+        qa.head_dim = hd; qa.max_ctx = c.max_ctx;
+        r = launch_qk_post_rows(qa, m->stream);
+        if (r != hipSuccess) return r;
+        AttnPrefillArgs aa{};
+        aa.q16 = b.q16; aa.kc = qa.kc; aa.vc = qa.vc; aa.out16 = b.att16;
+        aa.S = S; aa.p0 = p0; aa.n_heads = c.n_heads; aa.n_kv = c.n_kv_heads;
+        aa.head_dim = hd; aa.max_ctx = c.max_ctx;
+        aa.window = L.local ? c.sliding_window : 0;
+        return launch_attn_prefill(aa, m->stream);
+    }
+    case DF_K_PF_O:
+        g.A = b.att16; g.lda = qd;
+        g.B = static_cast<const uint16_t*>(L.wo.data); g.ldb = qd; g.Bsc = L.wo.scales;
+        g.C = gemma ? static_cast<void*>(b.tmp) : b.x; g.ldc = d; g.N = d; g.K = qd;
+        r = launch_gemm(g, gemma ? GEMM_STORE_F32 : GEMM_ADD_F32, m->stream);
+        if (r == hipSuccess && gemma) r = launch_norm_add_rows(b.x, b.tmp, L.post_attn_norm, S, d, eps, m->stream);
+        return r;
+    case DF_K_PF_GATE_UP:
+        r = launch_rmsnorm_rows(b.x, L.ffn_norm, S, d, eps, b.h16, m->stream);
+        g.A = b.h16; g.lda = d;
+        g.B = static_cast<const uint16_t*>(L.wgu.data); g.ldb = d; g.Bsc = L.wgu.scales;
+        g.C = b.mid16; g.ldc = F; g.N = F; g.K = d; g.up_rows = F;
+        g.act = gemma ? ACT_GELU_TANH : ACT_SILU;
+        if (r == hipSuccess) r = launch_gemm(g, GEMM_SWIGLU_F16, m->stream);
+        return r;
+    case DF_K_PF_DOWN:
+        g.A = b.mid16; g.lda = F;
+        g.B = static_cast<const uint16_t*>(L.wd.data); g.ldb = F; g.Bsc = L.wd.scales;
+        g.C = gemma ? static_cast<void*>(b.tmp) : b.x; g.ldc = d; g.N = d; g.K = F;
+        r = launch_gemm(g, gemma ? GEMM_STORE_F32 : GEMM_ADD_F32, m->stream);
+        if (r == hipSuccess && gemma) r = launch_norm_add_rows(b.x, b.tmp, L.post_ffn_norm, S, d, eps, m->stream);
+        return r;
+    }
+    return hipErrorInvalidValue;
+}
+
 df_status prefill(df_model* m, const int32_t* tokens, int32_t n, float* logits)
 {
     const df_config& c = m->cfg;
     Fail e{DF_OK, ""};
     const int S = n, p0 = m->kv_len;
-    const int d = c.d_model, hd = c.head_dim, F = c.ffn_dim;
-    const int qd = c.n_heads * hd, kvd = c.n_kv_heads * hd;
-    const float eps = float(c.rms_eps);
     m->pool.reset();
-    auto A = [&](size_t bytes) { return m->pool.alloc(bytes, USAGE_DEVICE, &e); };
-    float* x = static_cast<float*>(A(size_t(S) * d * 4));
-    uint16_t* h16 = static_cast<uint16_t*>(A(size_t(S) * d * 2));
-    float* qkv = static_cast<float*>(A(size_t(S) * (qd + 2 * kvd) * 4));
-    uint16_t* q16 = static_cast<uint16_t*>(A(size_t(S) * qd * 2));
-    uint16_t* att16 = static_cast<uint16_t*>(A(size_t(S) * qd * 2));
-    uint16_t* mid16 = static_cast<uint16_t*>(A(size_t(S) * F * 2));
-    int* toks = static_cast<int*>(A(size_t(S) * 4));
-    const bool gemma = c.arch == DF_ARCH_GEMMA3;
-    // gemma3: o / down outputs before their rms_norm
-    float* tmp = gemma ? static_cast<float*>(A(size_t(S) * d * 4)) : nullptr;
-    if (!x || !h16 || !qkv || !q16 || !att16 || !mid16 || !toks || (gemma && !tmp))
-        return set_err(m, e.code, e.msg);
-    const size_t kv_layer = size_t(c.n_kv_heads) * size_t(c.max_ctx) * size_t(hd);
-    hipError_t r = hipMemcpyAsync(toks, tokens, size_t(S) * 4, hipMemcpyHostToDevice, m->stream);
-    if (r == hipSuccess) r = launch_embed(m->embd, toks, nullptr, S, x, m->stream, embed_scale(c));
-    for (int l = 0; l < c.n_layers && r == hipSuccess; ++l) {
-        const Layer& L = m->layers[size_t(l)];
-        r = launch_rmsnorm_rows(x, L.attn_norm, S, d, eps, h16, m->stream);
-        if (r != hipSuccess) break;
-        GemmArgs g{};
-        g.zeros = m->zeros;
-        g.A = h16; g.lda = d;
-        g.B = static_cast<const uint16_t*>(L.wqkv.data); g.ldb = d; g.Bsc = L.wqkv.scales;
-        g.C = qkv; g.ldc = qd + 2 * kvd;
-        g.M = S; g.N = qd + 2 * kvd; g.K = d;
-        r = launch_gemm(g, GEMM_STORE_F32, m->stream);
-        if (r != hipSuccess) break;
-        QkPostArgs qa{};
-        qa.qkv = qkv; qa.q_norm = L.q_norm; qa.k_norm = L.k_norm; qa.eps = eps;
-        qa.bias = L.bqkv; qa.adjacent = c.rope_pairing == DF_ROPE_ADJACENT;
-        qa.cos_t = L.local ? m->cos_l : m->cos_t; qa.sin_t = L.local ? m->sin_l : m->sin_t;
-        qa.kc = m->kc + size_t(l) * kv_layer; qa.vc = m->vc + size_t(l) * kv_layer;
-        qa.q16 = q16; qa.S = S; qa.p0 = p0; qa.n_heads = c.n_heads; qa.n_kv = c.n_kv_heads;
-        qa.head_dim = hd; qa.max_ctx = c.max_ctx;
-        r = launch_qk_post_rows(qa, m->stream);
-        if (r != hipSuccess) break;
-        AttnPrefillArgs aa{};
-        aa.q16 = q16; aa.kc = qa.kc; aa.vc = qa.vc; aa.out16 = att16;
-        aa.S = S; aa.p0 = p0; aa.n_heads = c.n_heads; aa.n_kv = c.n_kv_heads;
-        aa.head_dim = hd; aa.max_ctx = c.max_ctx;
-        aa.window = L.local ? c.sliding_window : 0;
-        r = launch_attn_prefill(aa, m->stream);
-        if (r != hipSuccess) break;
-        g = GemmArgs{};
-        g.zeros = m->zeros;
-        g.A = att16; g.lda = qd;
-        g.B = static_cast<const uint16_t*>(L.wo.data); g.ldb = qd; g.Bsc = L.wo.scales;
-        g.C = gemma ? tmp : x; g.ldc = d; g.M = S; g.N = d; g.K = qd;
-        r = launch_gemm(g, gemma ? GEMM_STORE_F32 : GEMM_ADD_F32, m->stream);
-        if (r == hipSuccess && gemma) r = launch_norm_add_rows(x, tmp, L.post_attn_norm, S, d, eps, m->stream);
-        if (r != hipSuccess) break;
-        r = launch_rmsnorm_rows(x, L.ffn_norm, S, d, eps, h16, m->stream);
-        if (r != hipSuccess) break;
-        g = GemmArgs{};
-        g.zeros = m->zeros;
-        g.A = h16; g.lda = d;
-        g.B = static_cast<const uint16_t*>(L.wgu.data); g.ldb = d; g.Bsc = L.wgu.scales;
-        g.C = mid16; g.ldc = F; g.M = S; g.N = F; g.K = d; g.up_rows = F;
-        g.act = gemma ? ACT_GELU_TANH : ACT_SILU;
-        r = launch_gemm(g, GEMM_SWIGLU_F16, m->stream);
-        if (r != hipSuccess) break;
-        g = GemmArgs{};
-        g.zeros = m->zeros;
-        g.A = mid16; g.lda = F;
-        g.B = static_cast<const uint16_t*>(L.wd.data); g.ldb = F; g.Bsc = L.wd.scales;
-        g.C = gemma ? tmp : x; g.ldc = d; g.M = S; g.N = d; g.K = F;
-        r = launch_gemm(g, gemma ? GEMM_STORE_F32 : GEMM_ADD_F32, m->stream);
-        if (r == hipSuccess && gemma) r = launch_norm_add_rows(x, tmp, L.post_ffn_norm, S, d, eps, m->stream);
-    }
+    PfBufs b{};
+    if (!pf_buffers(m, S, &b, &e)) return set_err(m, e.code, e.msg);
+    static const int classes[] = {DF_K_PF_QKV, DF_K_PF_ATTN, DF_K_PF_O, DF_K_PF_GATE_UP, DF_K_PF_DOWN};
+    hipError_t r = hipMemcpyAsync(b.toks, tokens, size_t(S) * 4, hipMemcpyHostToDevice, m->stream);
+    if (r == hipSuccess) r = launch_embed(m->embd, b.toks, nullptr, S, b.x, m->stream, embed_scale(c));
+    for (int l = 0; l < c.n_layers && r == hipSuccess; ++l)
+        for (int k : classes) {
+            r = pf_launch(m, b, k, l, S, p0);
+            if (r != hipSuccess) break;
+        }
     if (r == hipSuccess && logits)
-        r = launch_matvec(m->out, MV_STORE, x + size_t(S - 1) * d, m->out_norm, eps, c.vocab, 0,
-                          logits, m->stream);
+        r = launch_matvec(m->out, MV_STORE, b.x + size_t(S - 1) * c.d_model, m->out_norm,
+                          float(c.rms_eps), c.vocab, 0, logits, m->stream);
     if (r != hipSuccess) {
         (void)hipGetLastError();
         return set_err(m, DF_ERR_DEVICE, fmt("bulk prefill launch failed: %s", hipGetErrorString(r)));
@@ -1621,6 +1659,48 @@ df_status df_time_kernel(df_model* m, int32_t kernel, int32_t reps, double* mean
     m->ev_kind = 0;
     *mean_us = double(ms) * 1e3 / double(reps * nl);
     return step_check(m, "df_time_kernel");
+}
+
+df_status df_time_prefill(df_model* m, int32_t kernel, int32_t rows, int32_t reps, double* mean_us)
+{
+    if (!m || !mean_us || reps <= 0 || kernel < DF_K_PF_QKV || kernel > DF_K_PF_DOWN)
+        return DF_ERR_INVALID_ARGUMENT;
+    if (rows < 1 || rows > m->cfg.max_ctx)
+        return set_err(m, DF_ERR_INVALID_ARGUMENT,
+                       fmt("df_time_prefill: rows = %d: expected 1..%d", rows, m->cfg.max_ctx));
+    if (m->cfg.n_layers == 0) return set_err(m, DF_ERR_INVALID_ARGUMENT, "df_time_prefill: no layers");
+    if (!bulk_supported(m))
+        return set_err(m, DF_ERR_UNSUPPORTED_OP, "df_time_prefill: bulk prefill needs f16 or 8-bit weights");
+    BusyGuard guard(m);
+    if (!guard.ok) return DF_ERR_BUSY;
+    (void)hipSetDevice(m->device);
+    Fail e{DF_OK, ""};
+    m->pool.reset();
+    PfBufs b{};
+    if (!pf_buffers(m, rows, &b, &e)) return set_err(m, e.code, e.msg);
+    // defined inputs: zero activations (the GEMMs' timing does not depend on values)
+    const df_config& c = m->cfg;
+    const size_t qd = size_t(c.n_heads) * c.head_dim, kvd = size_t(c.n_kv_heads) * c.head_dim;
+    hipError_t r = hipMemsetAsync(b.x, 0, size_t(rows) * c.d_model * 4, m->stream);
+    if (r == hipSuccess) r = hipMemsetAsync(b.h16, 0, size_t(rows) * c.d_model * 2, m->stream);
+    if (r == hipSuccess) r = hipMemsetAsync(b.qkv, 0, size_t(rows) * (qd + 2 * kvd) * 4, m->stream);
+    if (r == hipSuccess) r = hipMemsetAsync(b.att16, 0, size_t(rows) * qd * 2, m->stream);
+    if (r == hipSuccess) r = hipMemsetAsync(b.mid16, 0, size_t(rows) * c.ffn_dim * 2, m->stream);
+    if (r == hipSuccess) r = hipEventRecord(m->ev0, m->stream);
+    const int nl = c.n_layers;
+    for (int rep = 0; rep < reps && r == hipSuccess; ++rep)
+        for (int l = 0; l < nl && r == hipSuccess; ++l) r = pf_launch(m, b, kernel, l, rows, 0);
+    if (r == hipSuccess) r = hipEventRecord(m->ev1, m->stream);
+    if (r == hipSuccess) r = hipEventSynchronize(m->ev1);
+    float ms = 0.f;
+    if (r == hipSuccess) r = hipEventElapsedTime(&ms, m->ev0, m->ev1);
+    if (r != hipSuccess) {
+        (void)hipGetLastError();
+        return set_err(m, DF_ERR_DEVICE, fmt("df_time_prefill: %s", hipGetErrorString(r)));
+    }
+    m->ev_kind = 0;
+    *mean_us = double(ms) * 1e3 / double(reps * nl);
+    return DF_OK;
 }
 
 df_status df_profile(df_model* m, int32_t kernel, int32_t enable)

@@ -265,6 +265,12 @@ void* df_stream(const df_model* m);
 #define DF_K_ATTN_MERGE 8   /* merge of the attention splits */
 #define DF_K_STEP 9         /* the whole decode step as one persistent launch */
 #define DF_K_COUNT 10
+/* Bulk-prefill launch classes, for df_time_prefill. */
+#define DF_K_PF_QKV 10      /* rms_norm rows + q/k/v GEMM */
+#define DF_K_PF_ATTN 11     /* bias / norm_heads / rope / KV append + causal attention */
+#define DF_K_PF_O 12        /* o GEMM + residual add */
+#define DF_K_PF_GATE_UP 13  /* rms_norm rows + gate/up GEMM + gate activation * up */
+#define DF_K_PF_DOWN 14     /* down GEMM + residual add */
 
 /* Time every launch of one kernel class (enable = 1) with start / end
  * stamps taken by the kernel dispatch itself, or stop (enable = 0). The
@@ -286,6 +292,16 @@ df_status df_profile_read(df_model* m, int32_t kernel, int64_t* launches,
  * DF_ERR_UNSUPPORTED_OP). Synchronises. */
 df_status df_time_kernel(df_model* m, int32_t kernel, int32_t reps,
                          double* mean_us);
+
+/* Mean device time of one layer's launches of a bulk-prefill class
+ * (DF_K_PF_QKV .. DF_K_PF_DOWN) for `rows` rows (1 .. max_ctx) at positions
+ * 0..rows-1: each layer's launches in turn, `reps` times, back to back
+ * between one pair of HIP events, on zeroed activation buffers. The KV cache
+ * rows 0..rows-1 are overwritten (DF_K_PF_ATTN) and kv_len is left as it
+ * was. Needs f16 or 8-bit block weights (else DF_ERR_UNSUPPORTED_OP).
+ * Synchronises. */
+df_status df_time_prefill(df_model* m, int32_t kernel, int32_t rows, int32_t reps,
+                          double* mean_us);
 
 #ifdef __cplusplus
 }
