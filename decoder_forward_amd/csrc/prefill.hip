@@ -366,8 +366,9 @@ hipError_t launch_gemm_t(const GemmArgs& g, hipStream_t s)
 
 // ---------------------------------------------------------------------------
 // Per row s (position p0 + s) and head: bias (qwen2), norm_heads (qwen3),
-// RoPE at the position, then q -> Q16[s][head][d] (f16, the attention's A
-// operand) and k (after RoPE), v (+ bias) -> the f32 KV cache at slot p0 + s.
+// RoPE at the position, then q * log2(e)/sqrt(hd) -> Q16[s][head][d] (f16,
+// the attention's operand, scores in base 2) and k (after RoPE), v (+ bias)
+// -> the f32 KV cache at slot p0 + s.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(64)
 qk_post_rows_kernel(QkPostArgs a)
@@ -404,8 +405,11 @@ qk_post_rows_kernel(QkPostArgs a)
     }
     __syncthreads();
     if (is_q) {
+        // q for the attention's A operand: times log2(e) / sqrt(hd) (the
+        // attention takes its softmax in base 2), then rounded to f16 once
         uint16_t* q = a.q16 + (int64_t(s) * a.n_heads + h) * HD;
-        for (int i = lane; i < HD; i += WAVE) q[i] = f2h(v[i]);
+        const float qs = 1.4426950408889634f / sqrtf(static_cast<float>(HD));
+        for (int i = lane; i < HD; i += WAVE) q[i] = f2h(v[i] * qs);
     } else {
         const int64_t slot = (int64_t(g) * a.max_ctx + pos) * HD;
         const int voff = qd + kvd + g * HD;
@@ -418,167 +422,323 @@ qk_post_rows_kernel(QkPostArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// Causal flash attention over the cache for 16 query rows and one KV head;
-// wave w handles query head g*G + w of the group, so each K/V tile is staged
-// once for G heads. Per tile of 32 keys: S = Q K^T (16x32) on
-// v_mfma_f32_16x16x32_f16, mask keys past each row's position, online
-// softmax in f32 (row statistics reduced over the 16 lanes of a DPP row),
-// P rounded to f16 through LDS, O += P V on the same instruction.
+// Causal flash attention over the cache for QB query rows and one KV head;
+// each wave handles 16 * PF_RT rows of one query head of the group, so each
+// K/V tile is staged once for every head and row of the block and each K / V
+// fragment read from LDS feeds PF_RT MFMAs.
+//
+// Per tile of 32 keys, on v_mfma_f32_16x16x32_f16:
+//  * S^T = K Q^T (keys x queries; q arrives pre-scaled by log2(e)/sqrt(hd),
+//    so scores are in base 2): lane l holds 8 keys of query l%16, which is
+//    the layout P needs as the A operand of P V, so P never leaves the
+//    registers; the P V operand pairs keys in the order (l/16)*4 + i,
+//    16 + (l/16)*4 + i, and V is read from LDS in the same order.
+//  * Online softmax with a lazy maximum: each lane keeps the running
+//    maximum of its query and its own partial sum (the sum over the 4 lanes
+//    of a query is taken once, at the end); the maximum moves, with a
+//    cross-lane max and a rescale of O, only when some score of the wave's
+//    tile exceeds it by more than RESCALE_SLACK, so weights stay below
+//    2^slack. O / l is the same either way.
+//  * Keys past each row's position (and before its window) are masked only
+//    in tiles that reach past the block's first row (or before its last
+//    row's window).
+// The next tile's K and V rows are loaded into registers while the current
+// one is computed (when they fit: at most 8 float4 per thread). Query blocks
+// run latest first: they have the most tiles.
 //
 // Lane layout of v_mfma_f32_16x16x32_f16 (checked on the device): lane l
 // supplies A[l%16][(l/16)*8 + i] and B[(l/16)*8 + i][l%16] for i < 8 and
 // receives C[(l/16)*4 + i][l%16] for i < 4.
 // ---------------------------------------------------------------------------
+// Work split: each wave takes PF_RT row tiles of 16 queries of one head;
+// with up to four heads per KV head two waves share a head (the block then
+// holds 2G waves, two per SIMD, so one wave's softmax overlaps the other's
+// matrix work). Rows per block: 16 * PF_RT * waves per head.
+template <int HD>
+constexpr int attn_pf_rt() { return HD >= 256 ? 1 : 2; }
+template <int G>
+constexpr int attn_pf_wph() { return G <= 4 ? 2 : 1; }
 template <int HD, int G>
-__global__ void __launch_bounds__(64 * G)
+constexpr int attn_pf_rows() { return 16 * attn_pf_rt<HD>() * attn_pf_wph<G>(); }
+
+// Slack (base-2 units) by which a score may exceed the running maximum
+// before the maximum moves: weights stay below 2^8, well inside f16 for P.
+constexpr float RESCALE_SLACK = 8.0f;
+
+template <int HD, int G>
+__global__ void __launch_bounds__(64 * G * attn_pf_wph<G>())
 attn_prefill_kernel(AttnPrefillArgs a)
 {
     constexpr int KQ = HD < 32 ? 32 : HD;  // QK depth, zero padded to 32
     constexpr int TK = 32;                  // keys per tile
     constexpr int DB = HD / 16;             // 16-wide output blocks
+    constexpr int QB = attn_pf_rows<HD, G>();  // query rows per block
+    constexpr int RT = attn_pf_rt<HD>();    // 16-row tiles per wave
+    constexpr int WPH = attn_pf_wph<G>();   // waves per head
+    constexpr int NT = 64 * G * WPH;        // threads
+    constexpr int KE = TK * (KQ / 4);       // float4 chunks of a K tile (depth padded)
+    constexpr int VE = (TK / 2) * (HD / 4); // row-pair chunks of a V tile
+    constexpr int KPT = (KE + NT - 1) / NT; // per thread
+    constexpr int VPT = (VE + NT - 1) / NT;
+    constexpr bool PREF = KPT + 2 * VPT <= 8;  // next tile held in registers
     __shared__ __attribute__((aligned(16))) _Float16 Ks[TK][KQ + 8];
     __shared__ __attribute__((aligned(16))) _Float16 Vt[HD][TK + 8];
-    __shared__ _Float16 Ps[G][16][TK + 8];
-    const int qb = blockIdx.x;
+    const int qb = gridDim.x - 1 - blockIdx.x;
     const int g = blockIdx.y;
     const int tid = threadIdx.x;
     const int l = tid & 63;
+    const int lg = l >> 4;    // lane group: keys lg*4 .. lg*4+3 of each 16
+    const int lq = l & 15;    // this lane's query within a row tile
     const int w = tid >> 6;
-    const int j = g * G + w;  // query head
-    const int s0 = qb * 16;
-    // scores in base-2 units (log2(e) / sqrt(hd)), so that each softmax
-    // weight is one hardware exp2
-    const float scale = 1.4426950408889634f / sqrtf(static_cast<float>(HD));
+    const int j = g * G + w % G;  // query head
+    const int s0 = qb * QB;
+    const int r0 = (w / G) * (16 * RT);  // this wave's first row within the block
     const int64_t head_base = int64_t(g) * a.max_ctx * HD;
 
-    // Q fragments: A[q = l%16][d = kq*32 + (l/16)*8 + i].
-    half8 qa[KQ / 32];
-    {
-        const int s = s0 + (l & 15);
+    // Q fragments (the B operand of S^T): B[d = kq*32 + (l/16)*8 + i][q = l%16]
+    // of row tile rt, 8 consecutive dims per 16-byte load.
+    half8 qa[RT][KQ / 32];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int s = s0 + r0 + rt * 16 + lq;
 #pragma unroll
         for (int kq = 0; kq < KQ / 32; ++kq) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int d = kq * 32 + (l >> 4) * 8 + i;
-                qa[kq][i] = (s < a.S && d < HD)
-                                ? __builtin_bit_cast(_Float16, a.q16[(int64_t(s) * a.n_heads + j) * HD + d])
-                                : _Float16(0);
-            }
+            const int d = kq * 32 + lg * 8;
+            qa[rt][kq] = (s < a.S && d < HD)
+                             ? *reinterpret_cast<const half8*>(a.q16 + (int64_t(s) * a.n_heads + j) * HD + d)
+                             : half8{};
         }
     }
-    f32x4 o[DB];
+    f32x4 o[RT][DB];
+    float mq[RT], lsum[RT];  // query rt*16 + l%16: running maximum, this lane's partial sum
 #pragma unroll
-    for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m[4], lsum[4];
+    for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { m[i] = -INFINITY; lsum[i] = 0.f; }
+        for (int db = 0; db < DB; ++db) o[rt][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+        mq[rt] = -INFINITY;
+        lsum[rt] = 0.f;
+    }
 
-    const int s_last = min(a.S, s0 + 16) - 1;
+    const int s_last = min(a.S, s0 + QB) - 1;
     const int n_keys = a.p0 + s_last + 1;
     const int tiles = (n_keys + TK - 1) / TK;
     // With a window, keys before the first query row's window are skipped
     // whole tiles at a time and masked inside the first tile used.
     const int key_lo = a.window > 0 ? max(0, a.p0 + s0 - a.window + 1) : 0;
-    for (int kt = key_lo / TK; kt < tiles; ++kt) {
+    const int kt0 = key_lo / TK;
+    // Tiles whose keys all lie at or before the block's first row and, with
+    // a window, inside its last row's window, need no mask.
+    const int free_hi = a.p0 + s0 - (TK - 1);                            // t0 <= free_hi
+    const int free_lo = a.window > 0 ? a.p0 + s0 + QB - a.window : 0;    // t0 >= free_lo
+
+    // Tile loads: K chunk e (row e / (KQ/4), 4 dims), V row pair e (rows
+    // 2 (e % (TK/2)) and +1, 4 dims at 4 (e / (TK/2))); rows past n_keys and
+    // padded depth read as zero.
+    float4 kr[PREF ? KPT : 1], vr0[PREF ? VPT : 1], vr1[PREF ? VPT : 1];
+    auto load_tile = [&](int kt) {
         const int t0 = kt * TK;
-        // K tile (row-major, zero-padded depth): 4 halves per 8-byte store,
-        // consecutive threads on consecutive addresses.
-        for (int e = tid; e < TK * (KQ / 4); e += 64 * G) {
-            const int r = e / (KQ / 4);
-            const int c = (e % (KQ / 4)) * 4;
-            float4 kv = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (t0 + r < n_keys && c < HD)
-                kv = *reinterpret_cast<const float4*>(a.kc + head_base + int64_t(t0 + r) * HD + c);
-            *reinterpret_cast<uint2*>(&Ks[r][c]) = make_uint2(pack_h2(kv.x, kv.y), pack_h2(kv.z, kv.w));
+#pragma unroll
+        for (int u = 0; u < KPT; ++u) {
+            const int e = tid + u * NT;
+            const int r = e / (KQ / 4), c = (e % (KQ / 4)) * 4;
+            kr[u] = (e < KE && t0 + r < n_keys && c < HD)
+                        ? *reinterpret_cast<const float4*>(a.kc + head_base + int64_t(t0 + r) * HD + c)
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
         }
-        // V tile transposed: a thread takes rows (2i, 2i+1) at 4 dims and
-        // writes 4 half pairs; consecutive threads write consecutive pairs
-        // of one transposed row (no bank conflicts).
-        for (int e = tid; e < (TK / 2) * (HD / 4); e += 64 * G) {
-            const int r = (e % (TK / 2)) * 2;
-            const int c = (e / (TK / 2)) * 4;
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) {
+            const int e = tid + u * NT;
+            const int r = (e % (TK / 2)) * 2, c = (e / (TK / 2)) * 4;
+            const bool ok = e < VE;
+            vr0[u] = ok && t0 + r < n_keys
+                         ? *reinterpret_cast<const float4*>(a.vc + head_base + int64_t(t0 + r) * HD + c)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+            vr1[u] = ok && t0 + r + 1 < n_keys
+                         ? *reinterpret_cast<const float4*>(a.vc + head_base + int64_t(t0 + r + 1) * HD + c)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
+    // K row-major f16 (4 halves per 8-byte store, consecutive threads on
+    // consecutive addresses); V transposed: a thread writes rows (2i, 2i+1)
+    // at 4 dims as 4 half pairs, consecutive threads on consecutive pairs of
+    // one transposed row (no bank conflicts).
+    auto store_k = [&](int r, int c, float4 kv) {
+        *reinterpret_cast<uint2*>(&Ks[r][c]) = make_uint2(pack_h2(kv.x, kv.y), pack_h2(kv.z, kv.w));
+    };
+    auto store_v = [&](int r, int c, float4 v0, float4 v1) {
+        *reinterpret_cast<uint32_t*>(&Vt[c][r]) = pack_h2(v0.x, v1.x);
+        *reinterpret_cast<uint32_t*>(&Vt[c + 1][r]) = pack_h2(v0.y, v1.y);
+        *reinterpret_cast<uint32_t*>(&Vt[c + 2][r]) = pack_h2(v0.z, v1.z);
+        *reinterpret_cast<uint32_t*>(&Vt[c + 3][r]) = pack_h2(v0.w, v1.w);
+    };
+    auto store_tile = [&]() {
+#pragma unroll
+        for (int u = 0; u < KPT; ++u) {
+            const int e = tid + u * NT;
+            if (e < KE) store_k(e / (KQ / 4), (e % (KQ / 4)) * 4, kr[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) {
+            const int e = tid + u * NT;
+            if (e < VE) store_v((e % (TK / 2)) * 2, (e / (TK / 2)) * 4, vr0[u], vr1[u]);
+        }
+    };
+    // Without the register prefetch: each thread converts its chunks one at
+    // a time.
+    auto stage_direct = [&](int kt) {
+        const int t0 = kt * TK;
+        for (int e = tid; e < KE; e += NT) {
+            const int r = e / (KQ / 4), c = (e % (KQ / 4)) * 4;
+            store_k(r, c, (t0 + r < n_keys && c < HD)
+                              ? *reinterpret_cast<const float4*>(a.kc + head_base + int64_t(t0 + r) * HD + c)
+                              : make_float4(0.f, 0.f, 0.f, 0.f));
+        }
+        for (int e = tid; e < VE; e += NT) {
+            const int r = (e % (TK / 2)) * 2, c = (e / (TK / 2)) * 4;
             float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f), v1 = v0;
             if (t0 + r < n_keys) v0 = *reinterpret_cast<const float4*>(a.vc + head_base + int64_t(t0 + r) * HD + c);
             if (t0 + r + 1 < n_keys) v1 = *reinterpret_cast<const float4*>(a.vc + head_base + int64_t(t0 + r + 1) * HD + c);
-            *reinterpret_cast<uint32_t*>(&Vt[c][r]) = pack_h2(v0.x, v1.x);
-            *reinterpret_cast<uint32_t*>(&Vt[c + 1][r]) = pack_h2(v0.y, v1.y);
-            *reinterpret_cast<uint32_t*>(&Vt[c + 2][r]) = pack_h2(v0.z, v1.z);
-            *reinterpret_cast<uint32_t*>(&Vt[c + 3][r]) = pack_h2(v0.w, v1.w);
+            store_v(r, c, v0, v1);
         }
+    };
+
+    if constexpr (PREF) {
+        if (kt0 < tiles) load_tile(kt0);
+    }
+    for (int kt = kt0; kt < tiles; ++kt) {
+        const int t0 = kt * TK;
+        if constexpr (PREF) store_tile();
+        else stage_direct(kt);
         __syncthreads();
-        // Scores for keys kb*16 + l%16, rows (l/16)*4 + i.
-        f32x4 sc[2];
+        if constexpr (PREF) {
+            if (kt + 1 < tiles) load_tile(kt + 1);  // in flight during this tile
+        }
+        // K fragments as the A operand: A[key = kb*16 + l%16][d = kq*32 + (l/16)*8 + i].
+        half8 kf[2][KQ / 32];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int kq = 0; kq < KQ / 32; ++kq) {
-                const half8 kf = *reinterpret_cast<const half8*>(&Ks[kb * 16 + (l & 15)][kq * 32 + (l >> 4) * 8]);
-                sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kq], kf, sc[kb], 0, 0, 0);
+            for (int kq = 0; kq < KQ / 32; ++kq)
+                kf[kb][kq] = *reinterpret_cast<const half8*>(&Ks[kb * 16 + lq][kq * 32 + lg * 8]);
+        // S^T[key = kb*16 + lg*4 + i][query = rt*16 + l%16]
+        f32x4 st[RT][2];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                st[rt][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kq = 0; kq < KQ / 32; ++kq)
+                    st[rt][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[kb][kq], qa[rt][kq], st[rt][kb], 0, 0, 0);
+            }
+        const bool masked = t0 > free_hi || t0 < free_lo;  // uniform
+        bool grow = false;
+        float vmax[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            if (masked) {
+                const int qpos = a.p0 + s0 + r0 + rt * 16 + lq;
+                const int kmin = a.window > 0 ? qpos - a.window + 1 : 0;  // first key in the window
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int key = t0 + kb * 16 + lg * 4 + i;
+                        if (key > qpos || key < kmin) st[rt][kb][i] = -INFINITY;
+                    }
+            }
+            vmax[rt] = fmaxf(fmaxf(fmaxf(st[rt][0][0], st[rt][0][1]), fmaxf(st[rt][0][2], st[rt][0][3])),
+                             fmaxf(fmaxf(st[rt][1][0], st[rt][1][1]), fmaxf(st[rt][1][2], st[rt][1][3])));
+            grow |= vmax[rt] > mq[rt] + RESCALE_SLACK;
+        }
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+            // Move the maxima: the max of each query over its 4 lanes, the
+            // partial sums and O's rows scaled by 2^(old - new).
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                float rm = fmaxf(vmax[rt], __shfl_xor(vmax[rt], 16, WAVE));
+                rm = fmaxf(rm, __shfl_xor(rm, 32, WAVE));
+                const float mn = fmaxf(mq[rt], rm);
+                const float alpha = (mq[rt] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mq[rt] - mn);
+                lsum[rt] *= alpha;
+                mq[rt] = mn;
+                // O row (l/16)*4 + i is query (l/16)*4 + i, whose alpha lane (l/16)*4 + i holds
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float ai = __shfl(alpha, lg * 4 + i, WAVE);
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) o[rt][db][i] *= ai;
+                }
             }
         }
-        float alpha[4];
+        // P = 2^(s - m) in registers, as the A operand of P V (key slots
+        // lg*8 + i: keys lg*4 + i, then 16 + lg*4 + i).
+        half8 pa[RT];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int qpos = a.p0 + s0 + (l >> 4) * 4 + i;
-            float x0 = sc[0][i] * scale, x1 = sc[1][i] * scale;
-            const int kmin = a.window > 0 ? qpos - a.window + 1 : 0;  // first key in the window
-            if (t0 + (l & 15) > qpos || t0 + (l & 15) < kmin) x0 = -INFINITY;
-            if (t0 + 16 + (l & 15) > qpos || t0 + 16 + (l & 15) < kmin) x1 = -INFINITY;
-            const float mt = row16_max(fmaxf(x0, x1));
-            const float mn = fmaxf(m[i], mt);
-            const float p0v = (x0 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x0 - mn);
-            const float p1v = (x1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x1 - mn);
-            const float rs = row16_sum(p0v + p1v);
-            alpha[i] = (m[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[i] - mn);
-            lsum[i] = lsum[i] * alpha[i] + rs;
-            m[i] = mn;
-            Ps[w][(l >> 4) * 4 + i][l & 15] = _Float16(p0v);
-            Ps[w][(l >> 4) * 4 + i][16 + (l & 15)] = _Float16(p1v);
+        for (int rt = 0; rt < RT; ++rt) {
+            float ps = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float x = st[rt][kb][i];
+                    const float pv = (x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x - mq[rt]);
+                    ps += pv;
+                    pa[rt][kb * 4 + i] = static_cast<_Float16>(pv);
+                }
+            lsum[rt] += ps;
         }
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) o[db][i] *= alpha[i];
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // P as the A operand: A[q = l%16][key = (l/16)*8 + i].
-        const half8 pa = *reinterpret_cast<const half8*>(&Ps[w][l & 15][(l >> 4) * 8]);
+        // V fragments in the same key order: B[slot][d = db*16 + l%16].
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            const half8 vb = *reinterpret_cast<const half8*>(&Vt[db * 16 + (l & 15)][(l >> 4) * 8]);
-            o[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vb, o[db], 0, 0, 0);
+            const uint2 v0 = *reinterpret_cast<const uint2*>(&Vt[db * 16 + lq][lg * 4]);
+            const uint2 v1 = *reinterpret_cast<const uint2*>(&Vt[db * 16 + lq][16 + lg * 4]);
+            const half8 vb = __builtin_bit_cast(half8, u32x4{v0.x, v0.y, v1.x, v1.y});
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                o[rt][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[rt], vb, o[rt][db], 0, 0, 0);
         }
         __syncthreads();
     }
-    // O / l -> out[s][j*HD + d] in f16 (the o matmul's A operand).
+    // O / l -> out[s][j*HD + d] in f16 (the o matmul's A operand); l of a
+    // query is the sum of its 4 lanes' partial sums.
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int s = s0 + (l >> 4) * 4 + i;
-        if (s >= a.S) continue;
-        const float inv = 1.0f / lsum[i];
+    for (int rt = 0; rt < RT; ++rt) {
+        float lt = lsum[rt] + __shfl_xor(lsum[rt], 16, WAVE);
+        lt += __shfl_xor(lt, 32, WAVE);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            const int d = db * 16 + (l & 15);
-            a.out16[int64_t(s) * a.n_heads * HD + j * HD + d] = f2h(o[db][i] * inv);
+        for (int i = 0; i < 4; ++i) {
+            const float li = __shfl(lt, lg * 4 + i, WAVE);
+            const int s = s0 + r0 + rt * 16 + lg * 4 + i;
+            if (s >= a.S) continue;
+            const float inv = 1.0f / li;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const int d = db * 16 + lq;
+                a.out16[int64_t(s) * a.n_heads * HD + j * HD + d] = f2h(o[rt][db][i] * inv);
+            }
         }
     }
+}
+
+template <int HD, int G>
+dim3 pf_grid(const AttnPrefillArgs& a)
+{
+    return dim3((a.S + attn_pf_rows<HD, G>() - 1) / attn_pf_rows<HD, G>(), a.n_kv);
 }
 
 template <int HD>
 hipError_t launch_attn_prefill_hd(const AttnPrefillArgs& a, hipStream_t s)
 {
-    const dim3 grid((a.S + 15) / 16, a.n_kv);
     switch (a.n_heads / a.n_kv) {
-    case 1: DFK_LAUNCH((attn_prefill_kernel<HD, 1>), grid, dim3(64), 0, s, a); break;
-    case 2: DFK_LAUNCH((attn_prefill_kernel<HD, 2>), grid, dim3(128), 0, s, a); break;
-    case 3: DFK_LAUNCH((attn_prefill_kernel<HD, 3>), grid, dim3(192), 0, s, a); break;
-    case 4: DFK_LAUNCH((attn_prefill_kernel<HD, 4>), grid, dim3(256), 0, s, a); break;
-    case 5: DFK_LAUNCH((attn_prefill_kernel<HD, 5>), grid, dim3(320), 0, s, a); break;
-    case 6: DFK_LAUNCH((attn_prefill_kernel<HD, 6>), grid, dim3(384), 0, s, a); break;
-    case 7: DFK_LAUNCH((attn_prefill_kernel<HD, 7>), grid, dim3(448), 0, s, a); break;
-    case 8: DFK_LAUNCH((attn_prefill_kernel<HD, 8>), grid, dim3(512), 0, s, a); break;
+    case 1: DFK_LAUNCH((attn_prefill_kernel<HD, 1>), (pf_grid<HD, 1>(a)), dim3(128), 0, s, a); break;
+    case 2: DFK_LAUNCH((attn_prefill_kernel<HD, 2>), (pf_grid<HD, 2>(a)), dim3(256), 0, s, a); break;
+    case 3: DFK_LAUNCH((attn_prefill_kernel<HD, 3>), (pf_grid<HD, 3>(a)), dim3(384), 0, s, a); break;
+    case 4: DFK_LAUNCH((attn_prefill_kernel<HD, 4>), (pf_grid<HD, 4>(a)), dim3(512), 0, s, a); break;
+    case 5: DFK_LAUNCH((attn_prefill_kernel<HD, 5>), (pf_grid<HD, 5>(a)), dim3(320), 0, s, a); break;
+    case 6: DFK_LAUNCH((attn_prefill_kernel<HD, 6>), (pf_grid<HD, 6>(a)), dim3(384), 0, s, a); break;
+    case 7: DFK_LAUNCH((attn_prefill_kernel<HD, 7>), (pf_grid<HD, 7>(a)), dim3(448), 0, s, a); break;
+    case 8: DFK_LAUNCH((attn_prefill_kernel<HD, 8>), (pf_grid<HD, 8>(a)), dim3(512), 0, s, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
