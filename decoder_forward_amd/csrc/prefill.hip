@@ -96,10 +96,11 @@ rmsnorm_rows_kernel(const float* __restrict__ x, const float* __restrict__ w,
 // ---------------------------------------------------------------------------
 // GEMM C[M][N] = A[M][K] B[N][K]^T, f16 operands (both K-contiguous), f32
 // accumulation on v_mfma_f32_32x32x16_f16. BM x BN work-group tile, 64-deep
-// K stages double-buffered in LDS (rows padded by 16 bytes), four waves in a
-// 2x2 arrangement of (BM/2) x (BN/2) wave tiles. A wave reads BM/64 A and
-// BN/64 B fragments from LDS per 16-deep step and issues (BM/64)(BN/64)
-// MFMAs, so larger tiles need less LDS bandwidth per flop.
+// K stages double-buffered in LDS (rows padded by 16 bytes), 2 x WN waves
+// in a grid of (BM/2) x (BN/WN) wave tiles. A wave reads BM/64 A and BN/(32 WN)
+// B fragments from LDS per 16-deep step and issues one MFMA per pair, so
+// larger wave tiles need less LDS bandwidth per flop; 8 waves (two per SIMD)
+// let one wave's LDS traffic and waits overlap the other's MFMAs.
 //
 // Lane layout of v_mfma_f32_32x32x16_f16 (checked on the device): lane l
 // supplies A[l%32][(l/32)*8 + i] and B[(l/32)*8 + i][l%32] for i < 8 and
@@ -111,28 +112,28 @@ rmsnorm_rows_kernel(const float* __restrict__ x, const float* __restrict__ w,
 // sums, and writes f16(silu(g) * u).
 // ---------------------------------------------------------------------------
 constexpr int GBK = 64, GPAD = GBK + 8;
-// Work-group tile of the prefill GEMMs. The gate/up GEMM (twice the columns)
-// takes 256 x 256: half the LDS traffic per flop, and still enough tiles to
-// fill the device at prefill sizes; the others keep 128 x 128 for tile count.
+// Work-group tile of the prefill GEMMs for small problems (fewer than about
+// one 256 x 256 tile per compute unit): 128 x 128 on 4 waves.
 constexpr int GBM_ = 128, GBN_ = 128;
 
 template <int BM, int BN>
 constexpr size_t gemm_lds_bytes() { return size_t(2) * (BM + BN) * GPAD * sizeof(_Float16); }
 
-template <int BM, int BN, int MODE, bool WQ8>
-__global__ void __launch_bounds__(256)
+template <int BM, int BN, int WN, int MODE, bool WQ8>
+__global__ void __launch_bounds__(128 * WN)
 gemm_kernel(GemmArgs g)
 {
-    constexpr int WTM = BM / 2, WTN = BN / 2;
+    constexpr int NT = 128 * WN;               // 2 x WN waves
+    constexpr int WTM = BM / 2, WTN = BN / WN;
     constexpr int MI = WTM / 32, NI = WTN / 32;
-    constexpr int CA = BM / 32, CB = BN / 32;  // 16-byte chunks per thread per stage
+    constexpr int CA = BM * 8 / NT, CB = BN * 8 / NT;  // 16-byte chunks per thread per stage
     extern __shared__ _Float16 gsm[];
     _Float16 (*As)[BM][GPAD] = reinterpret_cast<_Float16 (*)[BM][GPAD]>(gsm);
     _Float16 (*Bs)[BN][GPAD] = reinterpret_cast<_Float16 (*)[BN][GPAD]>(gsm + 2 * BM * GPAD);
     const int tid = threadIdx.x;
     const int l = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WN, wn = wave % WN;
     constexpr int ncols = (MODE == GEMM_SWIGLU_F16) ? BN / 2 : BN;  // outputs per tile
     const int ntn = (g.N + ncols - 1) / ncols;
     const int ntm = (g.M + BM - 1) / BM;
@@ -158,13 +159,13 @@ gemm_kernel(GemmArgs g)
     const uint16_t* sptr[WQ8 ? CB : 1];
 #pragma unroll
     for (int i = 0; i < CA; ++i) {
-        const int c = tid + i * 256;
+        const int c = tid + i * NT;
         const int am = m0 + (c >> 3);
         aptr[i] = am < g.M ? g.A + int64_t(am) * g.lda + (c & 7) * 8 : nullptr;
     }
 #pragma unroll
     for (int i = 0; i < CB; ++i) {
-        const int c = tid + i * 256;
+        const int c = tid + i * NT;
         const int row = c >> 3;
         int bn;
         bool ok;
@@ -201,12 +202,12 @@ gemm_kernel(GemmArgs g)
         u32x4* rb = set == 0 ? rb0 : rb1;
 #pragma unroll
         for (int i = 0; i < CA; ++i) {
-            const bool ok = aptr[i] && k0 + ((tid + i * 256) & 7) * 8 < g.K;
+            const bool ok = aptr[i] && k0 + ((tid + i * NT) & 7) * 8 < g.K;
             ra[i] = *reinterpret_cast<const u32x4*>(ok ? aptr[i] + k0 : g.zeros);
         }
 #pragma unroll
         for (int i = 0; i < CB; ++i) {
-            const int kc = k0 + ((tid + i * 256) & 7) * 8;
+            const int kc = k0 + ((tid + i * NT) & 7) * 8;
             const bool ok = bptr[i] && kc < g.K;
             if constexpr (WQ8) {
                 const uint2 q = *reinterpret_cast<const uint2*>(
@@ -240,12 +241,12 @@ gemm_kernel(GemmArgs g)
         const u32x4* rb = set == 0 ? rb0 : rb1;
 #pragma unroll
         for (int i = 0; i < CA; ++i) {
-            const int c = tid + i * 256;
+            const int c = tid + i * NT;
             *reinterpret_cast<u32x4*>(&As[buf][c >> 3][(c & 7) * 8]) = ra[i];
         }
 #pragma unroll
         for (int i = 0; i < CB; ++i) {
-            const int c = tid + i * 256;
+            const int c = tid + i * NT;
             if constexpr (WQ8) *reinterpret_cast<u32x4*>(&Bs[buf][c >> 3][(c & 7) * 8]) = dequant(rb[i]);
             else *reinterpret_cast<u32x4*>(&Bs[buf][c >> 3][(c & 7) * 8]) = rb[i];
         }
@@ -341,27 +342,27 @@ gemm_kernel(GemmArgs g)
     }
 }
 
-template <int BM, int BN, int MODE, bool WQ8>
+template <int BM, int BN, int WN, int MODE, bool WQ8>
 hipError_t launch_gemm_q(const GemmArgs& g, hipStream_t s)
 {
     constexpr size_t lds = gemm_lds_bytes<BM, BN>();
     static std::atomic<bool> attr_set{false};  // sessions may launch from several threads
     if (!attr_set.load(std::memory_order_acquire)) {
-        const hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<BM, BN, MODE, WQ8>),
+        const hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<BM, BN, WN, MODE, WQ8>),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
         if (r != hipSuccess) return r;
         attr_set.store(true, std::memory_order_release);
     }
     constexpr int ncols = (MODE == GEMM_SWIGLU_F16) ? BN / 2 : BN;
     const int blocks = ((g.N + ncols - 1) / ncols) * ((g.M + BM - 1) / BM);
-    DFK_LAUNCH((gemm_kernel<BM, BN, MODE, WQ8>), dim3(blocks), dim3(256), lds, s, g);
+    DFK_LAUNCH((gemm_kernel<BM, BN, WN, MODE, WQ8>), dim3(blocks), dim3(128 * WN), lds, s, g);
     return hipGetLastError();
 }
 
-template <int BM, int BN, int MODE>
+template <int BM, int BN, int WN, int MODE>
 hipError_t launch_gemm_t(const GemmArgs& g, hipStream_t s)
 {
-    return g.Bsc ? launch_gemm_q<BM, BN, MODE, true>(g, s) : launch_gemm_q<BM, BN, MODE, false>(g, s);
+    return g.Bsc ? launch_gemm_q<BM, BN, WN, MODE, true>(g, s) : launch_gemm_q<BM, BN, WN, MODE, false>(g, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -757,11 +758,19 @@ hipError_t launch_rmsnorm_rows(const float* x, const float* w, int rows, int d, 
 hipError_t launch_gemm(const GemmArgs& g, int mode, hipStream_t s)
 {
     if (g.M <= 0 || g.N <= 0) return hipSuccess;
+    // 256 x 256 tiles on 8 waves (two per SIMD, each 128 x 64) where they
+    // still give about one tile per compute unit; else 128 x 128 on 4 waves.
+    const int64_t cols = mode == GEMM_SWIGLU_F16 ? 128 : 256;
+    const bool big = int64_t((g.M + 255) / 256) * ((g.N + cols - 1) / cols) >= 240;
     switch (mode) {
-    case GEMM_STORE_F32: return launch_gemm_t<GBM_, GBN_, GEMM_STORE_F32>(g, s);
-    case GEMM_ADD_F32: return launch_gemm_t<GBM_, GBN_, GEMM_ADD_F32>(g, s);
-    case GEMM_STORE_F16: return launch_gemm_t<GBM_, GBN_, GEMM_STORE_F16>(g, s);
-    case GEMM_SWIGLU_F16: return launch_gemm_t<256, 256, GEMM_SWIGLU_F16>(g, s);
+    case GEMM_STORE_F32:
+        return big ? launch_gemm_t<256, 256, 4, GEMM_STORE_F32>(g, s) : launch_gemm_t<GBM_, GBN_, 2, GEMM_STORE_F32>(g, s);
+    case GEMM_ADD_F32:
+        return big ? launch_gemm_t<256, 256, 4, GEMM_ADD_F32>(g, s) : launch_gemm_t<GBM_, GBN_, 2, GEMM_ADD_F32>(g, s);
+    case GEMM_STORE_F16:
+        return big ? launch_gemm_t<256, 256, 4, GEMM_STORE_F16>(g, s) : launch_gemm_t<GBM_, GBN_, 2, GEMM_STORE_F16>(g, s);
+    case GEMM_SWIGLU_F16:
+        return big ? launch_gemm_t<256, 256, 4, GEMM_SWIGLU_F16>(g, s) : launch_gemm_t<GBM_, GBN_, 2, GEMM_SWIGLU_F16>(g, s);
     }
     return hipErrorInvalidValue;
 }
