@@ -758,20 +758,24 @@ hipError_t launch_rmsnorm_rows(const float* x, const float* w, int rows, int d, 
 hipError_t launch_gemm(const GemmArgs& g, int mode, hipStream_t s)
 {
     if (g.M <= 0 || g.N <= 0) return hipSuccess;
-    // 256 x 256 tiles on 8 waves (two per SIMD, each 128 x 64) where they
-    // still give about one tile per compute unit; else 128 x 128 on 4 waves.
-    const int64_t cols = mode == GEMM_SWIGLU_F16 ? 128 : 256;
-    const bool big = int64_t((g.M + 255) / 256) * ((g.N + cols - 1) / cols) >= 240;
+    // Tile by grid size (measured on the 8B shapes at 2048 and 4096 rows):
+    // 256 x 256 on 8 waves (two per SIMD, 128 x 64 wave tiles) from about
+    // 160 tiles up; 128 x 256 on 8 waves (64 x 64 wave tiles) below that;
+    // 128 x 128 on 4 waves for small problems.
+    const int64_t cols = mode == GEMM_SWIGLU_F16 ? 128 : 256;  // output columns of a 256-wide B tile
+    const int64_t nt = (g.N + cols - 1) / cols;
+    const int shape = int64_t((g.M + 255) / 256) * nt >= 160 ? 2 : int64_t((g.M + 127) / 128) * nt >= 64 ? 1 : 0;
+#define DF_GEMM_BY_SHAPE(MODE_)                                                  \
+    return shape == 2   ? launch_gemm_t<256, 256, 4, MODE_>(g, s)                \
+           : shape == 1 ? launch_gemm_t<128, 256, 4, MODE_>(g, s)                \
+                        : launch_gemm_t<GBM_, GBN_, 2, MODE_>(g, s);
     switch (mode) {
-    case GEMM_STORE_F32:
-        return big ? launch_gemm_t<256, 256, 4, GEMM_STORE_F32>(g, s) : launch_gemm_t<GBM_, GBN_, 2, GEMM_STORE_F32>(g, s);
-    case GEMM_ADD_F32:
-        return big ? launch_gemm_t<256, 256, 4, GEMM_ADD_F32>(g, s) : launch_gemm_t<GBM_, GBN_, 2, GEMM_ADD_F32>(g, s);
-    case GEMM_STORE_F16:
-        return big ? launch_gemm_t<256, 256, 4, GEMM_STORE_F16>(g, s) : launch_gemm_t<GBM_, GBN_, 2, GEMM_STORE_F16>(g, s);
-    case GEMM_SWIGLU_F16:
-        return big ? launch_gemm_t<256, 256, 4, GEMM_SWIGLU_F16>(g, s) : launch_gemm_t<GBM_, GBN_, 2, GEMM_SWIGLU_F16>(g, s);
+    case GEMM_STORE_F32: DF_GEMM_BY_SHAPE(GEMM_STORE_F32)
+    case GEMM_ADD_F32: DF_GEMM_BY_SHAPE(GEMM_ADD_F32)
+    case GEMM_STORE_F16: DF_GEMM_BY_SHAPE(GEMM_STORE_F16)
+    case GEMM_SWIGLU_F16: DF_GEMM_BY_SHAPE(GEMM_SWIGLU_F16)
     }
+#undef DF_GEMM_BY_SHAPE
     return hipErrorInvalidValue;
 }
 
