@@ -119,6 +119,59 @@ constexpr int GBM_ = 128, GBN_ = 128;
 template <int BM, int BN>
 constexpr size_t gemm_lds_bytes() { return size_t(2) * (BM + BN) * GPAD * sizeof(_Float16); }
 
+// Tile (tm, tn) of block b. XCD-aware order: blocks b, b+8, b+16, ... run on
+// one XCD; give them the same n tile (weights) so its rows are reused from
+// that XCD's L2.
+__device__ inline void gemm_tile_of(int b, int ntm, int ntn, int& tm, int& tn)
+{
+    if (ntn % 8 == 0) {
+        const int x = b & 7, y = b >> 3;
+        tn = (y / ntm) * 8 + x;
+        tm = y % ntm;
+    } else {
+        tn = b / ntm;
+        tm = b % ntm;
+    }
+}
+
+// Epilogue of a wave's (MI*32) x (NI*32) accumulator tile at rows m0 + wm*WTM,
+// columns n0 + wn*WTN (for SwiGLU: output columns of the gate/up block pairs).
+template <int MODE, int MI, int NI, int WTM, int WTN>
+__device__ inline void gemm_epilogue(const GemmArgs& g, const f32x16 (&acc)[MI][NI], int m0, int n0,
+                                     int wm, int wn, int l)
+{
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int r = m0 + wm * WTM + mi * 32 + (i >> 2) * 8 + (l >> 5) * 4 + (i & 3);
+            if (r >= g.M) continue;
+            if constexpr (MODE == GEMM_SWIGLU_F16) {
+#pragma unroll
+                for (int ni = 0; ni < NI; ni += 2) {
+                    const int f = n0 + ((wn * WTN) / 64 + ni / 2) * 32 + (l & 31);
+                    if (f < g.N) {
+                        const float gt = acc[mi][ni][i];
+                        const float up = acc[mi][ni + 1][i];
+                        static_cast<uint16_t*>(g.C)[int64_t(r) * g.ldc + f] = f2h(gate_act(gt, g.act) * up);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int ni = 0; ni < NI; ++ni) {
+                    const int c = n0 + wn * WTN + ni * 32 + (l & 31);
+                    if (c >= g.N) continue;
+                    const int64_t o = int64_t(r) * g.ldc + c;
+                    if constexpr (MODE == GEMM_STORE_F32) static_cast<float*>(g.C)[o] = acc[mi][ni][i];
+                    else if constexpr (MODE == GEMM_ADD_F32) static_cast<float*>(g.C)[o] += acc[mi][ni][i];
+                    else static_cast<uint16_t*>(g.C)[o] = f2h(acc[mi][ni][i]);
+                }
+            }
+        }
+    }
+}
+
+
 template <int BM, int BN, int WN, int MODE, bool WQ8>
 __global__ void __launch_bounds__(128 * WN)
 gemm_kernel(GemmArgs g)
@@ -137,18 +190,8 @@ gemm_kernel(GemmArgs g)
     constexpr int ncols = (MODE == GEMM_SWIGLU_F16) ? BN / 2 : BN;  // outputs per tile
     const int ntn = (g.N + ncols - 1) / ncols;
     const int ntm = (g.M + BM - 1) / BM;
-    // XCD-aware order: blocks b, b+8, b+16, ... run on one XCD; give them the
-    // same n tile (weights) so its rows are reused from that XCD's L2.
-    const int b = blockIdx.x;
     int tn, tm;
-    if (ntn % 8 == 0) {
-        const int x = b & 7, y = b >> 3;
-        tn = (y / ntm) * 8 + x;
-        tm = y % ntm;
-    } else {
-        tn = b / ntm;
-        tm = b % ntm;
-    }
+    gemm_tile_of(blockIdx.x, ntm, ntn, tm, tn);
     const int m0 = tm * BM;
     const int n0 = tn * ncols;
 
@@ -310,36 +353,153 @@ gemm_kernel(GemmArgs g)
     }
     if (st < nst) compute(S0{});  // odd number of stages: the last one
 
-    // Epilogue.
+    gemm_epilogue<MODE, MI, NI, WTM, WTN>(g, acc, m0, n0, wm, wn, l);
+}
+
+
+// ---------------------------------------------------------------------------
+// The same GEMM for f16 weights with the operand tiles loaded straight into
+// LDS (global_load_lds_dwordx4: lane i of a wave writes 16 bytes at LDS base
+// + 16 i), no register staging. A stage holds A rows [BM][64] and B rows
+// [BN][64] unpadded; the 16-byte chunk at position p of row r is K chunk
+// p ^ (r & 7), so a load instruction fills 8 whole rows and the fragment
+// reads (32 rows of one chunk column per half-wave) fall in distinct banks.
+// NB stage buffers (3 where they fit in LDS, else 2): the loads of stage
+// s + NB - 1 are issued right after the barrier that opens stage s, and a
+// wave waits only for the loads of the stage it is about to read.
+// ---------------------------------------------------------------------------
+constexpr int GDK = 64;  // K depth of a stage
+
+template <int BM, int BN>
+constexpr int gemm_dma_stages() { return size_t(3) * (BM + BN) * GDK * 2 <= 160 * 1024 ? 3 : 2; }
+template <int BM, int BN>
+constexpr size_t gemm_dma_lds_bytes() { return size_t(gemm_dma_stages<BM, BN>()) * (BM + BN) * GDK * 2; }
+
+// s_waitcnt with vmcnt = N (N < 64) and the other counters left alone.
+template <int N>
+__device__ inline void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int BM, int BN, int WN, int MODE>
+__global__ void __launch_bounds__(128 * WN)
+gemm_dma_kernel(GemmArgs g)
+{
+    constexpr int NW = 2 * WN;                 // waves: 2 x WN grid
+    constexpr int WTM = BM / 2, WTN = BN / WN;
+    constexpr int MI = WTM / 32, NI = WTN / 32;
+    constexpr int NB = gemm_dma_stages<BM, BN>();
+    constexpr int IA = BM / (8 * NW), IB = BN / (8 * NW);  // 8-row load instructions per wave per stage
+    static_assert(IA * 8 * NW == BM && IB * 8 * NW == BN, "tile rows split over the waves");
+    constexpr int SA = BM * GDK, SB = BN * GDK;  // halves per stage
+    extern __shared__ _Float16 gsm[];
+    const int tid = threadIdx.x;
+    const int l = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    constexpr int ncols = (MODE == GEMM_SWIGLU_F16) ? BN / 2 : BN;  // outputs per tile
+    const int ntn = (g.N + ncols - 1) / ncols;
+    const int ntm = (g.M + BM - 1) / BM;
+    int tn, tm;
+    gemm_tile_of(blockIdx.x, ntm, ntn, tm, tn);
+    const int m0 = tm * BM;
+    const int n0 = tn * ncols;
+
+    // This lane's source rows: load instruction q of the wave fills rows
+    // (wave*I + q)*8 .. +7; lane l takes row + l/8, position l%8, which holds
+    // K chunk (l%8) ^ (l/8) (the row's low three bits are l/8).
+    const int kc = ((l & 7) ^ (l >> 3)) * 8;  // K offset of this lane's chunk in a stage
+    const uint16_t* asrc[IA];
+    const uint16_t* bsrc[IB];
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int r = m0 + wm * WTM + mi * 32 + (i >> 2) * 8 + (l >> 5) * 4 + (i & 3);
-            if (r >= g.M) continue;
-            if constexpr (MODE == GEMM_SWIGLU_F16) {
-#pragma unroll
-                for (int ni = 0; ni < NI; ni += 2) {
-                    const int f = n0 + ((wn * WTN) / 64 + ni / 2) * 32 + (l & 31);
-                    if (f < g.N) {
-                        const float gt = acc[mi][ni][i];
-                        const float up = acc[mi][ni + 1][i];
-                        static_cast<uint16_t*>(g.C)[int64_t(r) * g.ldc + f] = f2h(gate_act(gt, g.act) * up);
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int ni = 0; ni < NI; ++ni) {
-                    const int c = n0 + wn * WTN + ni * 32 + (l & 31);
-                    if (c >= g.N) continue;
-                    const int64_t o = int64_t(r) * g.ldc + c;
-                    if constexpr (MODE == GEMM_STORE_F32) static_cast<float*>(g.C)[o] = acc[mi][ni][i];
-                    else if constexpr (MODE == GEMM_ADD_F32) static_cast<float*>(g.C)[o] += acc[mi][ni][i];
-                    else static_cast<uint16_t*>(g.C)[o] = f2h(acc[mi][ni][i]);
-                }
-            }
-        }
+    for (int q = 0; q < IA; ++q) {
+        const int am = m0 + (wave * IA + q) * 8 + (l >> 3);
+        asrc[q] = am < g.M ? g.A + int64_t(am) * g.lda + kc : nullptr;
     }
+#pragma unroll
+    for (int q = 0; q < IB; ++q) {
+        const int row = (wave * IB + q) * 8 + (l >> 3);
+        int bn;
+        bool ok;
+        if constexpr (MODE == GEMM_SWIGLU_F16) {
+            const int cb = row >> 5, within = row & 31;
+            const int f = n0 + (cb >> 1) * 32 + within;
+            ok = f < g.N;
+            bn = f + ((cb & 1) ? int(g.up_rows) : 0);
+        } else {
+            bn = n0 + row;
+            ok = bn < g.N;
+        }
+        bsrc[q] = ok ? g.B + int64_t(bn) * g.ldb + kc : nullptr;
+    }
+    const int nst = (g.K + GDK - 1) / GDK;
+    // Loads of stage st into buffer buf; rows or K chunks past the end read
+    // 16 zero bytes.
+    auto issue = [&](int st, int buf) {
+        const int k0 = st * GDK;
+        const bool kin = k0 + kc < g.K;
+        _Float16* a_lds = gsm + buf * (SA + SB);
+        _Float16* b_lds = a_lds + SA;
+#pragma unroll
+        for (int q = 0; q < IA; ++q) {
+            const void* src = (asrc[q] && kin) ? static_cast<const void*>(asrc[q] + k0) : g.zeros;
+            __builtin_amdgcn_global_load_lds(src, a_lds + (wave * IA + q) * 8 * GDK, 16, 0, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < IB; ++q) {
+            const void* src = (bsrc[q] && kin) ? static_cast<const void*>(bsrc[q] + k0) : g.zeros;
+            __builtin_amdgcn_global_load_lds(src, b_lds + (wave * IB + q) * 8 * GDK, 16, 0, 0);
+        }
+    };
+
+    f32x16 acc[MI][NI];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.f;
+
+    // Fragment rows: A rows wm*WTM + mi*32 + l%32, B rows wn*WTN + ni*32 +
+    // l%32; K chunk kk*2 + l/32 sits at position chunk ^ (row & 7), and
+    // row & 7 == l & 7 for every fragment row.
+    auto compute = [&](int buf) {
+        const _Float16* a_lds = gsm + buf * (SA + SB);
+        const _Float16* b_lds = a_lds + SA;
+#pragma unroll
+        for (int kk = 0; kk < GDK / 16; ++kk) {
+            const int pos = ((kk * 2 + (l >> 5)) ^ (l & 7)) * 8;
+            half8 af[MI], bf[NI];
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi)
+                af[mi] = *reinterpret_cast<const half8*>(a_lds + (wm * WTM + mi * 32 + (l & 31)) * GDK + pos);
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni)
+                bf[ni] = *reinterpret_cast<const half8*>(b_lds + (wn * WTN + ni * 32 + (l & 31)) * GDK + pos);
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < NI; ++ni)
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
+        }
+    };
+
+    // Prologue: stages 0 .. NB-2 in flight.
+#pragma unroll
+    for (int i = 0; i < NB - 1; ++i)
+        if (i < nst) issue(i, i);
+    for (int st = 0; st < nst; ++st) {
+        // Wait for this wave's loads of stage st; those of the (at most
+        // NB-2) later stages already issued may stay in flight.
+        if (NB == 3 && st + 1 < nst) wait_vmcnt<(NB == 3 ? IA + IB : 0)>();
+        else wait_vmcnt<0>();
+        __syncthreads();  // every wave's loads of stage st landed; stage st-1's buffer is free
+        if (st + NB - 1 < nst) issue(st + NB - 1, (st + NB - 1) % NB);
+        compute(st % NB);
+    }
+    gemm_epilogue<MODE, MI, NI, WTM, WTN>(g, acc, m0, n0, wm, wn, l);
 }
 
 template <int BM, int BN, int WN, int MODE, bool WQ8>
@@ -360,9 +520,32 @@ hipError_t launch_gemm_q(const GemmArgs& g, hipStream_t s)
 }
 
 template <int BM, int BN, int WN, int MODE>
+hipError_t launch_gemm_dma(const GemmArgs& g, hipStream_t s)
+{
+    constexpr size_t lds = gemm_dma_lds_bytes<BM, BN>();
+    static std::atomic<bool> attr_set{false};  // sessions may launch from several threads
+    if (!attr_set.load(std::memory_order_acquire)) {
+        const hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_dma_kernel<BM, BN, WN, MODE>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+        if (r != hipSuccess) return r;
+        attr_set.store(true, std::memory_order_release);
+    }
+    constexpr int ncols = (MODE == GEMM_SWIGLU_F16) ? BN / 2 : BN;
+    const int blocks = ((g.N + ncols - 1) / ncols) * ((g.M + BM - 1) / BM);
+    DFK_LAUNCH((gemm_dma_kernel<BM, BN, WN, MODE>), dim3(blocks), dim3(128 * WN), lds, s, g);
+    return hipGetLastError();
+}
+
+// f16 weights on 256-row tiles: operand tiles loaded straight into LDS
+// (measured 3% faster there, slower on the smaller tiles); otherwise, and
+// for 8-bit blocks (dequantised on the way into LDS), the register-staged
+// kernel.
+template <int BM, int BN, int WN, int MODE>
 hipError_t launch_gemm_t(const GemmArgs& g, hipStream_t s)
 {
-    return g.Bsc ? launch_gemm_q<BM, BN, WN, MODE, true>(g, s) : launch_gemm_q<BM, BN, WN, MODE, false>(g, s);
+    if (g.Bsc) return launch_gemm_q<BM, BN, WN, MODE, true>(g, s);
+    if constexpr (BM == 256) return launch_gemm_dma<BM, BN, WN, MODE>(g, s);
+    else return launch_gemm_q<BM, BN, WN, MODE, false>(g, s);
 }
 
 // ---------------------------------------------------------------------------
