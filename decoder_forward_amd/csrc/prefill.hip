@@ -536,6 +536,7 @@ hipError_t launch_gemm_dma(const GemmArgs& g, hipStream_t s)
     return hipGetLastError();
 }
 
+
 // f16 weights on 256-row tiles: operand tiles loaded straight into LDS
 // (measured 3% faster there, slower on the smaller tiles); otherwise, and
 // for 8-bit blocks (dequantised on the way into LDS), the register-staged
