@@ -720,27 +720,40 @@ attn_prefill_kernel(AttnPrefillArgs a)
     // 2 (e % (TK/2)) and +1, 4 dims at 4 (e / (TK/2))); rows past n_keys and
     // padded depth read as zero.
     float4 kr[PREF ? KPT : 1], vr0[PREF ? VPT : 1], vr1[PREF ? VPT : 1];
-    auto load_tile = [&](int kt) {
-        const int t0 = kt * TK;
+    // Per-thread tile offsets (row within the tile, element offset from the
+    // head's row 0), fixed across tiles.
+    int krow[PREF ? KPT : 1], vrow[PREF ? VPT : 1];
+    const float* kbase[PREF ? KPT : 1];
+    const float* vbase[PREF ? VPT : 1];
+    if constexpr (PREF) {
 #pragma unroll
         for (int u = 0; u < KPT; ++u) {
             const int e = tid + u * NT;
             const int r = e / (KQ / 4), c = (e % (KQ / 4)) * 4;
-            kr[u] = (e < KE && t0 + r < n_keys && c < HD)
-                        ? *reinterpret_cast<const float4*>(a.kc + head_base + int64_t(t0 + r) * HD + c)
-                        : make_float4(0.f, 0.f, 0.f, 0.f);
+            krow[u] = (e < KE && c < HD) ? r : 1 << 30;  // never inside n_keys: reads zero
+            kbase[u] = a.kc + head_base + int64_t(r) * HD + c;
         }
 #pragma unroll
         for (int u = 0; u < VPT; ++u) {
             const int e = tid + u * NT;
             const int r = (e % (TK / 2)) * 2, c = (e / (TK / 2)) * 4;
-            const bool ok = e < VE;
-            vr0[u] = ok && t0 + r < n_keys
-                         ? *reinterpret_cast<const float4*>(a.vc + head_base + int64_t(t0 + r) * HD + c)
-                         : make_float4(0.f, 0.f, 0.f, 0.f);
-            vr1[u] = ok && t0 + r + 1 < n_keys
-                         ? *reinterpret_cast<const float4*>(a.vc + head_base + int64_t(t0 + r + 1) * HD + c)
-                         : make_float4(0.f, 0.f, 0.f, 0.f);
+            vrow[u] = e < VE ? r : 1 << 30;
+            vbase[u] = a.vc + head_base + int64_t(r) * HD + c;
+        }
+    }
+    auto load_tile = [&](int kt) {
+        const int t0 = kt * TK;
+        const int64_t off = int64_t(t0) * HD;
+#pragma unroll
+        for (int u = 0; u < KPT; ++u)
+            kr[u] = t0 + krow[u] < n_keys ? *reinterpret_cast<const float4*>(kbase[u] + off)
+                                           : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) {
+            vr0[u] = t0 + vrow[u] < n_keys ? *reinterpret_cast<const float4*>(vbase[u] + off)
+                                            : make_float4(0.f, 0.f, 0.f, 0.f);
+            vr1[u] = t0 + vrow[u] + 1 < n_keys ? *reinterpret_cast<const float4*>(vbase[u] + off + HD)
+                                                : make_float4(0.f, 0.f, 0.f, 0.f);
         }
     };
     // K row-major f16 (4 halves per 8-byte store, consecutive threads on
@@ -857,17 +870,20 @@ attn_prefill_kernel(AttnPrefillArgs a)
             }
         }
         // P = 2^(s - m) in registers, as the A operand of P V (key slots
-        // lg*8 + i: keys lg*4 + i, then 16 + lg*4 + i).
+        // lg*8 + i: keys lg*4 + i, then 16 + lg*4 + i). A masked score is
+        // -inf and gives 0; the maximum is clamped to a finite value so that
+        // a row with no key yet (maximum still -inf, all its scores masked)
+        // also gives 0 instead of 2^NaN.
         half8 pa[RT];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
+            const float mref = fmaxf(mq[rt], -1e30f);
             float ps = 0.f;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float x = st[rt][kb][i];
-                    const float pv = (x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x - mq[rt]);
+                    const float pv = __builtin_amdgcn_exp2f(st[rt][kb][i] - mref);
                     ps += pv;
                     pa[rt][kb * 4 + i] = static_cast<_Float16>(pv);
                 }
