@@ -555,53 +555,76 @@ hipError_t launch_gemm_t(const GemmArgs& g, hipStream_t s)
 // the attention's operand, scores in base 2) and k (after RoPE), v (+ bias)
 // -> the f32 KV cache at slot p0 + s.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(64)
+__global__ void __launch_bounds__(256)
 qk_post_rows_kernel(QkPostArgs a)
 {
-    extern __shared__ float v[];  // head_dim floats
+    // One block per row; wave w takes heads w, w + 4, ... (query heads, then
+    // KV heads). Lane l holds rope pairs l and l + 64 (those below hd/2).
     const int s = blockIdx.x;
-    const int h = blockIdx.y;     // < n_heads: query head; else KV head h - n_heads
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int w = threadIdx.x >> 6;
     const int HD = a.head_dim, half = HD / 2;
     const int qd = a.n_heads * HD, kvd = a.n_kv * HD;
     const int pos = a.p0 + s;
-    const bool is_q = h < a.n_heads;
-    const int g = h - a.n_heads;
-    const int off = is_q ? h * HD : qd + g * HD;
-    const float* src = a.qkv + int64_t(s) * (qd + 2 * kvd) + off;
-    for (int i = lane; i < HD; i += WAVE) v[i] = a.bias ? src[i] + a.bias[off + i] : src[i];
-    __syncthreads();
-    const float* nw = is_q ? a.q_norm : a.k_norm;
-    if (nw) {
-        float ss = 0.f;
-        for (int i = lane; i < HD; i += WAVE) ss = fmaf(v[i], v[i], ss);
-        ss = wave_sum(ss);
-        const float r = 1.0f / sqrtf(ss / static_cast<float>(HD) + a.eps);
-        for (int i = lane; i < HD; i += WAVE) v[i] = nw[i] * (v[i] * r);
-        __syncthreads();
-    }
+    const float* row = a.qkv + int64_t(s) * (qd + 2 * kvd);
     const float* cs = a.cos_t + int64_t(pos) * half;
     const float* sn = a.sin_t + int64_t(pos) * half;
-    for (int i = lane; i < half; i += WAVE) {
-        const int i0 = a.adjacent ? 2 * i : i, i1 = a.adjacent ? 2 * i + 1 : i + half;
-        const float x0 = v[i0], x1 = v[i1];
-        v[i0] = fmaf(x0, cs[i], -x1 * sn[i]);
-        v[i1] = fmaf(x0, sn[i], x1 * cs[i]);
-    }
-    __syncthreads();
-    if (is_q) {
-        // q for the attention's A operand: times log2(e) / sqrt(hd) (the
-        // attention takes its softmax in base 2), then rounded to f16 once
-        uint16_t* q = a.q16 + (int64_t(s) * a.n_heads + h) * HD;
-        const float qs = 1.4426950408889634f / sqrtf(static_cast<float>(HD));
-        for (int i = lane; i < HD; i += WAVE) q[i] = f2h(v[i] * qs);
-    } else {
-        const int64_t slot = (int64_t(g) * a.max_ctx + pos) * HD;
-        const int voff = qd + kvd + g * HD;
-        const float* vs = a.qkv + int64_t(s) * (qd + 2 * kvd) + voff;
-        for (int i = lane; i < HD; i += WAVE) {
-            a.kc[slot + i] = v[i];
-            a.vc[slot + i] = a.bias ? vs[i] + a.bias[voff + i] : vs[i];
+    // q for the attention's operand: times log2(e) / sqrt(hd) (the attention
+    // takes its softmax in base 2), then rounded to f16 once
+    const float qs = 1.4426950408889634f / sqrtf(static_cast<float>(HD));
+    for (int h = w; h < a.n_heads + a.n_kv; h += 4) {
+        const bool is_q = h < a.n_heads;
+        const int g = h - a.n_heads;
+        const int off = is_q ? h * HD : qd + g * HD;
+        float x0[2], x1[2];
+        int i0[2], i1[2];
+        float ss = 0.f;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int i = lane + r * WAVE;
+            i0[r] = a.adjacent ? 2 * i : i;
+            i1[r] = a.adjacent ? 2 * i + 1 : i + half;
+            x0[r] = 0.f;
+            x1[r] = 0.f;
+            if (i < half) {
+                x0[r] = row[off + i0[r]];
+                x1[r] = row[off + i1[r]];
+                if (a.bias) {
+                    x0[r] += a.bias[off + i0[r]];
+                    x1[r] += a.bias[off + i1[r]];
+                }
+                ss = fmaf(x0[r], x0[r], fmaf(x1[r], x1[r], ss));
+            }
+        }
+        const float* nw = is_q ? a.q_norm : a.k_norm;
+        float rn = 1.f;
+        if (nw) rn = 1.0f / sqrtf(wave_sum(ss) / static_cast<float>(HD) + a.eps);
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int i = lane + r * WAVE;
+            if (i >= half) continue;
+            float v0 = x0[r], v1 = x1[r];
+            if (nw) {
+                v0 = nw[i0[r]] * (v0 * rn);
+                v1 = nw[i1[r]] * (v1 * rn);
+            }
+            const float c = cs[i], sv = sn[i];
+            const float y0 = fmaf(v0, c, -v1 * sv);
+            const float y1 = fmaf(v0, sv, v1 * c);
+            if (is_q) {
+                uint16_t* q = a.q16 + (int64_t(s) * a.n_heads + h) * HD;
+                q[i0[r]] = f2h(y0 * qs);
+                q[i1[r]] = f2h(y1 * qs);
+            } else {
+                float* k = a.kc + (int64_t(g) * a.max_ctx + pos) * HD;
+                k[i0[r]] = y0;
+                k[i1[r]] = y1;
+            }
+        }
+        if (!is_q) {
+            const int voff = qd + kvd + g * HD;
+            float* v = a.vc + (int64_t(g) * a.max_ctx + pos) * HD;
+            for (int i = lane; i < HD; i += WAVE) v[i] = a.bias ? row[voff + i] + a.bias[voff + i] : row[voff + i];
         }
     }
 }
@@ -982,8 +1005,8 @@ hipError_t launch_gemm(const GemmArgs& g, int mode, hipStream_t s)
 hipError_t launch_qk_post_rows(const QkPostArgs& a, hipStream_t s)
 {
     if (a.S <= 0) return hipSuccess;
-    DFK_LAUNCH(qk_post_rows_kernel, dim3(a.S, a.n_heads + a.n_kv), dim3(64),
-                       size_t(a.head_dim) * sizeof(float), s, a);
+    if (a.head_dim > 4 * WAVE) return hipErrorInvalidValue;  // two rope pairs per lane at most
+    DFK_LAUNCH(qk_post_rows_kernel, dim3(a.S), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
