@@ -10,8 +10,11 @@
 //
 // Work layout. A block of NW waves walks its rows in sweeps of NW*4*ITER
 // rows: wave w takes rows w*4*ITER .. w*4*ITER + 4*ITER - 1 of a sweep, 16
-// lanes per row (4 rows per wave instruction, hd/16 dims per lane), so a K or
-// V row is one contiguous 16-lane load. Each wave keeps its own online
+// lanes per row (4 rows per wave instruction, hd/16 dims per lane). For
+// hd >= 64 a lane's dims are float4 groups 64 floats apart (lane l of the
+// row holds dims 64c + 4l .. 64c + 4l + 3 for c = 0 .. hd/64 - 1), so each
+// 16-byte load instruction covers whole contiguous 256-byte runs of a row:
+// no cache line is requested by two instructions. Each wave keeps its own online
 // softmax (running max m, running sum l, accumulator) across sweeps: no
 // block-wide synchronisation inside the row loop. With DBUF the next sweep's
 // rows are loaded while the current one is consumed (twice the registers).
@@ -57,18 +60,28 @@ constexpr int attn_core_lds_floats()
     return G * HD + 2 * HD + NW * G * HD + 2 * NW * G;
 }
 
+// Offset within a row of a lane's d-th dim; l16 is the lane's index within
+// its 16-lane row group (see the work layout above).
+template <int DPL>
+__device__ inline int attn_dim(int l16, int d)
+{
+    if constexpr (DPL % 4 == 0) return (d >> 2) * 64 + l16 * 4 + (d & 3);
+    else return l16 * DPL + d;
+}
+
+// The lane's DPL dims of the row at p (in attn_dim order).
 template <int N>
-__device__ inline void load_row_slice(const float* p, float (&v)[N])
+__device__ inline void load_row_slice(const float* p, int l16, float (&v)[N])
 {
     if constexpr (N % 4 == 0) {
 #pragma unroll
         for (int i = 0; i < N; i += 4) {
-            const float4 x = load16f_nt(p + i);
+            const float4 x = load16f_nt(p + attn_dim<N>(l16, i));
             v[i] = x.x; v[i + 1] = x.y; v[i + 2] = x.z; v[i + 3] = x.w;
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < N; ++i) v[i] = *gmem(p + i);
+        for (int i = 0; i < N; ++i) v[i] = *gmem(p + attn_dim<N>(l16, i));
     }
 }
 
@@ -89,7 +102,7 @@ __device__ void attn_core(const AttnItem& a, float* lds, int tid)
     const int lane = tid & (WAVE - 1);
     const int w = tid >> 6;
     const int rg = lane >> 4;
-    const int ds = (lane & (LPR - 1)) * DPL;
+    const int l16 = lane & (LPR - 1);
     const int p = a.p;
     const bool owner = a.pos1 == p + 1;
     const int n_sweeps = (a.pos1 - a.pos0 + SW - 1) / SW;
@@ -103,8 +116,8 @@ __device__ void attn_core(const AttnItem& a, float* lds, int tid)
         for (int it = 0; it < ITER; ++it) {
             const int t = row_of(s, it);
             if (t < lim) {
-                load_row_slice<DPL>(a.kc + int64_t(t) * HD + ds, kk[it]);
-                load_row_slice<DPL>(a.vc + int64_t(t) * HD + ds, vv[it]);
+                load_row_slice<DPL>(a.kc + int64_t(t) * HD, l16, kk[it]);
+                load_row_slice<DPL>(a.vc + int64_t(t) * HD, l16, vv[it]);
             } else {
 #pragma unroll
                 for (int d = 0; d < DPL; ++d) { kk[it][d] = 0.f; vv[it][d] = 0.f; }
@@ -190,7 +203,7 @@ __device__ void attn_core(const AttnItem& a, float* lds, int tid)
     for (int j = 0; j < G; ++j) {
 #pragma unroll
         for (int d = 0; d < DPL; ++d) {
-            q[j][d] = qs[j * HD + ds + d] * qscale;
+            q[j][d] = qs[j * HD + attn_dim<DPL>(l16, d)] * qscale;
             acc[j][d] = 0.f;
         }
         m[j] = -INFINITY;
@@ -202,7 +215,10 @@ __device__ void attn_core(const AttnItem& a, float* lds, int tid)
         for (int it = 0; it < ITER; ++it) {
             if (row_of(s, it) == p) {
 #pragma unroll
-                for (int d = 0; d < DPL; ++d) { kk[it][d] = knew[ds + d]; vv[it][d] = vnew[ds + d]; }
+                for (int d = 0; d < DPL; ++d) {
+                    kk[it][d] = knew[attn_dim<DPL>(l16, d)];
+                    vv[it][d] = vnew[attn_dim<DPL>(l16, d)];
+                }
             }
         }
 #pragma unroll
@@ -264,7 +280,7 @@ __device__ void attn_core(const AttnItem& a, float* lds, int tid)
                          (lane_value(l[j], 32) + lane_value(l[j], 48));
         if (lane < LPR) {
 #pragma unroll
-            for (int d = 0; d < DPL; ++d) red[(w * G + j) * HD + ds + d] = acc[j][d];
+            for (int d = 0; d < DPL; ++d) red[(w * G + j) * HD + attn_dim<DPL>(l16, d)] = acc[j][d];
         }
         if (lane == 0) {
             sm[w * G + j] = m[j];
