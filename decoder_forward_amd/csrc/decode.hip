@@ -29,7 +29,7 @@ matvec_kernel(const void* __restrict__ W, const uint16_t* __restrict__ scales, M
     extern __shared__ float hs[];
     __shared__ float red[16];
     MvState<WT, MODE> st;
-    mv_begin<WT, MODE>(W, L, blockIdx.x, st, threadIdx.x);
+    mv_begin<WT, MODE>(W, scales, L, blockIdx.x, st, threadIdx.x);
     mv_finish<WT, MODE, NORM, false>(scales, W, L, st, x, norm_w, eps, out, hs, red, threadIdx.x);
 }
 

@@ -184,7 +184,7 @@ decode_step_kernel(const StepArgs* __restrict__ Ap, float* logits_out, int advan
             const DFK_CONST StepLayer& Ly = layer_of(A, l);
             const int t = opaque(tid);
             MvState<WT, MV_STORE, MV_DEPTH> st;
-            mv_begin<WT, MV_STORE>(Ly.wqkv, mv_layout(A.mv_qkv), b, st, t);
+            mv_begin<WT, MV_STORE>(Ly.wqkv, Ly.sqkv, mv_layout(A.mv_qkv), b, st, t);
             sync();
             mv_finish<WT, MV_STORE, true, true, MV_DEPTH, false>(Ly.sqkv, Ly.wqkv, mv_layout(A.mv_qkv), st, A.x,
                                                 Ly.attn_norm, A.eps, A.qkv, lds, red, t);
@@ -226,7 +226,7 @@ decode_step_kernel(const StepArgs* __restrict__ Ap, float* logits_out, int advan
             const DFK_CONST StepLayer& Ly = layer_of(A, l);
             const int t = opaque(tid);
             MvState<WT, MV_RESID, MV_DEPTH> st;
-            mv_begin<WT, MV_RESID>(Ly.wo, mv_layout(A.mv_o), b, st, t);
+            mv_begin<WT, MV_RESID>(Ly.wo, Ly.so, mv_layout(A.mv_o), b, st, t);
             sync();
             mv_finish<WT, MV_RESID, false, true, MV_DEPTH, false>(Ly.so, Ly.wo, mv_layout(A.mv_o), st, A.att, nullptr,
                                                  A.eps, A.x, lds, red, t);
@@ -237,7 +237,7 @@ decode_step_kernel(const StepArgs* __restrict__ Ap, float* logits_out, int advan
             const DFK_CONST StepLayer& Ly = layer_of(A, l);
             const int t = opaque(tid);
             MvState<WT, MV_SWIGLU, MV_DEPTH> st;
-            mv_begin<WT, MV_SWIGLU>(Ly.wgu, mv_layout(A.mv_gu), b, st, t);
+            mv_begin<WT, MV_SWIGLU>(Ly.wgu, Ly.sgu, mv_layout(A.mv_gu), b, st, t);
             sync();
             mv_finish<WT, MV_SWIGLU, true, true, MV_DEPTH, false>(Ly.sgu, Ly.wgu, mv_layout(A.mv_gu), st, A.x,
                                                  Ly.ffn_norm, A.eps, A.mid, lds, red, t);
@@ -248,7 +248,7 @@ decode_step_kernel(const StepArgs* __restrict__ Ap, float* logits_out, int advan
             const DFK_CONST StepLayer& Ly = layer_of(A, l);
             const int t = opaque(tid);
             MvState<WT, MV_RESID, MV_DEPTH> st;
-            mv_begin<WT, MV_RESID>(Ly.wd, mv_layout(A.mv_down), b, st, t);
+            mv_begin<WT, MV_RESID>(Ly.wd, Ly.sd, mv_layout(A.mv_down), b, st, t);
             sync();
             mv_finish<WT, MV_RESID, false, true, MV_DEPTH, false>(Ly.sd, Ly.wd, mv_layout(A.mv_down), st, A.mid,
                                                  nullptr, A.eps, A.x, lds, red, t);
@@ -262,7 +262,7 @@ decode_step_kernel(const StepArgs* __restrict__ Ap, float* logits_out, int advan
             const DFK_CONST StepArgs& A = *fresh(Ap);
             const int t = opaque(tid);
             MvState<WO, MV_STORE, MV_DEPTH> st;
-            mv_begin<WO, MV_STORE>(A.wout, mv_layout(A.mv_logits), b, st, t);
+            mv_begin<WO, MV_STORE>(A.wout, A.sout, mv_layout(A.mv_logits), b, st, t);
             sync();
             mv_finish<WO, MV_STORE, true, true, MV_DEPTH, false>(A.sout, A.wout, mv_layout(A.mv_logits), st, A.x,
                                                 A.out_norm, A.eps, logits_out, lds, red, t);

@@ -172,8 +172,7 @@ __device__ inline uint4 load_w(const void* base, int64_t elem)
 
 // dot of a lane's 16-byte weight vector with hs[k .. k + Epl).
 template <int WT>
-__device__ inline float lane_dot(uint4 w, const float* hs, int64_t k,
-                                 const uint16_t* srow)
+__device__ inline float lane_dot(uint4 w, const float* hs, int64_t k, uint16_t scale_bits)
 {
     if constexpr (WT == W_F32) {
         const float4 h = *reinterpret_cast<const float4*>(hs + k);
@@ -207,7 +206,7 @@ __device__ inline float lane_dot(uint4 w, const float* hs, int64_t k,
             a = fmaf(static_cast<float>(static_cast<int8_t>((v >> 16) & 0xff)), h.z, a);
             b = fmaf(static_cast<float>(static_cast<int8_t>(v >> 24)), h.w, b);
         }
-        return f16_bits_to_f32(*gmem(srow + (k >> 5))) * (a + b);
+        return f16_bits_to_f32(scale_bits) * (a + b);
     }
 }
 
@@ -234,6 +233,7 @@ __device__ inline float lane_dot(uint4 w, const float* hs, int64_t k,
 template <int WT, int NR, int U>
 struct ChunkBatch {
     uint4 w[U][NR];
+    uint16_t s[WT == W_Q8 ? U : 1][NR];  // 8-bit blocks: the chunk's block scale (f16 bits)
 };
 
 // Position in a block's stream of (unit, slice) items, chunk by chunk.
@@ -252,8 +252,8 @@ __device__ inline void advance(Cursor& c, int cps)
 }
 
 template <int WT, int NR, int U>
-__device__ inline void fetch(const void* W, const MvLayout L, int64_t unit0, Cursor& c,
-                             int item_end, int lane, ChunkBatch<WT, NR, U>& b)
+__device__ inline void fetch(const void* W, const uint16_t* scales, const MvLayout L, int64_t unit0,
+                             Cursor& c, int item_end, int lane, ChunkBatch<WT, NR, U>& b)
 {
     constexpr int E = Epl<WT>::v;
     constexpr int64_t CH = int64_t(WAVE) * E;
@@ -271,6 +271,9 @@ __device__ inline void fetch(const void* W, const MvLayout L, int64_t unit0, Cur
         for (int r = 0; r < NR; ++r) {
             const int64_t row = unit + (r == 1 ? L.up_rows : 0);
             b.w[u][r] = load_w<WT>(W, ok ? row * L.K + k : 0);
+            // the scale travels with its weights, so that no dependent load
+            // is left for the consuming step
+            if constexpr (WT == W_Q8) b.s[u][r] = *gmem(scales + (ok ? row * (L.K >> 5) + (k >> 5) : 0));
         }
         advance(c, L.cps);
     }
@@ -330,8 +333,8 @@ __device__ inline void act_st(float* p, float v)
 // tid is threadIdx.x, passed in so that a caller running several phases in
 // one kernel can keep each phase's per-lane values local to that phase.
 template <int WT, int MODE, int DEPTH>
-__device__ inline void mv_begin(const void* W, const MvLayout L, int block, MvState<WT, MODE, DEPTH>& st,
-                                int tid)
+__device__ inline void mv_begin(const void* W, const uint16_t* scales, const MvLayout L, int block,
+                                MvState<WT, MODE, DEPTH>& st, int tid)
 {
     const int lane = tid & (WAVE - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -344,15 +347,18 @@ __device__ inline void mv_begin(const void* W, const MvLayout L, int block, MvSt
     st.fc = Cursor{item_begin, 0};
     st.uc = Cursor{item_begin, 0};
     if (st.n_chunks > 0) {
-        fetch<WT, MvState<WT, MODE, DEPTH>::NR, MvState<WT, MODE, DEPTH>::U>(W, L, st.unit0, st.fc, st.item_end,
-                                                                            lane, st.cur);
+        fetch<WT, MvState<WT, MODE, DEPTH>::NR, MvState<WT, MODE, DEPTH>::U>(W, scales, L, st.unit0, st.fc,
+                                                                            st.item_end, lane, st.cur);
     } else {
         // Defined contents: an undefined batch lets the register allocator
         // merge it with live ranges of other phases.
 #pragma unroll
         for (int u = 0; u < MvState<WT, MODE, DEPTH>::U; ++u)
 #pragma unroll
-            for (int r = 0; r < MvState<WT, MODE, DEPTH>::NR; ++r) st.cur.w[u][r] = make_uint4(0u, 0u, 0u, 0u);
+            for (int r = 0; r < MvState<WT, MODE, DEPTH>::NR; ++r) {
+                st.cur.w[u][r] = make_uint4(0u, 0u, 0u, 0u);
+                if constexpr (WT == W_Q8) st.cur.s[u][r] = 0;
+            }
     }
 }
 
@@ -428,12 +434,7 @@ __device__ inline void mv_finish(const uint16_t* scales, const void* W, const Mv
                               int64_t(lane) * E;
             if (k < L.K) {
 #pragma unroll
-                for (int i = 0; i < NR; ++i) {
-                    const uint16_t* srow = nullptr;
-                    if constexpr (WT == W_Q8)
-                        srow = scales + (unit + (i == 1 ? L.up_rows : 0)) * (L.K >> 5);
-                    acc[i] += lane_dot<WT>(cb.w[u][i], hs, k, srow);
-                }
+                for (int i = 0; i < NR; ++i) acc[i] += lane_dot<WT>(cb.w[u][i], hs, k, cb.s[WT == W_Q8 ? u : 0][i]);
             }
             if (st.uc.within == L.cps - 1) {
 #pragma unroll
@@ -457,14 +458,17 @@ __device__ inline void mv_finish(const uint16_t* scales, const void* W, const Mv
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int r = 0; r < NR; ++r) nb.w[u][r] = make_uint4(0u, 0u, 0u, 0u);  // defined (see mv_begin)
+            for (int r = 0; r < NR; ++r) {  // defined (see mv_begin)
+                nb.w[u][r] = make_uint4(0u, 0u, 0u, 0u);
+                if constexpr (WT == W_Q8) nb.s[u][r] = 0;
+            }
         for (int q = 0; q < st.n_chunks;) {
             if (q + U >= st.n_chunks) { consume(st.cur); break; }
-            fetch<WT, NR, U>(W, L, st.unit0, st.fc, st.item_end, lane, nb);
+            fetch<WT, NR, U>(W, scales, L, st.unit0, st.fc, st.item_end, lane, nb);
             consume(st.cur);
             q += U;
             if (q + U >= st.n_chunks) { consume(nb); break; }
-            fetch<WT, NR, U>(W, L, st.unit0, st.fc, st.item_end, lane, st.cur);
+            fetch<WT, NR, U>(W, scales, L, st.unit0, st.fc, st.item_end, lane, st.cur);
             consume(nb);
             q += U;
         }
@@ -472,7 +476,7 @@ __device__ inline void mv_finish(const uint16_t* scales, const void* W, const Mv
         for (int q = 0; q < st.n_chunks; q += U) {
             ChunkBatch<WT, NR, U> nxt;
             const bool more = q + U < st.n_chunks;
-            if (more) fetch<WT, NR, U>(W, L, st.unit0, st.fc, st.item_end, lane, nxt);
+            if (more) fetch<WT, NR, U>(W, scales, L, st.unit0, st.fc, st.item_end, lane, nxt);
             consume(st.cur);
             if (more) st.cur = nxt;
         }
