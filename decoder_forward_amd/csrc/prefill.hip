@@ -635,12 +635,13 @@ qk_post_rows_kernel(QkPostArgs a)
 // K/V tile is staged once for every head and row of the block and each K / V
 // fragment read from LDS feeds PF_RT MFMAs.
 //
-// Per tile of 32 keys, on v_mfma_f32_16x16x32_f16:
+// Per tile of PF_TK keys, on v_mfma_f32_16x16x32_f16:
 //  * S^T = K Q^T (keys x queries; q arrives pre-scaled by log2(e)/sqrt(hd),
-//    so scores are in base 2): lane l holds 8 keys of query l%16, which is
-//    the layout P needs as the A operand of P V, so P never leaves the
-//    registers; the P V operand pairs keys in the order (l/16)*4 + i,
-//    16 + (l/16)*4 + i, and V is read from LDS in the same order.
+//    so scores are in base 2): per 32 keys lane l holds 8 keys of query
+//    l%16, which is the layout P needs as the A operand of P V, so P never
+//    leaves the registers; the P V operand pairs keys in the order
+//    (l/16)*4 + i, 16 + (l/16)*4 + i, and V is read from LDS in the same
+//    order.
 //  * Online softmax with a lazy maximum: each lane keeps the running
 //    maximum of its query and its own partial sum (the sum over the 4 lanes
 //    of a query is taken once, at the end); the maximum moves, with a
@@ -669,6 +670,9 @@ constexpr int attn_pf_wph() { return G <= 4 ? 2 : 1; }
 template <int HD, int G>
 constexpr int attn_pf_rows() { return 16 * attn_pf_rt<HD>() * attn_pf_wph<G>(); }
 
+// Keys per tile of the prefill attention (a multiple of 32).
+constexpr int PF_TK = 64;
+
 // Slack (base-2 units) by which a score may exceed the running maximum
 // before the maximum moves: weights stay below 2^8, well inside f16 for P.
 constexpr float RESCALE_SLACK = 8.0f;
@@ -678,7 +682,9 @@ __global__ void __launch_bounds__(64 * G * attn_pf_wph<G>())
 attn_prefill_kernel(AttnPrefillArgs a)
 {
     constexpr int KQ = HD < 32 ? 32 : HD;  // QK depth, zero padded to 32
-    constexpr int TK = 32;                  // keys per tile
+    constexpr int TK = PF_TK;               // keys per tile
+    constexpr int KB = TK / 16;             // 16-key blocks of a tile
+    constexpr int NP = TK / 32;             // 32-key halves: P V steps
     constexpr int DB = HD / 16;             // 16-wide output blocks
     constexpr int QB = attn_pf_rows<HD, G>();  // query rows per block
     constexpr int RT = attn_pf_rt<HD>();    // 16-row tiles per wave
@@ -834,24 +840,23 @@ attn_prefill_kernel(AttnPrefillArgs a)
         if constexpr (PREF) {
             if (kt + 1 < tiles) load_tile(kt + 1);  // in flight during this tile
         }
-        // K fragments as the A operand: A[key = kb*16 + l%16][d = kq*32 + (l/16)*8 + i].
-        half8 kf[2][KQ / 32];
+        // S^T[key = kb*16 + lg*4 + i][query = rt*16 + l%16], with the K
+        // fragments as the A operand: A[key = kb*16 + l%16][d = kq*32 + (l/16)*8 + i].
+        f32x4 st[RT][KB];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < KB; ++kb) {
+            half8 kf[KQ / 32];
 #pragma unroll
             for (int kq = 0; kq < KQ / 32; ++kq)
-                kf[kb][kq] = *reinterpret_cast<const half8*>(&Ks[kb * 16 + lq][kq * 32 + lg * 8]);
-        // S^T[key = kb*16 + lg*4 + i][query = rt*16 + l%16]
-        f32x4 st[RT][2];
+                kf[kq] = *reinterpret_cast<const half8*>(&Ks[kb * 16 + lq][kq * 32 + lg * 8]);
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+            for (int rt = 0; rt < RT; ++rt) {
                 st[rt][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kq = 0; kq < KQ / 32; ++kq)
-                    st[rt][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[kb][kq], qa[rt][kq], st[rt][kb], 0, 0, 0);
+                    st[rt][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[kq], qa[rt][kq], st[rt][kb], 0, 0, 0);
             }
+        }
         const bool masked = t0 > free_hi || t0 < free_lo;  // uniform
         bool grow = false;
         float vmax[RT];
@@ -861,15 +866,18 @@ attn_prefill_kernel(AttnPrefillArgs a)
                 const int qpos = a.p0 + s0 + r0 + rt * 16 + lq;
                 const int kmin = a.window > 0 ? qpos - a.window + 1 : 0;  // first key in the window
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
+                for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int key = t0 + kb * 16 + lg * 4 + i;
                         if (key > qpos || key < kmin) st[rt][kb][i] = -INFINITY;
                     }
             }
-            vmax[rt] = fmaxf(fmaxf(fmaxf(st[rt][0][0], st[rt][0][1]), fmaxf(st[rt][0][2], st[rt][0][3])),
-                             fmaxf(fmaxf(st[rt][1][0], st[rt][1][1]), fmaxf(st[rt][1][2], st[rt][1][3])));
+            float vm = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+                vm = fmaxf(vm, fmaxf(fmaxf(st[rt][kb][0], st[rt][kb][1]), fmaxf(st[rt][kb][2], st[rt][kb][3])));
+            vmax[rt] = vm;
             grow |= vmax[rt] > mq[rt] + RESCALE_SLACK;
         }
         if (__builtin_amdgcn_ballot_w64(grow) != 0) {
@@ -892,35 +900,39 @@ attn_prefill_kernel(AttnPrefillArgs a)
                 }
             }
         }
-        // P = 2^(s - m) in registers, as the A operand of P V (key slots
-        // lg*8 + i: keys lg*4 + i, then 16 + lg*4 + i). A masked score is
-        // -inf and gives 0; the maximum is clamped to a finite value so that
-        // a row with no key yet (maximum still -inf, all its scores masked)
-        // also gives 0 instead of 2^NaN.
-        half8 pa[RT];
+        // P = 2^(s - m) in registers, as the A operand of P V: step h takes
+        // keys 32h .. 32h + 31 in the slot order lg*8 + i: keys 32h + lg*4 + i,
+        // then 32h + 16 + lg*4 + i. A masked score is -inf and gives 0; the
+        // maximum is clamped to a finite value so that a row with no key yet
+        // (maximum still -inf, all its scores masked) also gives 0 instead of
+        // 2^NaN.
+        half8 pa[RT][NP];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             const float mref = fmaxf(mq[rt], -1e30f);
             float ps = 0.f;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float pv = __builtin_amdgcn_exp2f(st[rt][kb][i] - mref);
                     ps += pv;
-                    pa[rt][kb * 4 + i] = static_cast<_Float16>(pv);
+                    pa[rt][kb >> 1][(kb & 1) * 4 + i] = static_cast<_Float16>(pv);
                 }
             lsum[rt] += ps;
         }
         // V fragments in the same key order: B[slot][d = db*16 + l%16].
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            const uint2 v0 = *reinterpret_cast<const uint2*>(&Vt[db * 16 + lq][lg * 4]);
-            const uint2 v1 = *reinterpret_cast<const uint2*>(&Vt[db * 16 + lq][16 + lg * 4]);
-            const half8 vb = __builtin_bit_cast(half8, u32x4{v0.x, v0.y, v1.x, v1.y});
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-                o[rt][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[rt], vb, o[rt][db], 0, 0, 0);
+            for (int h = 0; h < NP; ++h) {
+                const uint2 v0 = *reinterpret_cast<const uint2*>(&Vt[db * 16 + lq][32 * h + lg * 4]);
+                const uint2 v1 = *reinterpret_cast<const uint2*>(&Vt[db * 16 + lq][32 * h + 16 + lg * 4]);
+                const half8 vb = __builtin_bit_cast(half8, u32x4{v0.x, v0.y, v1.x, v1.y});
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+                    o[rt][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[rt][h], vb, o[rt][db], 0, 0, 0);
+            }
         }
         __syncthreads();
     }
