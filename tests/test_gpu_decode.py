@@ -70,6 +70,21 @@ def test_tiny_token_by_token_and_decode(dfa, arch, wdtype, over):
     m.close()
 
 
+@pytest.mark.parametrize("hd,n_heads,n_kv", [(32, 4, 2), (64, 4, 1), (64, 6, 3)])
+def test_head_dims_across_attention_tiles(dfa, hd, n_heads, n_kv):
+    # head_dim 32 (two dims per lane) and 64 (one float4 group per lane) at
+    # positions that span several 64-row attention tiles and a ragged tail
+    say(f"[tiny qwen3 f16, head_dim {hd}, {n_heads}/{n_kv} heads] 150-token prompt + 8 steps")
+    cfg = synth.config("tiny", wdtype="f16", head_dim=hd, n_heads=n_heads, n_kv_heads=n_kv, max_ctx=192)
+    W = synth.make_weights(cfg)
+    prompt = synth.make_prompt(cfg, 150)
+    fed, ref = oracle_greedy(cfg, W, prompt, 8, max_ctx=192)
+    m, got = gpu_teacher_forced(dfa, cfg, W, fed, max_ctx=192)
+    worst, ties = check_steps(got, ref, 1e-4, f"head_dim {hd}")
+    say(f"  worst rel-L2 {worst:.2e}, near-ties {ties}")
+    m.close()
+
+
 def test_tiny_long_context_multi_chunk(dfa):
     say("[tiny qwen3 f32] 200-token prompt (4 attention chunks, ragged) + 8 steps")
     cfg = synth.config("tiny", max_ctx=256)

@@ -87,6 +87,30 @@ def test_tiny_f16_bulk_then_bulk_then_decode(dfa, arch, over):
     m.close()
 
 
+@pytest.mark.parametrize("hd,n_heads,n_kv", [(32, 4, 2), (64, 4, 1), (64, 6, 3)])
+def test_head_dims_bulk_across_key_tiles(dfa, hd, n_heads, n_kv):
+    # bulk prefill of 150 rows (two full 64-key tiles and a ragged one, 64-row
+    # query blocks) after a 37-token bulk call, then decode
+    say(f"[tiny qwen3 f16, head_dim {hd}, {n_heads}/{n_kv} heads] bulk 37 + bulk 150 + 4 decode steps")
+    cfg = synth.config("tiny", wdtype="f16", head_dim=hd, n_heads=n_heads, n_kv_heads=n_kv, max_ctx=208)
+    W = synth.make_weights(cfg)
+    toks = synth.make_prompt(cfg, 187)
+    om, ref = oracle_run(cfg, W, [toks[:37], toks[37:]], 208)
+    m = dfa.Model(cfg, W)
+    g1 = m.forward(toks[:37]).cpu().numpy().copy()
+    g2 = m.forward(toks[37:]).cpu().numpy().copy()
+    check_logits(g1, ref[0], "after 37")
+    check_logits(g2, ref[1], "after 187")
+    check_kv(m, om, cfg, 187)
+    nxt = first_argmax(ref[1])
+    for i in range(4):
+        r = om.forward([nxt])
+        g = m.forward([nxt]).cpu().numpy()
+        check_logits(g, r, f"decode {i}")
+        nxt = first_argmax(r)
+    m.close()
+
+
 @pytest.mark.parametrize("arch", ["qwen3", "llama", "qwen2"])
 def test_tiny_q8_bulk_then_decode(dfa, arch):
     """8-bit block weights: the GEMMs dequantise the weight tiles to f16."""
