@@ -635,7 +635,7 @@ qk_post_rows_kernel(QkPostArgs a)
 // K/V tile is staged once for every head and row of the block and each K / V
 // fragment read from LDS feeds PF_RT MFMAs.
 //
-// Per tile of PF_TK keys, on v_mfma_f32_16x16x32_f16:
+// Per tile of 64 (or 32) keys, on v_mfma_f32_16x16x32_f16:
 //  * S^T = K Q^T (keys x queries; q arrives pre-scaled by log2(e)/sqrt(hd),
 //    so scores are in base 2): per 32 keys lane l holds 8 keys of query
 //    l%16, which is the layout P needs as the A operand of P V, so P never
@@ -670,8 +670,20 @@ constexpr int attn_pf_wph() { return G <= 4 ? 2 : 1; }
 template <int HD, int G>
 constexpr int attn_pf_rows() { return 16 * attn_pf_rt<HD>() * attn_pf_wph<G>(); }
 
-// Keys per tile of the prefill attention (a multiple of 32).
-constexpr int PF_TK = 64;
+// Keys per tile of the prefill attention: 64 where the next tile's K and V
+// chunks still fit the register prefetch (at most 8 float4 per thread),
+// else 32 (fewer threads per block, or head_dim 256).
+template <int HD, int G>
+constexpr bool attn_pf_prefetch_fits(int tk)
+{
+    constexpr int KQ = HD < 32 ? 32 : HD;
+    constexpr int NT = 64 * G * attn_pf_wph<G>();
+    const int kpt = (tk * (KQ / 4) + NT - 1) / NT;
+    const int vpt = ((tk / 2) * (HD / 4) + NT - 1) / NT;
+    return kpt + 2 * vpt <= 8;
+}
+template <int HD, int G>
+constexpr int attn_pf_tk() { return attn_pf_prefetch_fits<HD, G>(64) ? 64 : 32; }
 
 // Slack (base-2 units) by which a score may exceed the running maximum
 // before the maximum moves: weights stay below 2^8, well inside f16 for P.
@@ -682,7 +694,7 @@ __global__ void __launch_bounds__(64 * G * attn_pf_wph<G>())
 attn_prefill_kernel(AttnPrefillArgs a)
 {
     constexpr int KQ = HD < 32 ? 32 : HD;  // QK depth, zero padded to 32
-    constexpr int TK = PF_TK;               // keys per tile
+    constexpr int TK = attn_pf_tk<HD, G>(); // keys per tile
     constexpr int KB = TK / 16;             // 16-key blocks of a tile
     constexpr int NP = TK / 32;             // 32-key halves: P V steps
     constexpr int DB = HD / 16;             // 16-wide output blocks
