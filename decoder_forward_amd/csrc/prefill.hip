@@ -652,7 +652,8 @@ qk_post_rows_kernel(QkPostArgs a)
 //    in tiles that reach past the block's first row (or before its last
 //    row's window).
 // The next tile's K and V rows are loaded into registers while the current
-// one is computed (when they fit: at most 8 float4 per thread). Query blocks
+// one is computed (when they fit: 8 float4 per thread, 16 with one wave per
+// SIMD). Query blocks
 // run latest first: they have the most tiles.
 //
 // Lane layout of v_mfma_f32_16x16x32_f16 (checked on the device): lane l
@@ -670,9 +671,13 @@ constexpr int attn_pf_wph() { return G <= 4 ? 2 : 1; }
 template <int HD, int G>
 constexpr int attn_pf_rows() { return 16 * attn_pf_rt<HD>() * attn_pf_wph<G>(); }
 
+// Float4 registers per thread for the next tile's K and V chunks: 8, or 16
+// where a block has at most one wave per SIMD (twice the registers each).
+template <int G>
+constexpr int attn_pf_prefetch_budget() { return G * attn_pf_wph<G>() <= 4 ? 16 : 8; }
+
 // Keys per tile of the prefill attention: 64 where the next tile's K and V
-// chunks still fit the register prefetch (at most 8 float4 per thread),
-// else 32 (fewer threads per block, or head_dim 256).
+// chunks still fit the register prefetch, else 32.
 template <int HD, int G>
 constexpr bool attn_pf_prefetch_fits(int tk)
 {
@@ -680,7 +685,7 @@ constexpr bool attn_pf_prefetch_fits(int tk)
     constexpr int NT = 64 * G * attn_pf_wph<G>();
     const int kpt = (tk * (KQ / 4) + NT - 1) / NT;
     const int vpt = ((tk / 2) * (HD / 4) + NT - 1) / NT;
-    return kpt + 2 * vpt <= 8;
+    return kpt + 2 * vpt <= attn_pf_prefetch_budget<G>();
 }
 template <int HD, int G>
 constexpr int attn_pf_tk() { return attn_pf_prefetch_fits<HD, G>(64) ? 64 : 32; }
@@ -706,7 +711,7 @@ attn_prefill_kernel(AttnPrefillArgs a)
     constexpr int VE = (TK / 2) * (HD / 4); // row-pair chunks of a V tile
     constexpr int KPT = (KE + NT - 1) / NT; // per thread
     constexpr int VPT = (VE + NT - 1) / NT;
-    constexpr bool PREF = KPT + 2 * VPT <= 8;  // next tile held in registers
+    constexpr bool PREF = KPT + 2 * VPT <= attn_pf_prefetch_budget<G>();  // next tile held in registers
     __shared__ __attribute__((aligned(16))) _Float16 Ks[TK][KQ + 8];
     __shared__ __attribute__((aligned(16))) _Float16 Vt[HD][TK + 8];
     const int qb = gridDim.x - 1 - blockIdx.x;
