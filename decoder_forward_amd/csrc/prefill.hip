@@ -671,10 +671,14 @@ constexpr int attn_pf_wph() { return G <= 4 ? 2 : 1; }
 template <int HD, int G>
 constexpr int attn_pf_rows() { return 16 * attn_pf_rt<HD>() * attn_pf_wph<G>(); }
 
-// Float4 registers per thread for the next tile's K and V chunks: 8, or 16
-// where a block has at most one wave per SIMD (twice the registers each).
+// Float4 registers per thread for the next tile's K and V chunks: 8 with
+// two waves per SIMD, 12 where some SIMDs hold one wave (5-7 waves), 16
+// where a block has at most one wave per SIMD.
 template <int G>
-constexpr int attn_pf_prefetch_budget() { return G * attn_pf_wph<G>() <= 4 ? 16 : 8; }
+constexpr int attn_pf_prefetch_budget()
+{
+    return G * attn_pf_wph<G>() <= 4 ? 16 : G * attn_pf_wph<G>() < 8 ? 12 : 8;
+}
 
 // Keys per tile of the prefill attention: 64 where the next tile's K and V
 // chunks still fit the register prefetch, else 32.
