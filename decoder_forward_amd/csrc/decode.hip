@@ -350,6 +350,25 @@ __global__ void to_f32_kernel(const void* __restrict__ src, int src_dtype,
     }
 }
 
+// Deterministic pseudo-random values, uniform in [-1, 1), for timing
+// replays: element i gets a 32-bit integer hash of (i, seed) (the
+// multiply-xorshift finaliser of MurmurHash3) scaled to [-1, 1).
+__global__ void fill_random_kernel(void* __restrict__ dst, int64_t n, int f16, uint32_t seed)
+{
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+         i += int64_t(gridDim.x) * blockDim.x) {
+        uint32_t h = uint32_t(i) ^ (uint32_t(i >> 32) * 0x9e3779b9u) ^ seed;
+        h ^= h >> 16;
+        h *= 0x85ebca6bu;
+        h ^= h >> 13;
+        h *= 0xc2b2ae35u;
+        h ^= h >> 16;
+        const float v = float(int32_t(h)) * (1.0f / 2147483648.0f);
+        if (f16) static_cast<_Float16*>(dst)[i] = static_cast<_Float16>(v);
+        else static_cast<float*>(dst)[i] = v;
+    }
+}
+
 __global__ void q8_split_kernel(const uint8_t* __restrict__ blocks,
                                 int64_t n_blocks, int8_t* __restrict__ values,
                                 uint16_t* __restrict__ scales)
@@ -497,6 +516,15 @@ hipError_t launch_set_state(DevState* st, int pos, int tok, int step,
                             hipStream_t s)
 {
     DFK_LAUNCH(set_state_kernel, dim3(1), dim3(64), 0, s, st, pos, tok, step);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_random(void* dst, int64_t n, int f16, uint32_t seed, hipStream_t s)
+{
+    if (n <= 0) return hipSuccess;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    DFK_LAUNCH(fill_random_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, dst, n, f16, seed);
     return hipGetLastError();
 }
 

@@ -275,6 +275,11 @@ struct AttnPrefillArgs {
 };
 hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t s);
 
+// Deterministic pseudo-random values in [-1, 1) (f32, or f16 when f16 is
+// set): inputs for timing replays, whose power draw, and so clocks, depend
+// on the data.
+hipError_t launch_fill_random(void* dst, int64_t n, int f16, uint32_t seed, hipStream_t s);
+
 // Upload helpers.
 hipError_t launch_to_f32(const void* src, int src_dtype, int64_t n, float* dst,
                          hipStream_t s);

@@ -1678,14 +1678,16 @@ df_status df_time_prefill(df_model* m, int32_t kernel, int32_t rows, int32_t rep
     m->pool.reset();
     PfBufs b{};
     if (!pf_buffers(m, rows, &b, &e)) return set_err(m, e.code, e.msg);
-    // defined inputs: zero activations (the GEMMs' timing does not depend on values)
+    // Defined, non-constant inputs: pseudo-random activations. The matrix
+    // cores draw more power on random operands than on zeros, and the
+    // clocks follow, so zero inputs would time the GEMMs about 20% fast.
     const df_config& c = m->cfg;
     const size_t qd = size_t(c.n_heads) * c.head_dim, kvd = size_t(c.n_kv_heads) * c.head_dim;
-    hipError_t r = hipMemsetAsync(b.x, 0, size_t(rows) * c.d_model * 4, m->stream);
-    if (r == hipSuccess) r = hipMemsetAsync(b.h16, 0, size_t(rows) * c.d_model * 2, m->stream);
-    if (r == hipSuccess) r = hipMemsetAsync(b.qkv, 0, size_t(rows) * (qd + 2 * kvd) * 4, m->stream);
-    if (r == hipSuccess) r = hipMemsetAsync(b.att16, 0, size_t(rows) * qd * 2, m->stream);
-    if (r == hipSuccess) r = hipMemsetAsync(b.mid16, 0, size_t(rows) * c.ffn_dim * 2, m->stream);
+    hipError_t r = launch_fill_random(b.x, int64_t(rows) * c.d_model, 0, 1u, m->stream);
+    if (r == hipSuccess) r = launch_fill_random(b.h16, int64_t(rows) * c.d_model, 1, 2u, m->stream);
+    if (r == hipSuccess) r = launch_fill_random(b.qkv, int64_t(rows) * int64_t(qd + 2 * kvd), 0, 3u, m->stream);
+    if (r == hipSuccess) r = launch_fill_random(b.att16, int64_t(rows) * int64_t(qd), 1, 4u, m->stream);
+    if (r == hipSuccess) r = launch_fill_random(b.mid16, int64_t(rows) * c.ffn_dim, 1, 5u, m->stream);
     if (r == hipSuccess) r = hipEventRecord(m->ev0, m->stream);
     const int nl = c.n_layers;
     for (int rep = 0; rep < reps && r == hipSuccess; ++rep)

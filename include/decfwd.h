@@ -296,7 +296,8 @@ df_status df_time_kernel(df_model* m, int32_t kernel, int32_t reps,
 /* Mean device time of one layer's launches of a bulk-prefill class
  * (DF_K_PF_QKV .. DF_K_PF_DOWN) for `rows` rows (1 .. max_ctx) at positions
  * 0..rows-1: each layer's launches in turn, `reps` times, back to back
- * between one pair of HIP events, on zeroed activation buffers. The KV cache
+ * between one pair of HIP events, on activation buffers filled with
+ * pseudo-random values in [-1, 1) (the clocks depend on the operands). The KV cache
  * rows 0..rows-1 are overwritten (DF_K_PF_ATTN) and kv_len is left as it
  * was. Needs f16 or 8-bit block weights (else DF_ERR_UNSUPPORTED_OP).
  * Synchronises. */
