@@ -35,25 +35,45 @@ constexpr int MV_DEPTH = 1;         // matvec batch depth
 constexpr unsigned ERR_POLL = 256;  // spins between reads of the error word
 
 // ---------------------------------------------------------------------------
-// Grid barrier. words[0] counts arrivals within the launch (0 at launch
-// start); barrier k completes when it reaches k * nb. Thread 0 of each block
-// adds its arrival (no return value needed) and polls the count with
-// L2-bypassing loads. Callers make their stores complete (drain_memory in
+// Grid barrier on per-block flags. Barrier k of a launch publishes the value
+// (epoch << 10) + k, where epoch = words[3] counts the launches so far: the
+// block's thread 0 stores it in its own flag word (a write-through store,
+// no read-modify-write on a shared address), and wave 0 then polls all nb
+// flags, four per lane with one 16-byte L2-bypassing load, until every one
+// has reached the value (signed difference, so a faster block already at
+// barrier k + 1 counts). Values of earlier launches are smaller, so the
+// flags need no reset. Callers make their stores complete (drain_memory in
 // every thread) before the barrier; loads issued after the drain (the next
-// phase's weights) stay in flight across it. At exit the last block resets
-// the count (words[1] counts exits), so the next launch starts from 0.
-// words[2] is the error flag.
+// phase's weights) stay in flight across it. words[2] is the error flag:
+// a wait that runs out of spins sets it and every later wait gives up.
 // ---------------------------------------------------------------------------
-__device__ inline void grid_sync(int* words, int target)
+constexpr int MAX_BARRIERS = 1 << 10;  // per launch
+
+__device__ inline void grid_sync(int* words, int* flags, int value)
 {
     __syncthreads();
-    if (threadIdx.x == 0) {
-        __hip_atomic_fetch_add(gmem(words), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x < WAVE) {
+        const int lane = threadIdx.x;
+        if (lane == 0) st_shared_i(flags + blockIdx.x, value);
+        const int nb = gridDim.x;
         unsigned spins = 0;
-        while (ld_shared_i(words) - target < 0) {
+        for (;;) {
+            bool done = true;
+            for (int i0 = 0; i0 < nb; i0 += 4 * WAVE) {
+                const int i = i0 + 4 * lane;
+                if (i < nb) {
+                    const float4 f4 = coh_load4(reinterpret_cast<const float*>(flags), i);
+                    const int f[4] = {__float_as_int(f4.x), __float_as_int(f4.y), __float_as_int(f4.z),
+                                      __float_as_int(f4.w)};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (i + j < nb && int(unsigned(f[j]) - unsigned(value)) < 0) done = false;
+                }
+            }
+            if (__builtin_amdgcn_ballot_w64(!done) == 0) break;
             __builtin_amdgcn_s_sleep(1);
             if (++spins % ERR_POLL == 0 && (spins >= SPIN_LIMIT || ld_shared_i(words + 2) != 0)) {
-                st_shared_i(words + 2, 1);
+                if (lane == 0) st_shared_i(words + 2, 1);
                 break;
             }
         }
@@ -61,17 +81,12 @@ __device__ inline void grid_sync(int* words, int target)
     __syncthreads();
 }
 
-__device__ inline void grid_exit(int* words, int nb)
+// Block 0 counts the launch once every block has passed a barrier (so has
+// read the epoch at its start).
+__device__ inline void grid_exit(int* words, int epoch)
 {
     drain_memory();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const int prev = __hip_atomic_fetch_add(gmem(words + 1), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (prev == nb - 1) {
-            st_shared_i(words, 0);
-            st_shared_i(words + 1, 0);
-        }
-    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) st_shared_i(words + 3, int(unsigned(epoch) + 1u));
 }
 
 // The value of x, hidden from the optimiser: per-lane values a phase derives
@@ -148,8 +163,11 @@ decode_step_kernel(const StepArgs* __restrict__ Ap, float* logits_out, int advan
     const int b = blockIdx.x;
     const int nb = gridDim.x;
     const int tid = threadIdx.x;
+    const int epoch = ld_shared_i(fresh(Ap)->bar + 3);
     int n_bar = 0;
-    auto sync = [&]() { grid_sync(fresh(Ap)->bar, ++n_bar * nb); };
+    auto sync = [&]() {
+        grid_sync(fresh(Ap)->bar, fresh(Ap)->bar_flags, int(unsigned(epoch) * MAX_BARRIERS + unsigned(++n_bar)));
+    };
     const int p = gmem(fresh(Ap)->st)->pos;
     const int tok = gmem(fresh(Ap)->st)->tok;
 
@@ -311,7 +329,7 @@ decode_step_kernel(const StepArgs* __restrict__ Ap, float* logits_out, int advan
             }
         }
     }
-    grid_exit(fresh(Ap)->bar, nb);
+    grid_exit(fresh(Ap)->bar, epoch);
 }
 
 template <int WT, int WO, int HD, int G>
@@ -353,6 +371,7 @@ bool step_fits(const StepArgs& a, int wdtype, int odtype, size_t* lds)
     const int G = a.n_heads / a.n_kv;
     const void* k = pick(wdtype, odtype, a.hd, G);
     if (!k) return false;
+    if (6 * a.n_layers + 4 >= MAX_BARRIERS) return false;  // barrier values of one launch
     size_t need = 0;
     need = std::max(need, mv_lds_bytes(a.mv_qkv, MV_STORE));
     need = std::max(need, mv_lds_bytes(a.mv_o, MV_RESID));

@@ -199,7 +199,8 @@ struct StepArgs {
     float* amax_val; int* amax_idx;          // argmax partials, one per block
     DevState* st;                            // position, token, step
     int* gen_out;                            // generated tokens
-    int* bar;                                // grid barrier: arrivals, exits, error flag
+    int* bar;                                // grid barrier words: [2] error flag, [3] launch count
+    int* bar_flags;                          // grid barrier: one flag per block
     int* attn_cnt;                           // per KV head: splits finished (ticket)
     MvLayout mv_qkv, mv_o, mv_gu, mv_down, mv_logits;
 };

@@ -174,7 +174,7 @@ struct df_model {
     int step_wdtype = 0, step_odtype = 0;
     StepArgs step{};
     StepArgs* step_dev = nullptr;
-    int* bar_words = nullptr;     // grid barrier (arrivals, exits, error flag), attention tickets
+    int* bar_words = nullptr;     // grid barrier (error flag, launch count, block flags), attention tickets
     size_t bar_bytes = 0;
     bool step_unchecked = false;  // step launches whose error flag is unread
 
@@ -768,7 +768,10 @@ bool setup_step(df_model* m, Fail* e)
     a.mid = static_cast<float*>(A(size_t(c.ffn_dim) * 4, "step activations"));
     a.amax_val = static_cast<float*>(A(size_t(nb) * 4, "argmax partials"));
     a.amax_idx = static_cast<int*>(A(size_t(nb) * 4, "argmax partials"));
-    const size_t n_words = 4 + size_t(c.n_kv_heads);
+    // barrier words, attention tickets, then one flag per block (padded to
+    // whole 16-byte groups: the barrier reads the flags four at a time)
+    const size_t flags_at = (4 + size_t(c.n_kv_heads) + 3) & ~size_t(3);
+    const size_t n_words = flags_at + ((size_t(nb) + 3) & ~size_t(3));
     m->bar_words = static_cast<int*>(A(n_words * 4, "grid barrier and tickets"));
     StepLayer* ly_dev = static_cast<StepLayer*>(A(size_t(c.n_layers) * sizeof(StepLayer), "layer table"));
     m->step_dev = static_cast<StepArgs*>(A(sizeof(StepArgs), "step description"));
@@ -777,6 +780,7 @@ bool setup_step(df_model* m, Fail* e)
         return false;
     a.bar = m->bar_words;
     a.attn_cnt = m->bar_words + 4;
+    a.bar_flags = m->bar_words + flags_at;
     a.layers = ly_dev;
     std::vector<StepLayer> ly(size_t(c.n_layers));
     for (int l = 0; l < c.n_layers; ++l) {
