@@ -87,10 +87,13 @@ def test_tiny_f16_bulk_then_bulk_then_decode(dfa, arch, over):
     m.close()
 
 
-@pytest.mark.parametrize("hd,n_heads,n_kv", [(32, 4, 2), (64, 4, 1), (64, 6, 3)])
+@pytest.mark.parametrize("hd,n_heads,n_kv", [(32, 4, 2), (64, 4, 1), (64, 6, 3),
+                                              (128, 4, 4), (128, 10, 2), (128, 12, 2), (128, 16, 2)])
 def test_head_dims_bulk_across_key_tiles(dfa, hd, n_heads, n_kv):
-    # bulk prefill of 150 rows (two full 64-key tiles and a ragged one, 64-row
-    # query blocks) after a 37-token bulk call, then decode
+    # bulk prefill of 150 rows (two full 64-key tiles and a ragged one) after
+    # a 37-token bulk call, then decode; 1, 5, 6 and 8 query heads per KV
+    # head at head_dim 128 take the 32- and 64-key tiles with each register
+    # prefetch budget
     say(f"[tiny qwen3 f16, head_dim {hd}, {n_heads}/{n_kv} heads] bulk 37 + bulk 150 + 4 decode steps")
     cfg = synth.config("tiny", wdtype="f16", head_dim=hd, n_heads=n_heads, n_kv_heads=n_kv, max_ctx=208)
     W = synth.make_weights(cfg)
