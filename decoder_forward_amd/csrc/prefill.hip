@@ -670,6 +670,9 @@ template <int G>
 constexpr int attn_pf_wph() { return G <= 4 ? 2 : 1; }
 template <int HD, int G>
 constexpr int attn_pf_rows() { return 16 * attn_pf_rt<HD>() * attn_pf_wph<G>(); }
+// Threads of a block: G heads x waves per head (the kernel's launch bound).
+template <int G>
+constexpr int attn_pf_threads() { return 64 * G * attn_pf_wph<G>(); }
 
 // Float4 registers per thread for the next tile's K and V chunks: 8 with
 // two waves per SIMD, 12 where some SIMDs hold one wave (5-7 waves), 16
@@ -699,7 +702,7 @@ constexpr int attn_pf_tk() { return attn_pf_prefetch_fits<HD, G>(64) ? 64 : 32; 
 constexpr float RESCALE_SLACK = 8.0f;
 
 template <int HD, int G>
-__global__ void __launch_bounds__(64 * G * attn_pf_wph<G>())
+__global__ void __launch_bounds__(attn_pf_threads<G>())
 attn_prefill_kernel(AttnPrefillArgs a)
 {
     constexpr int KQ = HD < 32 ? 32 : HD;  // QK depth, zero padded to 32
@@ -988,14 +991,14 @@ template <int HD>
 hipError_t launch_attn_prefill_hd(const AttnPrefillArgs& a, hipStream_t s)
 {
     switch (a.n_heads / a.n_kv) {
-    case 1: DFK_LAUNCH((attn_prefill_kernel<HD, 1>), (pf_grid<HD, 1>(a)), dim3(128), 0, s, a); break;
-    case 2: DFK_LAUNCH((attn_prefill_kernel<HD, 2>), (pf_grid<HD, 2>(a)), dim3(256), 0, s, a); break;
-    case 3: DFK_LAUNCH((attn_prefill_kernel<HD, 3>), (pf_grid<HD, 3>(a)), dim3(384), 0, s, a); break;
-    case 4: DFK_LAUNCH((attn_prefill_kernel<HD, 4>), (pf_grid<HD, 4>(a)), dim3(512), 0, s, a); break;
-    case 5: DFK_LAUNCH((attn_prefill_kernel<HD, 5>), (pf_grid<HD, 5>(a)), dim3(320), 0, s, a); break;
-    case 6: DFK_LAUNCH((attn_prefill_kernel<HD, 6>), (pf_grid<HD, 6>(a)), dim3(384), 0, s, a); break;
-    case 7: DFK_LAUNCH((attn_prefill_kernel<HD, 7>), (pf_grid<HD, 7>(a)), dim3(448), 0, s, a); break;
-    case 8: DFK_LAUNCH((attn_prefill_kernel<HD, 8>), (pf_grid<HD, 8>(a)), dim3(512), 0, s, a); break;
+    case 1: DFK_LAUNCH((attn_prefill_kernel<HD, 1>), (pf_grid<HD, 1>(a)), dim3(attn_pf_threads<1>()), 0, s, a); break;
+    case 2: DFK_LAUNCH((attn_prefill_kernel<HD, 2>), (pf_grid<HD, 2>(a)), dim3(attn_pf_threads<2>()), 0, s, a); break;
+    case 3: DFK_LAUNCH((attn_prefill_kernel<HD, 3>), (pf_grid<HD, 3>(a)), dim3(attn_pf_threads<3>()), 0, s, a); break;
+    case 4: DFK_LAUNCH((attn_prefill_kernel<HD, 4>), (pf_grid<HD, 4>(a)), dim3(attn_pf_threads<4>()), 0, s, a); break;
+    case 5: DFK_LAUNCH((attn_prefill_kernel<HD, 5>), (pf_grid<HD, 5>(a)), dim3(attn_pf_threads<5>()), 0, s, a); break;
+    case 6: DFK_LAUNCH((attn_prefill_kernel<HD, 6>), (pf_grid<HD, 6>(a)), dim3(attn_pf_threads<6>()), 0, s, a); break;
+    case 7: DFK_LAUNCH((attn_prefill_kernel<HD, 7>), (pf_grid<HD, 7>(a)), dim3(attn_pf_threads<7>()), 0, s, a); break;
+    case 8: DFK_LAUNCH((attn_prefill_kernel<HD, 8>), (pf_grid<HD, 8>(a)), dim3(attn_pf_threads<8>()), 0, s, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
