@@ -250,6 +250,15 @@ struct GemmArgs {
 };
 hipError_t launch_gemm(const GemmArgs& g, int mode, hipStream_t s);
 
+// 8-bit block rows to f16 rows: out[r][k] = f16(scale[r][k / 32] * q[r][k]),
+// the values the 8-bit GEMM stores in LDS; cols a multiple of 32.
+hipError_t launch_dequant_q8(const void* values, const uint16_t* scales, int64_t rows, int64_t cols,
+                             uint16_t* out, hipStream_t s);
+// Bulk prefill of at least this many rows dequantises each layer's 8-bit
+// matrices to f16 first and runs the f16 GEMMs: the conversion costs less
+// than the 8-bit GEMM's slower register-staged loads from about here on.
+constexpr int PF_DEQUANT_MIN_ROWS = 2048;
+
 struct QkPostArgs {
     const float* qkv;     // [S][qd | kvd | kvd] f32
     const float* q_norm;  // [hd] or null

@@ -1074,6 +1074,7 @@ struct PfBufs {
     uint16_t* mid16;   // [S][F] gated FFN activation, f16
     float* tmp;        // gemma3: [S][d] o / down outputs before their rms_norm
     int* toks;         // [S]
+    uint16_t* wdq;     // 8-bit weights, S >= PF_DEQUANT_MIN_ROWS: one matrix dequantised to f16
 };
 
 bool pf_buffers(df_model* m, int S, PfBufs* b, Fail* e)
@@ -1090,6 +1091,12 @@ bool pf_buffers(df_model* m, int S, PfBufs* b, Fail* e)
     b->mid16 = static_cast<uint16_t*>(A(size_t(S) * F * 2));
     b->toks = static_cast<int*>(A(size_t(S) * 4));
     b->tmp = c.arch == DF_ARCH_GEMMA3 ? static_cast<float*>(A(size_t(S) * d * 4)) : nullptr;
+    b->wdq = nullptr;
+    if (c.n_layers > 0 && m->layers[0].wqkv.scales && S >= PF_DEQUANT_MIN_ROWS) {
+        const size_t most = std::max(std::max((qd + 2 * kvd) * d, d * qd), std::max(2 * F * d, d * F));
+        b->wdq = static_cast<uint16_t*>(A(most * 2));
+        if (!b->wdq) return false;
+    }
     return b->x && b->h16 && b->qkv && b->q16 && b->att16 && b->mid16 && b->toks &&
            (c.arch != DF_ARCH_GEMMA3 || b->tmp);
 }
@@ -1114,11 +1121,22 @@ hipError_t pf_launch(df_model* m, const PfBufs& b, int kernel, int l, int S, int
     g.zeros = m->zeros;
     g.M = S;
     hipError_t r = hipSuccess;
+    // The GEMM's B operand: the weight as stored, or (8-bit blocks with a
+    // dequantisation buffer) its f16 rows converted just before the GEMM.
+    auto weights = [&](const Weight& W) {
+        g.B = static_cast<const uint16_t*>(W.data);
+        g.Bsc = W.scales;
+        if (r == hipSuccess && W.scales && b.wdq) {
+            r = launch_dequant_q8(W.data, W.scales, W.rows, W.cols, b.wdq, m->stream);
+            g.B = b.wdq;
+            g.Bsc = nullptr;
+        }
+    };
     switch (kernel) {
     case DF_K_PF_QKV:
         r = launch_rmsnorm_rows(b.x, L.attn_norm, S, d, eps, b.h16, m->stream);
         g.A = b.h16; g.lda = d;
-        g.B = static_cast<const uint16_t*>(L.wqkv.data); g.ldb = d; g.Bsc = L.wqkv.scales;
+        weights(L.wqkv); g.ldb = d;
         g.C = b.qkv; g.ldc = qd + 2 * kvd; g.N = qd + 2 * kvd; g.K = d;
         if (r == hipSuccess) r = launch_gemm(g, GEMM_STORE_F32, m->stream);
         return r;
@@ -1141,24 +1159,24 @@ hipError_t pf_launch(df_model* m, const PfBufs& b, int kernel, int l, int S, int
     }
     case DF_K_PF_O:
         g.A = b.att16; g.lda = qd;
-        g.B = static_cast<const uint16_t*>(L.wo.data); g.ldb = qd; g.Bsc = L.wo.scales;
+        weights(L.wo); g.ldb = qd;
         g.C = gemma ? static_cast<void*>(b.tmp) : b.x; g.ldc = d; g.N = d; g.K = qd;
-        r = launch_gemm(g, gemma ? GEMM_STORE_F32 : GEMM_ADD_F32, m->stream);
+        if (r == hipSuccess) r = launch_gemm(g, gemma ? GEMM_STORE_F32 : GEMM_ADD_F32, m->stream);
         if (r == hipSuccess && gemma) r = launch_norm_add_rows(b.x, b.tmp, L.post_attn_norm, S, d, eps, m->stream);
         return r;
     case DF_K_PF_GATE_UP:
         r = launch_rmsnorm_rows(b.x, L.ffn_norm, S, d, eps, b.h16, m->stream);
         g.A = b.h16; g.lda = d;
-        g.B = static_cast<const uint16_t*>(L.wgu.data); g.ldb = d; g.Bsc = L.wgu.scales;
+        weights(L.wgu); g.ldb = d;
         g.C = b.mid16; g.ldc = F; g.N = F; g.K = d; g.up_rows = F;
         g.act = gemma ? ACT_GELU_TANH : ACT_SILU;
         if (r == hipSuccess) r = launch_gemm(g, GEMM_SWIGLU_F16, m->stream);
         return r;
     case DF_K_PF_DOWN:
         g.A = b.mid16; g.lda = F;
-        g.B = static_cast<const uint16_t*>(L.wd.data); g.ldb = F; g.Bsc = L.wd.scales;
+        weights(L.wd); g.ldb = F;
         g.C = gemma ? static_cast<void*>(b.tmp) : b.x; g.ldc = d; g.N = d; g.K = F;
-        r = launch_gemm(g, gemma ? GEMM_STORE_F32 : GEMM_ADD_F32, m->stream);
+        if (r == hipSuccess) r = launch_gemm(g, gemma ? GEMM_STORE_F32 : GEMM_ADD_F32, m->stream);
         if (r == hipSuccess && gemma) r = launch_norm_add_rows(b.x, b.tmp, L.post_ffn_norm, S, d, eps, m->stream);
         return r;
     }

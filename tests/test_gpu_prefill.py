@@ -135,6 +135,30 @@ def test_tiny_q8_bulk_then_decode(dfa, arch):
     m.close()
 
 
+@pytest.mark.parametrize("arch", ["llama", "qwen2"])
+def test_tiny_q8_long_bulk_dequantised_first(dfa, arch):
+    """From 2048 rows on, each layer's 8-bit matrices are dequantised to f16
+    before the f16 GEMMs; the result must match the oracle as the in-GEMM
+    dequantisation does."""
+    S = 2100
+    say(f"[tiny {arch} q8] bulk {S} (weights dequantised before the GEMMs) + 3 decode steps vs the oracle")
+    cfg = synth.config("tiny", arch=arch, wdtype="q8", d_model=192, ffn_dim=416, max_ctx=S + 8)
+    W = synth.make_weights(cfg)
+    toks = synth.make_prompt(cfg, S)
+    om, ref = oracle_run(cfg, W, [toks], S + 8)
+    m = dfa.Model(cfg, W)
+    got = m.forward(toks).cpu().numpy().copy()
+    assert m.kv_len == S
+    check_logits(got, ref[0], f"after {S}")
+    check_kv(m, om, cfg, S)
+    nxt = first_argmax(ref[0])
+    for i in range(3):
+        r = om.forward([nxt])
+        check_logits(m.forward([nxt]).cpu().numpy(), r, f"decode {i}")
+        nxt = first_argmax(r)
+    m.close()
+
+
 @pytest.mark.parametrize("name,S,vocab", [("qwen3_8b", 300, None), ("llama_8b", 200, 4096),
                                           ("qwen3_0p6b", 137, None), ("llama_8b_q8", 160, 4096),
                                           ("qwen2_7b", 150, 4096)])
