@@ -301,9 +301,9 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} "
-              f"(WORLD_SIZE {world}) is not supported. Multi-GPU sharding is "
-              f"described in DESIGN.md, not built.", file=sys.stderr)
+        print(f"bench.py: the library runs a model on one GPU; --gpus {args.gpus} "
+              f"(WORLD_SIZE {world}) is not supported (sharding a model over "
+              f"several GPUs is not implemented).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
