@@ -94,25 +94,27 @@ rmsnorm_rows_kernel(const float* __restrict__ x, const float* __restrict__ w,
 }
 
 // ---------------------------------------------------------------------------
-// 8-bit block rows to f16: thread t of row blockIdx.y converts values
-// 8t .. 8t + 7 (one 8-byte load, one 16-byte store), with the same rounding
-// as the 8-bit GEMM's load path (f32 product, rounded once to f16).
+// 8-bit block rows to f16: thread t converts values 8t .. 8t + 7 (one
+// 8-byte load, one 16-byte store) of rows blockIdx.y, blockIdx.y +
+// gridDim.y, ..., with the same rounding as the 8-bit GEMM's load path (f32
+// product, rounded once to f16).
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256)
-dequant_q8_kernel(const int8_t* __restrict__ q, const uint16_t* __restrict__ sc, int64_t cols,
+dequant_q8_kernel(const int8_t* __restrict__ q, const uint16_t* __restrict__ sc, int64_t rows, int64_t cols,
                   uint16_t* __restrict__ out)
 {
-    const int64_t r = blockIdx.y;
     const int64_t c = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 8;
     if (c >= cols) return;
-    const uint2 v = *reinterpret_cast<const uint2*>(q + r * cols + c);
-    const float s = h2f(sc[r * (cols / 32) + c / 32]);
-    uint4 o;
-    o.x = pack_h2(float(int8_t(v.x & 0xff)) * s, float(int8_t((v.x >> 8) & 0xff)) * s);
-    o.y = pack_h2(float(int8_t((v.x >> 16) & 0xff)) * s, float(int8_t(v.x >> 24)) * s);
-    o.z = pack_h2(float(int8_t(v.y & 0xff)) * s, float(int8_t((v.y >> 8) & 0xff)) * s);
-    o.w = pack_h2(float(int8_t((v.y >> 16) & 0xff)) * s, float(int8_t(v.y >> 24)) * s);
-    *reinterpret_cast<uint4*>(out + r * cols + c) = o;
+    for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
+        const uint2 v = *reinterpret_cast<const uint2*>(q + r * cols + c);
+        const float s = h2f(sc[r * (cols / 32) + c / 32]);
+        uint4 o;
+        o.x = pack_h2(float(int8_t(v.x & 0xff)) * s, float(int8_t((v.x >> 8) & 0xff)) * s);
+        o.y = pack_h2(float(int8_t((v.x >> 16) & 0xff)) * s, float(int8_t(v.x >> 24)) * s);
+        o.z = pack_h2(float(int8_t(v.y & 0xff)) * s, float(int8_t((v.y >> 8) & 0xff)) * s);
+        o.w = pack_h2(float(int8_t((v.y >> 16) & 0xff)) * s, float(int8_t(v.y >> 24)) * s);
+        *reinterpret_cast<uint4*>(out + r * cols + c) = o;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1032,10 +1034,11 @@ hipError_t launch_dequant_q8(const void* values, const uint16_t* scales, int64_t
                              uint16_t* out, hipStream_t s)
 {
     if (rows <= 0 || cols <= 0) return hipSuccess;
-    if (cols % 32 != 0 || rows > 65535) return hipErrorInvalidValue;
+    if (cols % 32 != 0) return hipErrorInvalidValue;
     const int64_t per_row = cols / 8;  // 8 values per thread
-    const dim3 grid(unsigned((per_row + 255) / 256), unsigned(rows));
-    DFK_LAUNCH(dequant_q8_kernel, grid, dim3(256), 0, s, static_cast<const int8_t*>(values), scales, cols, out);
+    const dim3 grid(unsigned((per_row + 255) / 256), unsigned(rows < 65535 ? rows : 65535));
+    DFK_LAUNCH(dequant_q8_kernel, grid, dim3(256), 0, s, static_cast<const int8_t*>(values), scales, rows, cols,
+               out);
     return hipGetLastError();
 }
 

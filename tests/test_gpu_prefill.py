@@ -159,6 +159,22 @@ def test_tiny_q8_long_bulk_dequantised_first(dfa, arch):
     m.close()
 
 
+def test_q8_dequantised_first_at_the_widest_ffn(dfa):
+    """ffn 32768 (the widest the library takes): the gate/up matrix has 65536
+    rows, more than one launch grid dimension holds, at exactly the row count
+    from which the weights are dequantised before the GEMMs."""
+    S = 2048
+    say(f"[tiny llama q8, ffn 32768] bulk {S} vs the oracle")
+    cfg = synth.config("tiny", arch="llama", wdtype="q8", ffn_dim=32768, max_ctx=S + 4)
+    W = synth.make_weights(cfg)
+    toks = synth.make_prompt(cfg, S)
+    om, ref = oracle_run(cfg, W, [toks], S + 4)
+    m = dfa.Model(cfg, W)
+    got = m.forward(toks).cpu().numpy().copy()
+    check_logits(got, ref[0], f"after {S}")
+    m.close()
+
+
 @pytest.mark.parametrize("name,S,vocab", [("qwen3_8b", 300, None), ("llama_8b", 200, 4096),
                                           ("qwen3_0p6b", 137, None), ("llama_8b_q8", 160, 4096),
                                           ("qwen2_7b", 150, 4096)])
