@@ -135,14 +135,16 @@ def test_tiny_q8_bulk_then_decode(dfa, arch):
     m.close()
 
 
-@pytest.mark.parametrize("arch", ["llama", "qwen2"])
+@pytest.mark.parametrize("arch", ["llama", "qwen2", "gemma3"])
 def test_tiny_q8_long_bulk_dequantised_first(dfa, arch):
     """From 2048 rows on, each layer's 8-bit matrices are dequantised to f16
     before the f16 GEMMs; the result must match the oracle as the in-GEMM
     dequantisation does."""
     S = 2100
     say(f"[tiny {arch} q8] bulk {S} (weights dequantised before the GEMMs) + 3 decode steps vs the oracle")
-    cfg = synth.config("tiny", arch=arch, wdtype="q8", d_model=192, ffn_dim=416, max_ctx=S + 8)
+    name = "tiny_gemma3" if arch == "gemma3" else "tiny"
+    over = {} if arch == "gemma3" else dict(arch=arch)
+    cfg = synth.config(name, wdtype="q8", d_model=192, ffn_dim=416, max_ctx=S + 8, **over)
     W = synth.make_weights(cfg)
     toks = synth.make_prompt(cfg, S)
     om, ref = oracle_run(cfg, W, [toks], S + 8)
