@@ -198,7 +198,7 @@ def prefill_classes(dfa, m, cfg, S):
     events) and the algorithmic flops of its GEMM (2 S N K; the causal
     attention 2 S^2 hd n_heads, QK^T and PV over the lower triangle), then
     the MFMA roofline of the dominant class, the gate/up GEMM. Runs after
-    decode timing: it overwrites cache rows 0..S-1."""
+    decode timing, on an emptied cache (the replays write rows 0..S-1)."""
     d, F, hd = cfg["d_model"], cfg["ffn_dim"], cfg["head_dim"]
     qd, kvd = cfg["n_heads"] * hd, cfg["n_kv_heads"] * hd
     flops = {"qkv": 2 * S * (qd + 2 * kvd) * d, "attn": 2 * S * S * hd * cfg["n_heads"],
@@ -384,7 +384,7 @@ def main():
         n = per_step.get(k, cfg["n_layers"])
         kernels[k] = {"launches_per_step": n, "mean_us": round(us, 2),
                       "ms_per_step": round(us * n / 1e3, 4)}
-    rewind()
+    m.reset()  # the prefill replays write cache rows past kv_len: all S of them
     prefill_kernels, pf_roof = prefill_classes(dfa, m, cfg, ctx) if args.context_from == "prefill" else ({}, None)
     gu = kernels["gate_up"]
     gu_bytes = gate_up_launch_bytes(cfg)

@@ -39,10 +39,13 @@ EXPORTS = ("df_load", "df_forward", "df_generate", "df_reset_kv_cache",
            "df_free", "df_last_error", "df_get_timings", "df_kv_length",
            "df_argmax", "df_read_kv", "df_write_kv", "df_stream",
            "df_profile", "df_profile_read", "df_time_kernel", "df_session",
-           "df_time_prefill")
+           "df_time_prefill", "df_prefill_plan")
 KERNELS = {"embed": 0, "qkv": 1, "attn": 2, "o": 3, "gate_up": 4, "down": 5,
            "logits": 6, "argmax": 7, "attn_merge": 8, "step": 9}
 PREFILL_KERNELS = {"qkv": 10, "attn": 11, "o": 12, "gate_up": 13, "down": 14}
+# df_prefill_plan tile codes and flags.
+GEMM_TILES = {1: "128x128", 2: "128x256", 3: "256x256", 4: "256x256_lds"}
+DF_GEMM_TILE_MASK, DF_GEMM_Q8_IN_GEMM, DF_GEMM_Q8_DEQUANT_FIRST = 15, 16, 32
 # df_options.flags: every decode step as one persistent launch (opt-in).
 DF_FLAG_PERSISTENT_STEP = 1
 
@@ -118,6 +121,7 @@ def lib() -> C.CDLL:
     L.df_profile_read.argtypes = [vp, i32, P(C.c_int64), P(C.c_double)]
     L.df_time_kernel.argtypes = [vp, i32, i32, P(C.c_double)]
     L.df_time_prefill.argtypes = [vp, i32, i32, i32, P(C.c_double)]
+    L.df_prefill_plan.argtypes = [vp, i32, P(i32)]
     for name in EXPORTS:
         if name not in ("df_free", "df_last_error", "df_stream"):
             getattr(L, name).restype = i32
@@ -273,10 +277,23 @@ def df_time_kernel(h, kernel: str, reps: int = 8) -> float:
 
 def df_time_prefill(h, kernel: str, rows: int, reps: int = 2) -> float:
     """Mean microseconds of one layer's launches of a bulk-prefill class for
-    `rows` rows (overwrites cache rows 0..rows-1)."""
+    `rows` rows at positions kv_len.. (writes only cache rows past kv_len)."""
     us = C.c_double()
     _check(lib().df_time_prefill(h, PREFILL_KERNELS[kernel], rows, reps, C.byref(us)), h)
     return us.value
+
+
+def df_prefill_plan(h, rows: int) -> dict:
+    """The GEMM kernels a bulk prefill of `rows` rows runs: for each of
+    qkv / o / gate_up / down, (tile name, 8-bit in-GEMM dequantisation,
+    8-bit dequantised first)."""
+    plan = (C.c_int32 * 4)()
+    _check(lib().df_prefill_plan(h, rows, plan), h)
+    out = {}
+    for k, v in zip(("qkv", "o", "gate_up", "down"), plan):
+        out[k] = (GEMM_TILES.get(v & DF_GEMM_TILE_MASK), bool(v & DF_GEMM_Q8_IN_GEMM),
+                  bool(v & DF_GEMM_Q8_DEQUANT_FIRST))
+    return out
 
 
 def df_profile_read(h, kernel: str):

@@ -249,6 +249,19 @@ struct GemmArgs {
     int act;                   // GEMM_SWIGLU_F16's gate activation (GateAct)
 };
 hipError_t launch_gemm(const GemmArgs& g, int mode, hipStream_t s);
+// The GEMM kernel launch_gemm runs for an M x N problem in `mode` (q8:
+// 8-bit block weights dequantised inside the GEMM): a GEMM_PLAN_* tile
+// code, plus GEMM_PLAN_Q8_IN_GEMM for q8. Host only.
+enum GemmPlan {
+    GEMM_PLAN_128x128 = 1,      // 4 waves, register-staged operand loads
+    GEMM_PLAN_128x256 = 2,      // 8 waves, register-staged
+    GEMM_PLAN_256x256 = 3,      // 8 waves, register-staged (8-bit weights)
+    GEMM_PLAN_256x256_LDS = 4,  // 8 waves, operand tiles loaded straight into LDS
+    GEMM_PLAN_TILE_MASK = 15,
+    GEMM_PLAN_Q8_IN_GEMM = 16,  // weight tiles dequantised on their way into LDS
+    GEMM_PLAN_DEQUANT_FIRST = 32,  // 8-bit weights converted to f16 before the GEMM (runtime)
+};
+int gemm_plan(int64_t M, int64_t N, int mode, bool q8);
 
 // 8-bit block rows to f16 rows: out[r][k] = f16(scale[r][k / 32] * q[r][k]),
 // the values the 8-bit GEMM stores in LDS; cols a multiple of 32.

@@ -1066,26 +1066,39 @@ int gemm_cu_count()
     return v;
 }
 
-hipError_t launch_gemm(const GemmArgs& g, int mode, hipStream_t s)
+int gemm_plan(int64_t M, int64_t N, int mode, bool q8)
 {
-    if (g.M <= 0 || g.N <= 0) return hipSuccess;
+    if (M <= 0 || N <= 0) return 0;
     // Tile by grid size (measured on the 8B shapes at 2048 and 4096 rows):
     // 256 x 256 on 8 waves (two per SIMD, 128 x 64 wave tiles) from about
     // 160 tiles up; 128 x 256 on 8 waves (64 x 64 wave tiles) below that;
     // 128 x 128 on 4 waves for small problems.
     const int64_t cols = mode == GEMM_SWIGLU_F16 ? 128 : 256;  // output columns of a 256-wide B tile
-    const int64_t nt = (g.N + cols - 1) / cols;
-    int shape = int64_t((g.M + 255) / 256) * nt >= 160 ? 2 : int64_t((g.M + 127) / 128) * nt >= 64 ? 1 : 0;
+    const int64_t nt = (N + cols - 1) / cols;
+    int shape = int64_t((M + 255) / 256) * nt >= 160 ? 2 : int64_t((M + 127) / 128) * nt >= 64 ? 1 : 0;
     // Both large shapes run one block per compute unit. A 256 x 256 grid
     // whose last round of tiles is part-empty can finish sooner as 128 x 256
     // tiles, which take about 0.61 of the time of a 256 x 256 tile here
     // (q/k/v at 4096 rows of the 8B shapes: 384 tiles in 2 rounds, 768 in 3).
     if (shape == 2) {
         const int64_t cu = gemm_cu_count();
-        const int64_t t2 = ((g.M + 255) / 256) * nt, t1 = ((g.M + 127) / 128) * nt;
+        const int64_t t2 = ((M + 255) / 256) * nt, t1 = ((M + 127) / 128) * nt;
         const double r2 = double((t2 + cu - 1) / cu), r1 = double((t1 + cu - 1) / cu);
         if (r1 * 0.61 < r2 * 0.95) shape = 1;
     }
+    // f16 weights on 256-row tiles load straight into LDS; 8-bit blocks
+    // (dequantised on their way into LDS) and the smaller tiles use the
+    // register-staged kernel.
+    const int tile = shape == 2 ? (q8 ? GEMM_PLAN_256x256 : GEMM_PLAN_256x256_LDS)
+                     : shape == 1 ? GEMM_PLAN_128x256 : GEMM_PLAN_128x128;
+    return tile | (q8 ? GEMM_PLAN_Q8_IN_GEMM : 0);
+}
+
+hipError_t launch_gemm(const GemmArgs& g, int mode, hipStream_t s)
+{
+    if (g.M <= 0 || g.N <= 0) return hipSuccess;
+    const int plan = gemm_plan(g.M, g.N, mode, g.Bsc != nullptr) & GEMM_PLAN_TILE_MASK;
+    const int shape = plan == GEMM_PLAN_128x128 ? 0 : plan == GEMM_PLAN_128x256 ? 1 : 2;
 #define DF_GEMM_BY_SHAPE(MODE_)                                                  \
     return shape == 2   ? launch_gemm_t<256, 256, 4, MODE_>(g, s)                \
            : shape == 1 ? launch_gemm_t<128, 256, 4, MODE_>(g, s)                \

@@ -13,6 +13,13 @@
 #include "../../include/decfwd.h"
 
 static_assert(dfk::MAX_WIDTH == DF_MAX_WIDTH, "kernel width limit matches the header");
+static_assert(dfk::GEMM_PLAN_128x128 == DF_GEMM_T128x128 && dfk::GEMM_PLAN_128x256 == DF_GEMM_T128x256 &&
+                  dfk::GEMM_PLAN_256x256 == DF_GEMM_T256x256 &&
+                  dfk::GEMM_PLAN_256x256_LDS == DF_GEMM_T256x256_LDS &&
+                  dfk::GEMM_PLAN_TILE_MASK == DF_GEMM_TILE_MASK &&
+                  dfk::GEMM_PLAN_Q8_IN_GEMM == DF_GEMM_Q8_IN_GEMM &&
+                  dfk::GEMM_PLAN_DEQUANT_FIRST == DF_GEMM_Q8_DEQUANT_FIRST,
+              "GEMM plan codes match the header");
 
 #include <atomic>
 #include <chrono>
@@ -1656,13 +1663,21 @@ df_status df_time_kernel(df_model* m, int32_t kernel, int32_t reps, double* mean
     if (kernel == DF_K_STEP && !m->step_on)
         return set_err(m, DF_ERR_UNSUPPORTED_OP,
                        "df_time_kernel: this model runs its decode step as separate launches");
+    // The attention launch appends this step's K / V row at kv_len: on a full
+    // cache that row is live, so the replay is refused rather than clamped.
+    if ((kernel == DF_K_ATTN || kernel == DF_K_STEP) && m->kv_len >= m->cfg.max_ctx)
+        return set_err(m, DF_ERR_CONTEXT_FULL,
+                       fmt("df_time_kernel: the cache is full (kv_len %d == max_ctx); the replay "
+                           "would overwrite its last row", m->kv_len));
     const bool per_layer = kernel != DF_K_EMBED && kernel != DF_K_LOGITS && kernel != DF_K_ARGMAX &&
                            kernel != DF_K_STEP;
     const int nl = per_layer ? m->cfg.n_layers : 1;
     if (nl == 0) return set_err(m, DF_ERR_INVALID_ARGUMENT, "df_time_kernel: no layers");
-    const int splits = attn_splits(m->kv_len < m->cfg.max_ctx ? m->kv_len : m->cfg.max_ctx - 1);
-    hipError_t r = launch_set_state(m->state, m->kv_len < m->cfg.max_ctx ? m->kv_len : m->cfg.max_ctx - 1,
-                                    0, 0, m->stream);
+    // position of the replayed step: kv_len (the attention classes need a
+    // free row there); the other classes only read it
+    const int pos = m->kv_len < m->cfg.max_ctx ? m->kv_len : m->cfg.max_ctx - 1;
+    const int splits = attn_splits(pos);
+    hipError_t r = launch_set_state(m->state, pos, 0, 0, m->stream);
     if (r == hipSuccess) r = hipEventRecord(m->ev0, m->stream);
     for (int rep = 0; rep < reps && r == hipSuccess; ++rep)
         for (int l = 0; l < nl && r == hipSuccess; ++l)
@@ -1687,9 +1702,11 @@ df_status df_time_prefill(df_model* m, int32_t kernel, int32_t rows, int32_t rep
 {
     if (!m || !mean_us || reps <= 0 || kernel < DF_K_PF_QKV || kernel > DF_K_PF_DOWN)
         return DF_ERR_INVALID_ARGUMENT;
-    if (rows < 1 || rows > m->cfg.max_ctx)
+    if (rows < 1 || rows > m->cfg.max_ctx - m->kv_len)
         return set_err(m, DF_ERR_INVALID_ARGUMENT,
-                       fmt("df_time_prefill: rows = %d: expected 1..%d", rows, m->cfg.max_ctx));
+                       fmt("df_time_prefill: rows = %d: expected 1..%d (max_ctx %d - kv_len %d: the "
+                           "replay writes cache rows past kv_len only)",
+                           rows, m->cfg.max_ctx - m->kv_len, m->cfg.max_ctx, m->kv_len));
     if (m->cfg.n_layers == 0) return set_err(m, DF_ERR_INVALID_ARGUMENT, "df_time_prefill: no layers");
     if (!bulk_supported(m))
         return set_err(m, DF_ERR_UNSUPPORTED_OP, "df_time_prefill: bulk prefill needs f16 or 8-bit weights");
@@ -1713,7 +1730,7 @@ df_status df_time_prefill(df_model* m, int32_t kernel, int32_t rows, int32_t rep
     if (r == hipSuccess) r = hipEventRecord(m->ev0, m->stream);
     const int nl = c.n_layers;
     for (int rep = 0; rep < reps && r == hipSuccess; ++rep)
-        for (int l = 0; l < nl && r == hipSuccess; ++l) r = pf_launch(m, b, kernel, l, rows, 0);
+        for (int l = 0; l < nl && r == hipSuccess; ++l) r = pf_launch(m, b, kernel, l, rows, m->kv_len);
     if (r == hipSuccess) r = hipEventRecord(m->ev1, m->stream);
     if (r == hipSuccess) r = hipEventSynchronize(m->ev1);
     float ms = 0.f;
@@ -1724,6 +1741,29 @@ df_status df_time_prefill(df_model* m, int32_t kernel, int32_t rows, int32_t rep
     }
     m->ev_kind = 0;
     *mean_us = double(ms) * 1e3 / double(reps * nl);
+    return DF_OK;
+}
+
+df_status df_prefill_plan(const df_model* m, int32_t rows, int32_t* plan)
+{
+    if (!m || !plan || rows < 1) return DF_ERR_INVALID_ARGUMENT;
+    const df_config& c = m->cfg;
+    if (c.n_layers == 0 || !bulk_supported(m)) {
+        for (int i = 0; i < 4; ++i) plan[i] = 0;
+        return DF_OK;
+    }
+    const int64_t qd = int64_t(c.n_heads) * c.head_dim, kvd = int64_t(c.n_kv_heads) * c.head_dim;
+    const bool q8 = m->layers[0].wqkv.scales != nullptr;
+    // 8-bit weights from PF_DEQUANT_MIN_ROWS rows on: converted to f16 first
+    // (pf_buffers / pf_launch), then the f16 GEMMs
+    const bool first = q8 && rows >= PF_DEQUANT_MIN_ROWS;
+    const bool in_gemm = q8 && !first;
+    const bool gemma = c.arch == DF_ARCH_GEMMA3;
+    const int64_t N[4] = {qd + 2 * kvd, c.d_model, c.ffn_dim, c.d_model};
+    const int mode[4] = {GEMM_STORE_F32, gemma ? GEMM_STORE_F32 : GEMM_ADD_F32, GEMM_SWIGLU_F16,
+                         gemma ? GEMM_STORE_F32 : GEMM_ADD_F32};
+    for (int i = 0; i < 4; ++i)
+        plan[i] = gemm_plan(rows, N[i], mode[i], in_gemm) | (first ? GEMM_PLAN_DEQUANT_FIRST : 0);
     return DF_OK;
 }
 

@@ -288,21 +288,38 @@ df_status df_profile_read(df_model* m, int32_t kernel, int64_t* launches,
  * the model's stream between one pair of HIP events, with no other work in
  * between. Activation buffers and the cache row at kv_len are overwritten
  * (the next df_forward / df_generate starts from its own inputs as always).
- * DF_K_STEP needs a model that runs the persistent step (else
- * DF_ERR_UNSUPPORTED_OP). Synchronises. */
+ * The row at kv_len is free, so the cached context stays intact; on a full
+ * cache (kv_len == max_ctx) DF_K_ATTN and DF_K_STEP return
+ * DF_ERR_CONTEXT_FULL. DF_K_STEP needs a model that runs the persistent step
+ * (else DF_ERR_UNSUPPORTED_OP). Synchronises. */
 df_status df_time_kernel(df_model* m, int32_t kernel, int32_t reps,
                          double* mean_us);
 
 /* Mean device time of one layer's launches of a bulk-prefill class
- * (DF_K_PF_QKV .. DF_K_PF_DOWN) for `rows` rows (1 .. max_ctx) at positions
- * 0..rows-1: each layer's launches in turn, `reps` times, back to back
- * between one pair of HIP events, on activation buffers filled with
- * pseudo-random values in [-1, 1) (the clocks depend on the operands). The KV cache
- * rows 0..rows-1 are overwritten (DF_K_PF_ATTN) and kv_len is left as it
- * was. Needs f16 or 8-bit block weights (else DF_ERR_UNSUPPORTED_OP).
- * Synchronises. */
+ * (DF_K_PF_QKV .. DF_K_PF_DOWN) for `rows` rows (1 .. max_ctx - kv_len) at
+ * positions kv_len .. kv_len+rows-1: each layer's launches in turn, `reps`
+ * times, back to back between one pair of HIP events, on activation buffers
+ * filled with pseudo-random values in [-1, 1) (the clocks depend on the
+ * operands). DF_K_PF_ATTN writes the cache rows kv_len .. kv_len+rows-1,
+ * which no later call reads before overwriting them, and kv_len is left as
+ * it was, so the cached context stays intact. Needs f16 or 8-bit block
+ * weights (else DF_ERR_UNSUPPORTED_OP). Synchronises. */
 df_status df_time_prefill(df_model* m, int32_t kernel, int32_t rows, int32_t reps,
                           double* mean_us);
+
+/* Debug query: the matrix-core kernels a bulk prefill of `rows` rows runs
+ * for the q/k/v, o, gate/up and down GEMMs (plan[0..3]), each a tile code
+ * DF_GEMM_* with the DF_GEMM_Q8_* flags or'ed in; all 0 when the model has
+ * no layers or no bulk path (f32 weights). The same host function picks the
+ * kernel at launch, so tests can check which kernels a run exercises. */
+#define DF_GEMM_T128x128 1        /* 4 waves, operands staged through registers */
+#define DF_GEMM_T128x256 2        /* 8 waves, staged through registers */
+#define DF_GEMM_T256x256 3        /* 8 waves, staged through registers */
+#define DF_GEMM_T256x256_LDS 4    /* 8 waves, operand tiles loaded straight into LDS */
+#define DF_GEMM_TILE_MASK 15
+#define DF_GEMM_Q8_IN_GEMM 16     /* 8-bit weight tiles dequantised on their way into LDS */
+#define DF_GEMM_Q8_DEQUANT_FIRST 32 /* 8-bit matrices converted to f16 before the GEMM */
+df_status df_prefill_plan(const df_model* m, int32_t rows, int32_t* plan);
 
 #ifdef __cplusplus
 }

@@ -4,7 +4,7 @@ f16 and 8-bit block weights).
 Bulk prefill must give the same result as token-by-token within epsilon
 (page "Execution contract", "Forward phase"). The GEMM operands are rounded
 to f16, so the bar is rel-L2 <= 5e-3 on logits against the oracle, with the
-greedy token identical unless the oracle's top-2 gap is a near-tie. Cases
+greedy token identical. Cases
 span several 128-row tiles with a ragged tail, prefill on top of an
 existing cache (absolute positions), and the decode steps that follow.
 """
@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import synth
-from parity import check_steps, first_argmax, near_tie, rel_l2
+from parity import first_argmax, rel_l2
 
 pytestmark = pytest.mark.gpu
 TOL = 5e-3
@@ -44,11 +44,12 @@ def oracle_run(cfg, W, chunks, max_ctx):
 
 
 def check_logits(got, ref, what):
+    """rel-L2 within the bulk tolerance and the greedy token identical (a
+    seed that lands on a genuine near-tie is replaced, not exempted)."""
     e = rel_l2(got, ref)
     say(f"  {what}: rel-L2 {e:.2e}")
     assert e <= TOL, f"{what}: rel-L2 {e:.3e}"
-    if first_argmax(got) != first_argmax(ref):
-        assert near_tie(ref, TOL), f"{what}: argmax differs off a near-tie"
+    assert first_argmax(got) == first_argmax(ref), f"{what}: greedy token differs"
 
 
 def check_kv(m, om, cfg, n, tol=TOL):

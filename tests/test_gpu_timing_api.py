@@ -69,17 +69,19 @@ def test_time_kernel_then_forward_matches(dfa, kernel):
 def test_time_prefill_then_bulk_matches(dfa, kernel):
     cfg = synth.config("tiny", arch="qwen3", wdtype="f16", max_ctx=160)
     W = synth.make_weights(cfg)
-    say(f"[tiny qwen3 f16] df_time_prefill({kernel}, 100 rows), then bulk 30 on a 20-token context")
+    say(f"[tiny qwen3 f16] df_time_prefill({kernel}, 100 rows) on a 20-token context, then bulk 30")
     toks = synth.make_prompt(cfg, 50)
     m = dfa.Model(cfg, W)
     m.forward(toks[:20], logits=False)
+    before = [m.read_kv(layer, which, 0, 20) for layer in range(cfg["n_layers"]) for which in (0, 1)]
     us = dfa.df_time_prefill(m.h, kernel, 100, 2)
     assert us > 0.0
     assert m.kv_len == 20
-    # the replays overwrote cache rows 0..99: restore the context, then
-    # check a bulk call on top of it against the oracle
-    m.reset()
-    m.forward(toks[:20], logits=False)
+    # the replays wrote only rows past kv_len: the context is intact, bit for bit
+    after = [m.read_kv(layer, which, 0, 20) for layer in range(cfg["n_layers"]) for which in (0, 1)]
+    for a, b in zip(before, after):
+        assert np.array_equal(a, b)
+    # a bulk call on top of the kept context against the oracle
     got = m.forward(toks[20:]).cpu().numpy()
     om = oracle.Model(cfg, W)
     om.forward(toks[:-1], logits=False)
@@ -87,5 +89,25 @@ def test_time_prefill_then_bulk_matches(dfa, kernel):
     e = rel_l2(got, ref)
     say(f"  bulk 30 on 20: rel-L2 {e:.2e}")
     assert e <= 5e-3
+    # more rows than the cache has free past kv_len: refused
+    with pytest.raises(dfa.DecFwdError) as ei:
+        dfa.df_time_prefill(m.h, kernel, 160 - 50 + 1, 1)
+    assert ei.value.status == "INVALID_ARGUMENT"
     om.close()
+    m.close()
+
+
+def test_time_kernel_refuses_attention_on_a_full_cache(dfa):
+    cfg = synth.config("tiny", arch="llama", wdtype="f16", max_ctx=24)
+    W = synth.make_weights(cfg)
+    say("[tiny llama f16] df_time_kernel(attn) on a full cache is refused; the context stays intact")
+    m = dfa.Model(cfg, W)
+    m.forward(synth.make_prompt(cfg, 24), logits=False)
+    assert m.kv_len == 24
+    before = m.read_kv(0, 0, 0, 24)
+    with pytest.raises(dfa.DecFwdError) as ei:
+        dfa.df_time_kernel(m.h, "attn", 1)
+    assert ei.value.status == "CONTEXT_FULL"
+    assert dfa.df_time_kernel(m.h, "gate_up", 1) > 0.0  # classes that only read the position
+    assert np.array_equal(before, m.read_kv(0, 0, 0, 24))
     m.close()
