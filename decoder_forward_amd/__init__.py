@@ -39,7 +39,7 @@ EXPORTS = ("df_load", "df_forward", "df_generate", "df_reset_kv_cache",
            "df_free", "df_last_error", "df_get_timings", "df_kv_length",
            "df_argmax", "df_read_kv", "df_write_kv", "df_stream",
            "df_profile", "df_profile_read", "df_time_kernel", "df_session",
-           "df_time_prefill", "df_prefill_plan")
+           "df_time_prefill", "df_prefill_plan", "df_forward_noalloc")
 KERNELS = {"embed": 0, "qkv": 1, "attn": 2, "o": 3, "gate_up": 4, "down": 5,
            "logits": 6, "argmax": 7, "attn_merge": 8, "step": 9}
 PREFILL_KERNELS = {"qkv": 10, "attn": 11, "o": 12, "gate_up": 13, "down": 14}
@@ -104,6 +104,7 @@ def lib() -> C.CDLL:
     L.df_load.argtypes = [P(df_config), P(df_tensor), C.c_size_t, P(df_options), P(vp)]
     L.df_session.argtypes = [vp, i32, P(df_options), P(vp)]
     L.df_forward.argtypes = [vp, P(i32), i32, vp]
+    L.df_forward_noalloc.argtypes = [vp, P(i32), i32, vp]
     L.df_generate.argtypes = [vp, i32, i32, vp, vp]
     L.df_reset_kv_cache.argtypes = [vp]
     L.df_free.argtypes = [P(vp)]
@@ -205,6 +206,15 @@ def df_forward(h, tokens, logits=None) -> None:
     ptr = logits.data_ptr() if logits is not None else None
     _check(lib().df_forward(h, toks.ctypes.data_as(C.POINTER(C.c_int32)),
                             toks.size, ptr), h)
+
+
+def df_forward_noalloc(h, tokens, logits=None) -> None:
+    """df_forward through the decode kernels with the step's activations in
+    the library's fixed device array: the call allocates nothing."""
+    toks = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32).reshape(-1))
+    ptr = logits.data_ptr() if logits is not None else None
+    _check(lib().df_forward_noalloc(h, toks.ctypes.data_as(C.POINTER(C.c_int32)),
+                                    toks.size, ptr), h)
 
 
 def df_generate(h, first_token: int, n_steps: int, tokens_out, logits=None) -> None:

@@ -29,6 +29,7 @@ static_assert(dfk::GEMM_PLAN_128x128 == DF_GEMM_T128x128 && dfk::GEMM_PLAN_128x2
 #include <cstring>
 #include <map>
 #include <memory>
+#include <mutex>
 #include <string>
 #include <utility>
 #include <vector>
@@ -137,6 +138,47 @@ struct Layer {
     bool local = false;        // attends through the sliding window, local rope theta
 };
 
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Fixed staging for df_forward_noalloc: the decode step's activations (x,
+// q|k|v, attention output, gated FFN activation, gemma3's norm input) in one
+// file-scope device array, so that the call allocates nothing. Each GPU the
+// library runs on holds its own copy until the process ends. In host code
+// `scratch` names a host-side stand-in, not device memory: host code uses
+// only the per-device address hipGetSymbolAddress gives (noalloc_scratch).
+// ---------------------------------------------------------------------------
+constexpr size_t NOALLOC_SCRATCH_BYTES = DF_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch_addr;  // device ordinal -> address of its `scratch`
+
+// Once per device, with that device current: the device address of the
+// array. Called by df_load.
+bool noalloc_scratch_init(int dev, std::string* err)
+{
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch_addr.count(dev)) return true;
+    void* p = nullptr;
+    const hipError_t r = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (r != hipSuccess || !p) {
+        (void)hipGetLastError();
+        *err = fmt("backend init: hipGetSymbolAddress of the fixed staging array failed on device %d (%s)",
+                   dev, hipGetErrorString(r));
+        return false;
+    }
+    g_scratch_addr[dev] = p;
+    return true;
+}
+
+void* noalloc_scratch(int dev)
+{
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    auto it = g_scratch_addr.find(dev);
+    return it == g_scratch_addr.end() ? nullptr : it->second;
+}
 }  // namespace
 
 struct df_model {
@@ -1275,6 +1317,7 @@ df_status df_load(const df_config* cfg, const df_tensor* tensors, size_t n_tenso
         g_load_error = fmt("backend init: hipSetDevice(%d) failed", dev);
         return DF_ERR_BACKEND_INIT;
     }
+    if (!noalloc_scratch_init(dev, &g_load_error)) return DF_ERR_BACKEND_INIT;
 
     df_model* m = new (std::nothrow) df_model();
     if (!m) {
@@ -1428,6 +1471,84 @@ df_status df_forward(df_model* m, const int32_t* tokens, int32_t n, float* logit
     if (st == DF_OK) st = chk;
     if (st == DF_OK) m->n_forward++;
     return st;
+}
+
+df_status df_forward_noalloc(df_model* m, const int32_t* tokens, int32_t n, float* logits_dev)
+{
+    if (!m) return DF_ERR_INVALID_ARGUMENT;
+    BusyGuard guard(m);
+    if (!guard.ok) return DF_ERR_BUSY;
+    const df_config& c = m->cfg;
+    if (!tokens || n <= 0)
+        return set_err(m, DF_ERR_INVALID_ARGUMENT, fmt("df_forward_noalloc: tokens %s, n = %d",
+                                                       tokens ? "given" : "NULL", n));
+    if (int64_t(m->kv_len) + n > c.max_ctx)
+        return set_err(m, DF_ERR_CONTEXT_FULL,
+                       fmt("df_forward_noalloc: %d positions in the cache + %d new > max_ctx %d",
+                           m->kv_len, n, c.max_ctx));
+    for (int32_t i = 0; i < n; ++i)
+        if (tokens[i] < 0 || tokens[i] >= c.vocab)
+            return set_err(m, DF_ERR_INVALID_ARGUMENT,
+                           fmt("df_forward_noalloc: token %d at index %d outside [0, %d)", tokens[i], i,
+                               c.vocab));
+    if (m->prof_kernel >= 0)
+        return set_err(m, DF_ERR_INVALID_ARGUMENT,
+                       "df_forward_noalloc: a kernel class is being profiled (df_profile), which creates "
+                       "events; turn profiling off first");
+    // The step's activations, each 256-byte aligned, carved from the fixed array.
+    const size_t qd = size_t(c.n_heads) * c.head_dim, kvd = size_t(c.n_kv_heads) * c.head_dim;
+    const bool gemma = c.arch == DF_ARCH_GEMMA3;
+    auto up = [](size_t bytes) { return (bytes + 255) & ~size_t(255); };
+    const size_t sizes[5] = {size_t(c.d_model) * 4, (qd + 2 * kvd) * 4, qd * 4, size_t(c.ffn_dim) * 4,
+                             gemma ? size_t(c.d_model) * 4 + 4 : 0};
+    size_t need = 0;
+    for (size_t b : sizes) need += up(b);
+    if (need > NOALLOC_SCRATCH_BYTES)
+        return set_err(m, DF_ERR_UNSUPPORTED_OP,
+                       fmt("df_forward_noalloc: the decode step's activations take %zu bytes (d_model %d, "
+                           "q|k|v %zu, attention %zu, ffn %d floats); the fixed array holds %zu",
+                           need, c.d_model, qd + 2 * kvd, qd, c.ffn_dim, NOALLOC_SCRATCH_BYTES));
+    char* base = static_cast<char*>(noalloc_scratch(m->device));
+    if (!base)
+        return set_err(m, DF_ERR_DEVICE, fmt("df_forward_noalloc: no fixed array address for device %d",
+                                             m->device));
+    StepBufs b{};
+    size_t off = 0;
+    float* parts[5];
+    for (int i = 0; i < 5; ++i) {
+        parts[i] = sizes[i] ? reinterpret_cast<float*>(base + off) : nullptr;
+        off += up(sizes[i]);
+    }
+    b.x = parts[0];
+    b.qkv = parts[1];
+    b.att = parts[2];
+    b.mid = parts[3];
+    b.tmp = parts[4];
+    if (hipSetDevice(m->device) != hipSuccess) {
+        (void)hipGetLastError();
+        return set_err(m, DF_ERR_DEVICE, "hipSetDevice failed");
+    }
+    collect_event_time(m);
+    (void)hipEventRecord(m->ev0, m->stream);
+    // Token by token through the decode kernels (separate launches), the
+    // same launches df_forward makes for one token.
+    hipError_t r = hipSuccess;
+    int32_t done = 0;
+    for (; done < n && r == hipSuccess; ++done) {
+        const int pos = m->kv_len + done;
+        r = launch_set_state(m->state, pos, tokens[done], 0, m->stream);
+        if (r == hipSuccess) r = launch_step(m, b, attn_splits(pos), done == n - 1 ? logits_dev : nullptr);
+    }
+    if (r != hipSuccess) {
+        (void)hipGetLastError();
+        m->kv_len += done - 1;  // the failed step's position was not completed
+        return set_err(m, DF_ERR_DEVICE, fmt("df_forward_noalloc: launch failed: %s", hipGetErrorString(r)));
+    }
+    (void)hipEventRecord(m->ev1, m->stream);
+    m->ev_kind = n == 1 ? 1 : 2;
+    m->kv_len += n;
+    m->n_forward++;
+    return DF_OK;
 }
 
 df_status df_generate(df_model* m, int32_t first_token, int32_t n_steps, int32_t* tokens_dev,

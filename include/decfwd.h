@@ -208,6 +208,28 @@ df_status df_session(const df_model* model, int32_t max_ctx, const df_options* o
 df_status df_forward(df_model* m, const int32_t* tokens, int32_t n,
                      float* logits_dev);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * result as n df_forward calls of one token each, with no allocation in the
+ * call. The n tokens run through the decode kernels one position at a time
+ * (never the bulk matrix-core path, whose buffers grow with n; never the
+ * persistent step). The activations that pass between the step's kernels
+ * live in one fixed device array of DF_NOALLOC_SCRATCH_BYTES bytes per GPU,
+ * held by the library until the process ends and shared by every call on
+ * that GPU: calls that overlap on one GPU (two models, or two sessions, on
+ * different streams) race on it and must be ordered by the caller. Nothing
+ * in the array needs clearing between calls: every value is written before
+ * it is read. A model whose step activations (d_model + q|k|v + n_heads *
+ * head_dim + ffn_dim floats, plus d_model + 1 for gemma3, each rounded up to
+ * 256 bytes) exceed the array is refused with DF_ERR_UNSUPPORTED_OP; the
+ * llama-8B shape takes 112 KiB. Also refused while df_profile is on. Other
+ * arguments and errors as df_forward: an argument error leaves kv_len
+ * unchanged; a failed launch (DF_ERR_DEVICE) leaves it at the positions
+ * completed before it. */
+#define DF_NOALLOC_SCRATCH_BYTES (256 * 1024)
+df_status df_forward_noalloc(df_model* m, const int32_t* tokens, int32_t n,
+                             float* logits_dev);
+
 /* Greedy decode on the device: step i feeds token t_i (t_0 = first_token),
  * computes the logits, takes t_{i+1} = argmax (lowest index on ties) and
  * writes it to tokens_dev[i], for i < n_steps, with no host round trip.
