@@ -270,6 +270,176 @@ def concurrent_sessions(m, cfg, ctx, max_ctx, first, args):
             "timing": "host wall clock from a common start to the last thread's device sync"}
 
 
+# The pages' only sizing figure: about 200 MB of activation pool for a 7B
+# decoder at bs=1 on their wgpu backend (page "Execution contract", "Memory
+# lifecycle", "Activations"). Context for the pool bytes reported here.
+PAGES_POOL_BYTES = 200e6
+
+
+def copy_bandwidth(gib: int = 2) -> dict:
+    """Device-to-device copy of `gib` GiB (torch copy_, 8 repetitions between
+    events): read + write bytes per second, the achievable streaming rate of
+    the box next to the 8 TB/s peak."""
+    import torch
+    n = gib * (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(8):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / 8
+    gbps = 2 * n * 4 / sec / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"gbps": round(gbps, 1), "bytes_per_copy": 2 * n * 4,
+            "how": f"torch copy_ of {gib} GiB f32 on the device, read + write bytes, mean of 8"}
+
+
+def cpu_prefill_sample(cfg: dict, S: int) -> dict:
+    """The oracle's bulk prefill rate on a bounded sample: the oracle runs a
+    bulk call token by token (bulk equals token-by-token inside it), so one
+    prompt token at context S/2 (the mean context of an S-token prompt)
+    through 2 of the layers, no logits, with the KV cache restored to S/2
+    synthetic rows, and through 0 layers; the per-token time is scaled to
+    the full layer count and S tokens."""
+    import oracle
+    import synth
+    threads = len(os.sched_getaffinity(0))
+    oracle.set_threads(threads)
+    mid = S // 2
+    c2 = dict(cfg, n_layers=2, max_ctx=mid + 4)
+    W = synth.make_weights(c2)
+    m2 = oracle.Model(c2, W)
+    for layer in range(2):
+        K, V = synth.make_kv_rows(c2, layer, mid)
+        m2.kv_write(layer, 0, 0, K)
+        m2.kv_write(layer, 1, 0, V)
+    m0 = oracle.Model(dict(c2, n_layers=0), W)
+    tok = int(synth.make_prompt(cfg, 1, stream=7)[0])
+
+    def time_one(m, kv, reps):
+        ts = []
+        for _ in range(reps):
+            m.set_kv_len(kv)
+            t = time.perf_counter()
+            m.forward([tok], logits=False)
+            ts.append(time.perf_counter() - t)
+        return min(ts)
+    time_one(m2, mid, 1)
+    t2, t0 = time_one(m2, mid, 3), time_one(m0, 0, 3)
+    per_layer = max(0.0, (t2 - t0) / 2)
+    t_tok = t0 + cfg["n_layers"] * per_layer
+    m2.close()
+    m0.close()
+    return {"value": round(1.0 / t_tok, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"one prompt token at context {mid} (the mean context of a {S}-token prompt) "
+                       f"through 2 of {cfg['n_layers']} layers without logits (best of 3), "
+                       f"0-layer time {t0 * 1e3:.1f} ms, per-layer {per_layer * 1e3:.1f} ms, scaled to "
+                       f"{cfg['n_layers']} layers; a {S}-token prefill takes about "
+                       f"{S * t_tok:.0f} s")}
+
+
+def decode_run(dfa, cfg, ctx, steps, warmup, context_from, tag):
+    """Load `cfg` (random device weights), build a context of `ctx`
+    positions, then time `steps` greedy decode steps (df_generate) between
+    HIP events on the model's stream. Returns the open model and the
+    figures."""
+    import numpy as np
+    import torch
+    import synth
+    max_ctx = ctx + max(steps, warmup) + 8
+    log(f"[bench] {tag}: generating weights on the GPU")
+    W = synth.make_weights_device(cfg)
+    torch.cuda.synchronize()
+    m = dfa.Model(cfg, W, max_ctx=max_ctx)
+    del W
+    torch.cuda.empty_cache()
+    first = int(synth.make_prompt(cfg, 1, stream=3)[0])
+    # the decode step's own activation pool, before any bulk prefill
+    m.forward([first], logits=True)
+    torch.cuda.synchronize()
+    pool_decode = m.timings()["pool_bytes"]
+    m.reset()
+    res = {"load_ms": m.timings()["load_ms"], "pool_decode_bytes": pool_decode}
+    if context_from == "prefill":
+        prompt = synth.make_prompt(cfg, ctx, stream=0)
+        m.forward(prompt[:8], logits=False)  # warm the bulk path
+        m.reset()
+        torch.cuda.synchronize()
+        m.forward(prompt, logits=True)
+        torch.cuda.synchronize()
+        res["prefill_ms"] = m.timings()["last_prefill_ms"]  # HIP events around the launches
+        res["prefill_tokens_per_s"] = ctx / (res["prefill_ms"] / 1e3)
+        log(f"[bench] {tag}: bulk prefill of {ctx} tokens: {res['prefill_ms']:.1f} ms "
+            f"({res['prefill_tokens_per_s']:.0f} tokens/s)")
+    else:
+        for layer in range(cfg["n_layers"]):
+            K, V = synth.make_kv_rows_device(cfg, layer, ctx)
+            m.write_kv(layer, 0, 0, K.cpu().numpy(), ctx)
+            m.write_kv(layer, 1, 0, V.cpu().numpy(), ctx)
+        log(f"[bench] {tag}: restored {ctx} synthetic KV positions")
+    assert m.kv_len == ctx
+    res["pool_total_bytes"] = m.timings()["pool_bytes"]
+
+    def rewind():  # kv_len back to the context; rows past it are rewritten
+        m.write_kv(0, 0, 0, np.zeros((cfg["n_kv_heads"], 0, cfg["head_dim"]), np.float32), ctx)
+
+    if warmup > 0:  # also captures the step graph
+        m.generate(first, warmup)
+    torch.cuda.synchronize()
+    rewind()
+    toks = torch.empty(steps, dtype=torch.int32, device=m.device)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(m.stream)
+    dfa.df_generate(m.h, first, steps, toks, m.logits)
+    ev1.record(m.stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dev_ms = ev0.elapsed_time(ev1)
+    total_bytes = sum(step_bytes(cfg, ctx + i) for i in range(steps))
+    res.update(value=steps / (dev_ms / 1e3), ms_per_step=dev_ms / steps,
+               achieved=total_bytes / (dev_ms / 1e3) / 1e9, wall=wall,
+               mean_step_bytes=total_bytes / steps)
+    res["hbm_frac"] = res["achieved"] / PEAK_HBM_GBPS
+    log(f"[bench] {tag}: decode {steps} steps at {ctx}..: {res['ms_per_step']:.3f} ms/step, "
+        f"{res['value']:.1f} tok/s, {res['achieved']:.0f} GB/s ({res['hbm_frac']:.1%} of 8 TB/s); "
+        f"wall {wall:.3f} s")
+    return m, res
+
+
+def extra_workloads(dfa, args) -> dict:
+    """The other timed configurations, each on its own model: 8-bit blocks at
+    contexts 1024 and 8192 (128 steps each), and the qwen3-8B shape's bulk
+    prefill of 2048 tokens followed by 64 decode steps."""
+    import synth
+    out = {}
+    cfg = synth.config("llama_8b_q8")
+    for ctx in (1024, 8192):
+        m, r = decode_run(dfa, cfg, ctx, 128, 8, "prefill", f"llama_8b_q8 ctx {ctx}")
+        m.close()
+        out[f"llama_8b_q8_ctx{ctx}"] = {
+            "decode_tokens_per_s": round(r["value"], 1), "ms_per_step": round(r["ms_per_step"], 4),
+            "achieved_hbm_gbps": round(r["achieved"], 1), "hbm_frac": round(r["hbm_frac"], 4),
+            "steps": 128, "positions": f"{ctx}..{ctx + 127}",
+            "prefill_tokens_per_s": round(r["prefill_tokens_per_s"], 1)}
+    cfg = synth.config("qwen3_8b")
+    m, r = decode_run(dfa, cfg, 2048, 64, 8, "prefill", "qwen3_8b bulk 2048")
+    m.close()
+    out["qwen3_8b_bulk2048"] = {
+        "prefill_tokens_per_s": round(r["prefill_tokens_per_s"], 1), "prefill_ms": round(r["prefill_ms"], 2),
+        "decode_tokens_per_s": round(r["value"], 1), "ms_per_step": round(r["ms_per_step"], 4),
+        "hbm_frac": round(r["hbm_frac"], 4), "steps": 64, "positions": "2048..2111"}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -283,8 +453,8 @@ def main():
                     help="build the context by bulk prefill of a uniform-random prompt "
                          "(default, timed) or by writing synthetic KV rows")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--persistent-step", action="store_true",
-                    help="one persistent launch per step instead of one per operation class")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the 8-bit and qwen3-8B workloads timed after the headline")
     ap.add_argument("--sessions", type=int, default=0, metavar="N",
                     help="also time N conversations (df_session) decoding at once, "
                          "one host thread and stream each, same context")
@@ -306,7 +476,6 @@ def main():
               f"several GPUs is not implemented).", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
     import decoder_forward_amd as dfa
     import synth
@@ -315,64 +484,9 @@ def main():
 
     cfg = synth.config(args.workload)
     ctx = args.context
-    max_ctx = ctx + max(args.steps, args.warmup) + 8
-    log(f"[bench] {args.workload}: generating weights on the GPU")
-    W = synth.make_weights_device(cfg)
-    torch.cuda.synchronize()
-    m = dfa.Model(cfg, W, max_ctx=max_ctx, persistent_step=args.persistent_step)
-    del W
-    torch.cuda.empty_cache()
-    log(f"[bench] loaded in {m.timings()['load_ms']:.0f} ms")
-
-    prefill_tps = None
-    if args.context_from == "prefill":
-        prompt = synth.make_prompt(cfg, ctx, stream=0)
-        m.forward(prompt[:8], logits=False)  # warm the bulk path
-        m.reset()
-        torch.cuda.synchronize()
-        t = time.perf_counter()
-        m.forward(prompt, logits=True)
-        torch.cuda.synchronize()
-        prefill_wall = time.perf_counter() - t
-        prefill_s = m.timings()["last_prefill_ms"] / 1e3  # HIP events around the launches
-        prefill_tps = ctx / prefill_s
-        log(f"[bench] bulk prefill of {ctx} tokens: {prefill_s * 1e3:.1f} ms device, "
-            f"{prefill_wall * 1e3:.1f} ms wall ({prefill_tps:.0f} tokens/s)")
-    else:
-        for layer in range(cfg["n_layers"]):
-            K, V = synth.make_kv_rows_device(cfg, layer, ctx)
-            m.write_kv(layer, 0, 0, K.cpu().numpy(), ctx)
-            m.write_kv(layer, 1, 0, V.cpu().numpy(), ctx)
-        log(f"[bench] restored {ctx} synthetic KV positions")
-    assert m.kv_len == ctx
-    first = int(synth.make_prompt(cfg, 1, stream=3)[0])
-
-    def rewind():  # kv_len back to the context; rows past it are rewritten
-        m.write_kv(0, 0, 0, np.zeros((cfg["n_kv_heads"], 0, cfg["head_dim"]), np.float32), ctx)
-
-    # warmup (also captures the step graph), then rewind to the context
-    if args.warmup > 0:
-        m.generate(first, args.warmup)
-    torch.cuda.synchronize()
-    rewind()
-
-    toks = torch.empty(args.steps, dtype=torch.int32, device=m.device)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(m.stream)
-    dfa.df_generate(m.h, first, args.steps, toks, m.logits)
-    ev1.record(m.stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    dev_ms = ev0.elapsed_time(ev1)
-    ms_per_step = dev_ms / args.steps
-    value = args.steps / (dev_ms / 1e3)
-    total_bytes = sum(step_bytes(cfg, ctx + i) for i in range(args.steps))
-    achieved = total_bytes / (dev_ms / 1e3) / 1e9
-    log(f"[bench] decode {args.steps} steps: {ms_per_step:.3f} ms/step, {value:.1f} tok/s, "
-        f"{achieved:.0f} GB/s ({achieved / PEAK_HBM_GBPS:.1%} of 8 TB/s); wall {wall:.3f} s")
+    m, run = decode_run(dfa, cfg, ctx, args.steps, args.warmup, args.context_from, args.workload)
+    value, ms_per_step, achieved = run["value"], run["ms_per_step"], run["achieved"]
+    prefill_tps = run.get("prefill_tokens_per_s")
 
     # Per-kernel mean launch time in the same launch configuration: one
     # step's launches of a class replayed back to back between two HIP
@@ -384,23 +498,37 @@ def main():
         n = per_step.get(k, cfg["n_layers"])
         kernels[k] = {"launches_per_step": n, "mean_us": round(us, 2),
                       "ms_per_step": round(us * n / 1e3, 4)}
+    log(f"[bench] kernels: {json.dumps(kernels)}")
     m.reset()  # the prefill replays write cache rows past kv_len: all S of them
     prefill_kernels, pf_roof = prefill_classes(dfa, m, cfg, ctx) if args.context_from == "prefill" else ({}, None)
+
     gu = kernels["gate_up"]
-    gu_bytes = gate_up_launch_bytes(cfg)
-    gu_gbps = gu_bytes / (gu["mean_us"] * 1e-6) / 1e9
-    log(f"[bench] kernels: {json.dumps(kernels)}")
+    traffic = measured_traffic() if args.workload == "llama_8b" else None
+    dom = {"kernel": "gate/up matvec (rms_norm + gate,up matmul + silu * up)",
+           "bytes": gate_up_launch_bytes(cfg), "us": gu["mean_us"], "traffic": traffic}
+    dom_gbps = dom["bytes"] / (dom["us"] * 1e-6) / 1e9
 
-    sessions = concurrent_sessions(m, cfg, ctx, max_ctx, first, args) if args.sessions > 0 else None
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        log("[bench] CPU oracle baseline (bounded sample)")
-        cpu = cpu_baseline(cfg, ctx)
-        log(f"[bench] cpu baseline: {cpu}")
-
-    traffic = measured_traffic() if args.workload == "llama_8b" and not args.persistent_step else None
+    sessions = concurrent_sessions(m, cfg, ctx, ctx + max(args.steps, args.warmup) + 8, 
+                                   int(synth.make_prompt(cfg, 1, stream=3)[0]), args) \
+        if args.sessions > 0 else None
     t = m.timings()
+    m.close()
+    torch.cuda.empty_cache()
+
+    copy = copy_bandwidth()
+    log(f"[bench] device copy: {copy['gbps']:.0f} GB/s (read + write)")
+    extra = None if args.no_extra else extra_workloads(dfa, args)
+
+    cpu = cpu_pf = None
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline (bounded samples)")
+        cpu = cpu_baseline(cfg, ctx)
+        log(f"[bench] cpu decode baseline: {cpu}")
+        cpu_pf = cpu_prefill_sample(cfg, ctx)
+        log(f"[bench] cpu prefill baseline: {cpu_pf}")
+        cpu["prefill"] = cpu_pf
+
+    traffic = dom["traffic"]
     report = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -424,35 +552,44 @@ def main():
             "context": ctx,
             "context_from": args.context_from,
             "weight_dtype": cfg["wdtype"],
+            "decode_launch": "one launch per operation class, captured in a HIP graph",
         },
         "achieved_hbm_gbps": round(achieved, 1),
         "hbm_frac": round(achieved / PEAK_HBM_GBPS, 4),
+        "copy_bandwidth_gbps": copy["gbps"],
+        "hbm_frac_of_copy": round(achieved / copy["gbps"], 4),
         "prefill_tokens_per_s": round(prefill_tps, 1) if prefill_tps else None,
         "roofline": {
             "bound": "hbm",
-            "kernel": "gate/up matvec (rms_norm + gate,up matmul + silu * up)",
-            "achieved": round(gu_gbps, 1),
+            "kernel": dom["kernel"],
+            "achieved": round(dom_gbps, 1),
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
-            "frac": round(gu_gbps / PEAK_HBM_GBPS, 4),
+            "frac": round(dom_gbps / PEAK_HBM_GBPS, 4),
             "traffic": round(traffic["fetch"] + traffic["write"]) if traffic else None,
             "traffic_read_write": ([round(traffic["fetch"]), round(traffic["write"])]
                                    if traffic else None),
-            "bytes_per_launch": gu_bytes,
-            "mean_launch_us": gu["mean_us"],
-            "timing": (f"back-to-back replay of one step's {cfg['n_layers']} launches x 8, "
+            "bytes_per_launch": dom["bytes"],
+            "mean_launch_us": dom["us"],
+            "timing": ("back-to-back replay of one step's launches of the kernel x 8, "
                        "HIP events on the library's stream"),
+            "step_frac": round(achieved / PEAK_HBM_GBPS, 4),
         },
         "kernels": kernels,
         "prefill_roofline": pf_roof,
         "prefill_kernels": prefill_kernels,
+        "extra_workloads": extra,
         "sessions": sessions,
         "cpu_baseline": cpu,
         "memory": {"weight_bytes": t["weight_bytes"], "kv_bytes": t["kv_bytes"],
-                   "activation_pool_bytes": t["pool_bytes"]},
+                   "activation_pool_bytes": t["pool_bytes"],
+                   "activation_pool_decode_bytes": run["pool_decode_bytes"],
+                   "activation_pool_prefill_bytes": run["pool_total_bytes"] - run["pool_decode_bytes"],
+                   "pages_pool_bytes_context": PAGES_POOL_BYTES,
+                   "pages_pool_note": ("the pages' one sizing figure: about 200 MB of activation pool "
+                                       "for a 7B decoder at bs=1 on their wgpu backend")},
     }
     print(json.dumps(report), flush=True)
-    m.close()
 
 
 if __name__ == "__main__":

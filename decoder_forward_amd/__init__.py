@@ -41,13 +41,11 @@ EXPORTS = ("df_load", "df_forward", "df_generate", "df_reset_kv_cache",
            "df_profile", "df_profile_read", "df_time_kernel", "df_session",
            "df_time_prefill", "df_prefill_plan", "df_forward_noalloc")
 KERNELS = {"embed": 0, "qkv": 1, "attn": 2, "o": 3, "gate_up": 4, "down": 5,
-           "logits": 6, "argmax": 7, "attn_merge": 8, "step": 9}
+           "logits": 6, "argmax": 7, "attn_merge": 8}
 PREFILL_KERNELS = {"qkv": 10, "attn": 11, "o": 12, "gate_up": 13, "down": 14}
 # df_prefill_plan tile codes and flags.
 GEMM_TILES = {1: "128x128", 2: "128x256", 3: "256x256", 4: "256x256_lds"}
 DF_GEMM_TILE_MASK, DF_GEMM_Q8_IN_GEMM, DF_GEMM_Q8_DEQUANT_FIRST = 15, 16, 32
-# df_options.flags: every decode step as one persistent launch (opt-in).
-DF_FLAG_PERSISTENT_STEP = 1
 
 
 class DecFwdError(RuntimeError):
@@ -84,8 +82,7 @@ class df_timings(C.Structure):
     _fields_ = [("load_ms", C.c_double), ("last_prefill_ms", C.c_double),
                 ("last_step_ms", C.c_double), ("n_forward", C.c_int64),
                 ("weight_bytes", C.c_int64), ("kv_bytes", C.c_int64),
-                ("pool_bytes", C.c_int64), ("persistent_step", C.c_int32),
-                ("step_blocks", C.c_int32)]
+                ("pool_bytes", C.c_int64)]
 
 
 _lib = None
@@ -322,7 +319,7 @@ class Model:
     code before and after sees the results in order."""
 
     def __init__(self, cfg: dict, weights: dict | None, max_ctx: int | None = None,
-                 device: int = 0, persistent_step: bool = False, _base=None):
+                 device: int = 0, _base=None):
         import torch
         self._torch = torch
         self.cfg = dict(cfg)
@@ -335,8 +332,7 @@ class Model:
             self.h = df_session(_base.h, self.cfg["max_ctx"], stream=self.stream.cuda_stream)
         else:
             self.h = df_load(self.cfg, weights, stream=self.stream.cuda_stream,
-                             device=device,
-                             flags=DF_FLAG_PERSISTENT_STEP if persistent_step else 0)
+                             device=device)
         self.logits = torch.empty(self.cfg["vocab"], dtype=torch.float32,
                                   device=self.device)
 

@@ -15,7 +15,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdecfwd.so")
-SOURCES = ["runtime.hip", "decode.hip", "decode_persistent.hip", "prefill.hip"]
+SOURCES = ["runtime.hip", "decode.hip", "prefill.hip"]
 
 
 def hipcc() -> str:

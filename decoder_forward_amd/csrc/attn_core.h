@@ -1,5 +1,5 @@
-// attn_core.h — decode attention for one (KV head, row range) item, shared
-// by the separate attention kernel and the persistent step kernel.
+// attn_core.h — decode attention for one (KV head, row range) item, and the
+// merge of the partial results of one KV head's items.
 //
 // Page "Local inference and architectures", "The format" (the attention
 // step of the step list): for each query head j of KV head g,
@@ -27,7 +27,7 @@
 //
 // Result: with `out` set (the item covers every row) the normalised output
 // of the G heads; otherwise the partial (sum_t e^{s_t - M} v_t, M, sum_t
-// e^{s_t - M}) per head, merged across items by attn_merge_group.
+// e^{s_t - M}) per head, merged across items by the combine kernel.
 #pragma once
 
 #include "device_common.h"
@@ -85,8 +85,60 @@ __device__ inline void load_row_slice(const float* p, int l16, float (&v)[N])
     }
 }
 
-template <int HD, int G, int NW, int ITER, bool DBUF, bool COH>
+// The lane's K / V registers for one sweep of ITER row groups.
+template <int HD, int ITER>
+struct AttnRows {
+    float k[ITER][HD / 16];
+    float v[ITER][HD / 16];
+};
+
+// Row t of sweep s for lane group rg of wave w (see the work layout above).
+template <int NW, int ITER>
+__device__ inline int attn_row(const AttnItem& a, int s, int w, int it, int rg)
+{
+    return a.pos0 + s * (NW * 4 * ITER) + w * (4 * ITER) + it * 4 + rg;
+}
+
+// Loads of sweep s into r: the cache rows below min(pos1, p) it covers.
+// Every load is issued: a row past that bound reads the bound's last row (or
+// row 0), a valid address, and is replaced when consumed (row p by this
+// step's k and v, rows past it by zeros), so that no wait on these loads is
+// needed before the rows are consumed (a branch or a select on the loaded
+// values here would make the compiler wait for them at once). Needs only the
+// item's rows and cache pointers, so a caller may issue the first sweep
+// before the q / k / v of this step exist.
+template <int HD, int NW, int ITER>
+__device__ inline void attn_load(const AttnItem& a, int s, int tid, AttnRows<HD, ITER>& r)
+{
+    constexpr int DPL = HD / 16;
+    const int lane = tid & (WAVE - 1);
+    const int w = tid >> 6;
+    const int rg = lane >> 4;
+    const int l16 = lane & 15;
+    const int last = max(min(a.pos1, a.p) - 1, 0);
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+        const int t = min(attn_row<NW, ITER>(a, s, w, it, rg), last);
+        load_row_slice<DPL>(a.kc + int64_t(t) * HD, l16, r.k[it]);
+        load_row_slice<DPL>(a.vc + int64_t(t) * HD, l16, r.v[it]);
+    }
+}
+
+template <int HD, int G, int NW, int ITER, bool DBUF>
+__device__ void attn_run(const AttnItem& a, float* lds, int tid, AttnRows<HD, ITER>& first);
+
+// The whole item: first sweep's loads, then attn_run.
+template <int HD, int G, int NW, int ITER, bool DBUF>
 __device__ void attn_core(const AttnItem& a, float* lds, int tid)
+{
+    AttnRows<HD, ITER> first;
+    attn_load<HD, NW, ITER>(a, 0, tid, first);
+    attn_run<HD, G, NW, ITER, DBUF>(a, lds, tid, first);
+}
+
+// The item after its first sweep's loads were issued into `first`.
+template <int HD, int G, int NW, int ITER, bool DBUF>
+__device__ void attn_run(const AttnItem& a, float* lds, int tid, AttnRows<HD, ITER>& first)
 {
     constexpr int LPR = 16;
     constexpr int RG = WAVE / LPR;               // rows per wave instruction
@@ -106,25 +158,9 @@ __device__ void attn_core(const AttnItem& a, float* lds, int tid)
     const int p = a.p;
     const bool owner = a.pos1 == p + 1;
     const int n_sweeps = (a.pos1 - a.pos0 + SW - 1) / SW;
-    const int lim = min(a.pos1, p);   // cache rows below lim are read from memory
 
-    auto row_of = [&](int s, int it) { return a.pos0 + s * SW + w * (RG * ITER) + it * RG + rg; };
-    float ka[ITER][DPL], va[ITER][DPL];
-    float kb[DBUF ? ITER : 1][DPL], vb[DBUF ? ITER : 1][DPL];
-    auto load = [&](int s, float (&kk)[ITER][DPL], float (&vv)[ITER][DPL]) {
-#pragma unroll
-        for (int it = 0; it < ITER; ++it) {
-            const int t = row_of(s, it);
-            if (t < lim) {
-                load_row_slice<DPL>(a.kc + int64_t(t) * HD, l16, kk[it]);
-                load_row_slice<DPL>(a.vc + int64_t(t) * HD, l16, vv[it]);
-            } else {
-#pragma unroll
-                for (int d = 0; d < DPL; ++d) { kk[it][d] = 0.f; vv[it][d] = 0.f; }
-            }
-        }
-    };
-    load(0, ka, va);
+    auto row_of = [&](int s, int it) { return attn_row<NW, ITER>(a, s, w, it, rg); };
+    AttnRows<HD, ITER> second;  // the next sweep's rows (DBUF only)
 
     // q of the group's heads (and, for the owner, this step's k): one wave
     // per vector, lane l holding rope pairs l, l + 64, ... (< hd/2), pair i
@@ -145,8 +181,8 @@ __device__ void attn_core(const AttnItem& a, float* lds, int tid)
             x0[r] = 0.f;
             x1[r] = 0.f;
             if (i < HALF) {
-                x0[r] = act_ld<COH>(src + i0[r]);
-                x1[r] = act_ld<COH>(src + i1[r]);
+                x0[r] = *gmem(src + i0[r]);
+                x1[r] = *gmem(src + i1[r]);
                 if (a.bias) {
                     x0[r] += *gmem(a.bias + off + i0[r]);
                     x1[r] += *gmem(a.bias + off + i1[r]);
@@ -188,7 +224,7 @@ __device__ void attn_core(const AttnItem& a, float* lds, int tid)
     if (owner) {
         const int voff = a.qd + a.kvd + a.g * HD;
         for (int i = tid; i < HD; i += NW * WAVE) {
-            float v = act_ld<COH>(a.qkv + voff + i);
+            float v = *gmem(a.qkv + voff + i);
             if (a.bias) v += *gmem(a.bias + voff + i);
             vnew[i] = v;
             *gmem(a.vc + int64_t(p) * HD + i) = v;  // append v at slot p
@@ -210,14 +246,24 @@ __device__ void attn_core(const AttnItem& a, float* lds, int tid)
         l[j] = 0.f;
     }
 
+    const int lim = min(a.pos1, p);  // rows below come from the cache
     auto consume = [&](int s, float (&kk)[ITER][DPL], float (&vv)[ITER][DPL]) {
 #pragma unroll
         for (int it = 0; it < ITER; ++it) {
-            if (row_of(s, it) == p) {
+            const int t = row_of(s, it);
+            if (t == p) {
 #pragma unroll
                 for (int d = 0; d < DPL; ++d) {
                     kk[it][d] = knew[attn_dim<DPL>(l16, d)];
                     vv[it][d] = vnew[attn_dim<DPL>(l16, d)];
+                }
+            } else if (t >= lim) {
+                // past the item: its score is masked; zero values so that
+                // the rows it was loaded from cannot reach the output
+#pragma unroll
+                for (int d = 0; d < DPL; ++d) {
+                    kk[it][d] = 0.f;
+                    vv[it][d] = 0.f;
                 }
             }
         }
@@ -254,17 +300,17 @@ __device__ void attn_core(const AttnItem& a, float* lds, int tid)
     };
     if constexpr (DBUF) {
         for (int s = 0; s < n_sweeps; s += 2) {
-            if (s + 1 < n_sweeps) load(s + 1, kb, vb);
-            consume(s, ka, va);
+            if (s + 1 < n_sweeps) attn_load<HD, NW, ITER>(a, s + 1, tid, second);
+            consume(s, first.k, first.v);
             if (s + 1 < n_sweeps) {
-                if (s + 2 < n_sweeps) load(s + 2, ka, va);
-                consume(s + 1, kb, vb);
+                if (s + 2 < n_sweeps) attn_load<HD, NW, ITER>(a, s + 2, tid, first);
+                consume(s + 1, second.k, second.v);
             }
         }
     } else {
         for (int s = 0; s < n_sweeps; ++s) {
-            if (s > 0) load(s, ka, va);
-            consume(s, ka, va);
+            if (s > 0) attn_load<HD, NW, ITER>(a, s, tid, first);
+            consume(s, first.k, first.v);
         }
     }
 
@@ -302,86 +348,14 @@ __device__ void attn_core(const AttnItem& a, float* lds, int tid)
             L = fmaf(f, sl[ww * G + j], L);
         }
         if (a.out) {
-            act_st<COH>(a.out + (a.g * G + j) * HD + d, v / L);
+            *gmem(a.out + (a.g * G + j) * HD + d) = v / L;
         } else {
-            act_st<COH>(a.part + j * HD + d, v);
+            *gmem(a.part + j * HD + d) = v;
             if (d == 0) {
-                act_st<COH>(a.part + G * HD + j, M);
-                act_st<COH>(a.part + G * HD + G + j, L);
+                *gmem(a.part + G * HD + j) = M;
+                *gmem(a.part + G * HD + G + j) = L;
             }
         }
-    }
-    __syncthreads();
-}
-
-// Merge of the partials of one KV head's items (part_g: n_items items of
-// attn_part_stride floats, in row order) into out[G][hd]: weights
-// exp(m_c - M_j), sums in item order. The maxima and sums go through LDS
-// first; each thread then owns one float4 column of the accumulators and a
-// fixed residue class of items (loaded 8 at a time, all in flight), and the
-// classes are added in order through LDS. Needs G*hd/4 <= nthreads.
-// COH as for act_ld.
-template <int HD, int G, bool COH>
-__device__ void attn_merge_group(const float* part_g, int n_items, float* out, float* lds, int tid,
-                                 int nthreads)
-{
-    constexpr int CB = 8;
-    constexpr int STRIDE = attn_part_stride(G, HD);
-    constexpr int COLS = G * HD / 4;
-    const int P = nthreads / COLS;              // threads per column
-    float* ms = lds;                            // [n_items][G]
-    float* ls = ms + n_items * G;               // [n_items][G]
-    float4* pv = reinterpret_cast<float4*>(ls + n_items * G + ((4 - (2 * n_items * G) % 4) % 4));  // [P][COLS]
-    float* pl = reinterpret_cast<float*>(pv + P * COLS);                                          // [P][G]
-    for (int i = tid; i < n_items * G; i += nthreads) {
-        const int c = i / G, j = i % G;
-        ms[i] = act_ld<COH>(part_g + c * STRIDE + G * HD + j);
-        ls[i] = act_ld<COH>(part_g + c * STRIDE + G * HD + G + j);
-    }
-    __syncthreads();
-    const int col = tid % COLS, sub = tid / COLS;
-    const int j = col * 4 / HD;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    float L = 0.f;
-    if (sub < P) {
-        float M = -INFINITY;
-        for (int c = 0; c < n_items; ++c) M = fmaxf(M, ms[c * G + j]);
-        for (int c0 = sub; c0 < n_items; c0 += P * CB) {
-            float4 x[CB];
-#pragma unroll
-            for (int b = 0; b < CB; ++b) {
-                const int c = c0 + b * P;
-                x[b] = c < n_items ? act_ld4<COH>(part_g, c * STRIDE + col * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-            }
-#pragma unroll
-            for (int b = 0; b < CB; ++b) {
-                const int c = c0 + b * P;
-                if (c < n_items) {
-                    const float f = exp2_fast(ms[c * G + j] - M);
-                    v.x = fmaf(f, x[b].x, v.x);
-                    v.y = fmaf(f, x[b].y, v.y);
-                    v.z = fmaf(f, x[b].z, v.z);
-                    v.w = fmaf(f, x[b].w, v.w);
-                    L = fmaf(f, ls[c * G + j], L);
-                }
-            }
-        }
-        pv[sub * COLS + col] = v;
-        if ((col * 4) % HD == 0) pl[sub * G + j] = L;
-    }
-    __syncthreads();
-    if (tid < COLS) {
-        float4 t = pv[col];
-        float Lt = pl[j];
-        for (int s2 = 1; s2 < P; ++s2) {
-            const float4 u = pv[s2 * COLS + col];
-            t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
-            Lt += pl[s2 * G + j];
-        }
-        act_st<COH>(out + col * 4 + 0, t.x / Lt);
-        act_st<COH>(out + col * 4 + 1, t.y / Lt);
-        act_st<COH>(out + col * 4 + 2, t.z / Lt);
-        act_st<COH>(out + col * 4 + 3, t.w / Lt);
     }
     __syncthreads();
 }

@@ -30,7 +30,7 @@ matvec_kernel(const void* __restrict__ W, const uint16_t* __restrict__ scales, M
     __shared__ float red[16];
     MvState<WT, MODE> st;
     mv_begin<WT, MODE>(W, scales, L, blockIdx.x, st, threadIdx.x);
-    mv_finish<WT, MODE, NORM, false>(scales, W, L, st, x, norm_w, eps, out, hs, red, threadIdx.x);
+    mv_finish<WT, MODE, NORM>(scales, W, L, st, x, norm_w, eps, out, hs, red, threadIdx.x);
 }
 
 template <int WT, int MODE, bool NORM>
@@ -177,7 +177,7 @@ attn_decode_kernel(AttnDecodeArgs a)
     it.pos1 = min(p + 1, lo + (split + 1) * tpw * ATTN_T);
     it.out = n_active == 1 ? a.out : nullptr;
     it.part = a.part + (int64_t(g) * ATTN_MAX_SPLIT + split) * attn_part_stride(G, HD);
-    attn_core<HD, G, NW, ATTN_T / (NW * 4), false, false>(it, lds, threadIdx.x);
+    attn_core<HD, G, NW, ATTN_T / (NW * 4), false>(it, lds, threadIdx.x);
 }
 
 // Merge of the split partials of one query head (launched after the split
@@ -397,6 +397,7 @@ MvLayout make_mv_layout(int wdtype, int64_t K, int64_t n_out, int64_t up_rows, i
     L.K = K;
     L.n_out = n_out;
     L.up_rows = up_rows;
+    L.wdtype = wdtype;
     const int64_t CH = int64_t(64) * E;
     const int64_t nchunks = (K + CH - 1) / CH;
     const int64_t upb = n_out > 0 ? (n_out + max_blocks - 1) / max_blocks : 1;
@@ -419,7 +420,8 @@ size_t mv_lds_bytes(const MvLayout& L, int mode)
 {
     const int NR = mode == MV_SWIGLU ? 2 : 1;
     const int S = 1 << L.log_s;
-    return size_t(L.K) * sizeof(float) + size_t(L.upb) * S * NR * sizeof(float);
+    return size_t(dev::mv_staged_floats(L.wdtype, L.K)) * sizeof(float) +
+           size_t(L.upb) * S * NR * sizeof(float);
 }
 
 hipError_t launch_matvec(const Weight& W, int mode, const float* x,

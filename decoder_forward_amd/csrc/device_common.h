@@ -1,5 +1,4 @@
-// device_common.h — device-side building blocks shared by the decode
-// kernels (separate launches and the persistent step kernel): 16-byte
+// device_common.h — device-side building blocks of the decode kernels: 16-byte
 // streaming loads, hand-off between work-groups of one kernel, DPP
 // reductions, and the per-lane dot product of a weight vector.
 #pragma once
@@ -11,15 +10,11 @@ namespace dev {
 
 constexpr int WAVE = 64;
 
-// Global and constant address spaces. Pointers that a kernel loads from
-// memory (rather than receives as arguments) are generic to the compiler:
+// Global address space. Pointers the compiler cannot place are generic:
 // accesses through them become flat instructions, which also count against
 // the LDS wait counter, so every LDS access would wait for all loads in
-// flight. Casting to the global address space gives global instructions;
-// a step description read through a constant-space pointer gives scalar
-// loads of its fields.
+// flight. Casting to the global address space gives global instructions.
 #define DFK_GLOBAL __attribute__((address_space(1)))
-#define DFK_CONST __attribute__((address_space(4)))
 
 template <class T>
 __device__ inline DFK_GLOBAL T* gmem(T* p)
@@ -170,20 +165,46 @@ __device__ inline uint4 load_w(const void* base, int64_t elem)
     return load16_nt(p);
 }
 
-// dot of a lane's 16-byte weight vector with hs[k .. k + Epl).
+// The activation a matvec stages in LDS is stored lane-permuted: within
+// each chunk of 64 * E values (E = Epl, one 16-byte weight load per lane),
+// value j of lane l's E sits at (j / 4) * 256 + 4 l + j % 4. A lane then
+// reads its E activations as E / 4 float4 at a 16-byte stride across the
+// wave: every LDS read instruction is free of bank conflicts (consecutive
+// 32-byte slices per lane would put four lanes of each 16 on the same
+// banks). The staged region is padded to whole chunks.
 template <int WT>
-__device__ inline float lane_dot(uint4 w, const float* hs, int64_t k, uint16_t scale_bits)
+__device__ inline int64_t lds_pos(int64_t k)
+{
+    constexpr int E = Epl<WT>::v;
+    constexpr int64_t CH = int64_t(WAVE) * E;
+    const int64_t c = k / CH, w = k - c * CH;
+    const int64_t l = w / E, j = w - l * E;
+    return c * CH + (j >> 2) * 256 + l * 4 + (j & 3);
+}
+
+// Floats of LDS the staged activation of width K takes (whole chunks).
+__host__ __device__ inline int64_t mv_staged_floats(int wdtype, int64_t K)
+{
+    const int64_t CH = int64_t(64) * (wdtype == W_F32 ? 4 : wdtype == W_F16 ? 8 : 16);
+    return (K + CH - 1) / CH * CH;
+}
+
+// dot of a lane's 16-byte weight vector with its activations: hl points at
+// the lane's first float4 in the permuted layout (chunk start + 4 lane); the
+// others follow 256 floats apart.
+template <int WT>
+__device__ inline float lane_dot(uint4 w, const float* hl, uint16_t scale_bits)
 {
     if constexpr (WT == W_F32) {
-        const float4 h = *reinterpret_cast<const float4*>(hs + k);
+        const float4 h = *reinterpret_cast<const float4*>(hl);
         float a = __uint_as_float(w.x) * h.x;
         a = fmaf(__uint_as_float(w.y), h.y, a);
         a = fmaf(__uint_as_float(w.z), h.z, a);
         return fmaf(__uint_as_float(w.w), h.w, a);
     } else if constexpr (WT == W_F16) {
         const half8 hw = __builtin_bit_cast(half8, w);
-        const float4 h0 = *reinterpret_cast<const float4*>(hs + k);
-        const float4 h1 = *reinterpret_cast<const float4*>(hs + k + 4);
+        const float4 h0 = *reinterpret_cast<const float4*>(hl);
+        const float4 h1 = *reinterpret_cast<const float4*>(hl + 256);
         float a = static_cast<float>(hw[0]) * h0.x;
         float b = static_cast<float>(hw[1]) * h0.y;
         a = fmaf(static_cast<float>(hw[2]), h0.z, a);
@@ -199,7 +220,7 @@ __device__ inline float lane_dot(uint4 w, const float* hs, int64_t k, uint16_t s
         float a = 0.f, b = 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float4 h = *reinterpret_cast<const float4*>(hs + k + 4 * j);
+            const float4 h = *reinterpret_cast<const float4*>(hl + 256 * j);
             const uint32_t v = ww[j];
             a = fmaf(static_cast<float>(static_cast<int8_t>(v & 0xff)), h.x, a);
             b = fmaf(static_cast<float>(static_cast<int8_t>((v >> 8) & 0xff)), h.y, b);
@@ -220,15 +241,9 @@ __device__ inline float lane_dot(uint4 w, const float* hs, int64_t k, uint16_t s
 // so that its 8 waves get equal numbers of (unit, slice) items: no straggler
 // waves. Each wave walks its items as one stream of chunks, U chunks per
 // batch, and issues the loads of batch i+1 before it consumes batch i. The
-// first batch is issued by mv_begin, before the activation is even needed
-// (the persistent step kernel issues it before waiting at the barrier that
-// publishes the activation). The (unit, slice) sums meet in LDS and are
-// added in slice order after the streaming loop, so results do not depend
-// on timing.
-//
-// COH selects how the activation and the outputs are accessed: plain loads
-// and stores when they cross a kernel boundary, relaxed agent-scope atomics
-// when another work-group of the same kernel wrote them (see st_shared_f).
+// first batch is issued by mv_begin, before the activation is staged. The
+// (unit, slice) sums meet in LDS and are added in slice order after the
+// streaming loop, so results do not depend on timing.
 // ---------------------------------------------------------------------------
 template <int WT, int NR, int U>
 struct ChunkBatch {
@@ -260,8 +275,8 @@ __device__ inline void fetch(const void* W, const uint16_t* scales, const MvLayo
     const int smask = (1 << L.log_s) - 1;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int64_t unit = unit0 + (c.item >> L.log_s);
         const int64_t k = (int64_t((c.item & smask) * L.cps + c.within)) * CH + int64_t(lane) * E;
+        const int64_t unit = unit0 + (c.item >> L.log_s);
         // Chunks past the end are loaded from the start of W (a valid
         // address) and never consumed: the loads stay unconditional, so the
         // wait before consuming a batch can leave the next batch in flight
@@ -279,13 +294,10 @@ __device__ inline void fetch(const void* W, const uint16_t* scales, const MvLayo
     }
 }
 
-// DEPTH scales the chunks per batch (registers per lane: 2 batches of
-// U * NR * 4 VGPRs): more bytes in flight per wave where fewer waves share a
-// compute unit.
-template <int WT, int MODE, int DEPTH = 1>
+template <int WT, int MODE>
 struct MvState {
     static constexpr int NR = (MODE == MV_SWIGLU) ? 2 : 1;
-    static constexpr int U = DEPTH * ((WT == W_F32) ? 8 : (NR == 1 ? 8 : 4));
+    static constexpr int U = (WT == W_F32) ? 8 : (NR == 1 ? 8 : 4);
     ChunkBatch<WT, NR, U> cur;
     Cursor fc, uc;
     int item_end;
@@ -293,48 +305,10 @@ struct MvState {
     int64_t unit0;
 };
 
-template <bool COH>
-__device__ inline float act_ld(const float* p)
-{
-    if constexpr (COH) return ld_shared_f(p);
-    else return *gmem(p);
-}
-
-// 16 bytes at base[i .. i+4) through a buffer load that bypasses the
-// per-XCD L2 (cache policy sc1, as the relaxed agent-scope atomic loads):
-// sees what other work-groups of the same kernel stored with st_shared_f.
-// base must be wave-uniform; i is the lane's float index.
-constexpr int CPOL_SC1 = 16;
-constexpr int BUF_RSRC_WORD3 = 0x00020000;
-
-__device__ inline float4 coh_load4(const float* base, int i)
-{
-    const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, 0x7fffffff, BUF_RSRC_WORD3);
-    const f32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, i * 4, 0, CPOL_SC1);
-    return make_float4(v.x, v.y, v.z, v.w);
-}
-
-template <bool COH>
-__device__ inline float4 act_ld4(const float* base, int i)
-{
-    if constexpr (COH) return coh_load4(base, i);
-    else return load4f(base + i);
-}
-
-template <bool COH>
-__device__ inline void act_st(float* p, float v)
-{
-    if constexpr (COH) st_shared_f(p, v);
-    else *gmem(p) = v;
-}
-
 // Part 1: the block's item range and its first batch of weight loads.
-// tid is threadIdx.x, passed in so that a caller running several phases in
-// one kernel can keep each phase's per-lane values local to that phase.
-template <int WT, int MODE, int DEPTH>
+template <int WT, int MODE>
 __device__ inline void mv_begin(const void* W, const uint16_t* scales, const MvLayout L, int block,
-                                MvState<WT, MODE, DEPTH>& st, int tid)
+                                MvState<WT, MODE>& st, int tid)
 {
     const int lane = tid & (WAVE - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -347,42 +321,52 @@ __device__ inline void mv_begin(const void* W, const uint16_t* scales, const MvL
     st.fc = Cursor{item_begin, 0};
     st.uc = Cursor{item_begin, 0};
     if (st.n_chunks > 0) {
-        fetch<WT, MvState<WT, MODE, DEPTH>::NR, MvState<WT, MODE, DEPTH>::U>(W, scales, L, st.unit0, st.fc,
-                                                                            st.item_end, lane, st.cur);
+        fetch<WT, MvState<WT, MODE>::NR, MvState<WT, MODE>::U>(W, scales, L, st.unit0, st.fc, st.item_end,
+                                                               lane, st.cur);
     } else {
         // Defined contents: an undefined batch lets the register allocator
-        // merge it with live ranges of other phases.
+        // merge it with other live ranges.
 #pragma unroll
-        for (int u = 0; u < MvState<WT, MODE, DEPTH>::U; ++u)
+        for (int u = 0; u < MvState<WT, MODE>::U; ++u)
 #pragma unroll
-            for (int r = 0; r < MvState<WT, MODE, DEPTH>::NR; ++r) {
+            for (int r = 0; r < MvState<WT, MODE>::NR; ++r) {
                 st.cur.w[u][r] = make_uint4(0u, 0u, 0u, 0u);
                 if constexpr (WT == W_Q8) st.cur.s[u][r] = 0;
             }
     }
 }
 
-// Part 2: stage x (times the norm weight) in LDS (hs: K floats, then the
-// slice sums), then consume the batches and write the epilogue.
-template <int WT, int MODE, bool NORM, bool COH, int DEPTH, bool ALT = true>
+// Part 2: stage x (times the norm weight, if NORM) in LDS (hs: the staged
+// activation, then the slice sums), then consume the batches and write the
+// epilogue selected by MODE (MV_SWIGLU: gate and up rows together; the
+// others one row).
+template <int WT, int MODE, bool NORM>
 __device__ inline void mv_finish(const uint16_t* scales, const void* W, const MvLayout L,
-                                 MvState<WT, MODE, DEPTH>& st, const float* __restrict__ x,
+                                 MvState<WT, MODE>& st, const float* __restrict__ x,
                                  const float* __restrict__ norm_w, float eps,
                                  float* __restrict__ out, float* hs, float* red, int tid)
 {
-    constexpr int NR = MvState<WT, MODE, DEPTH>::NR;
-    constexpr int U = MvState<WT, MODE, DEPTH>::U;
+    constexpr int NR = MvState<WT, MODE>::NR;
+    constexpr int U = MvState<WT, MODE>::U;
     constexpr int E = Epl<WT>::v;
     constexpr int64_t CH = int64_t(WAVE) * E;
     const int lane = tid & (WAVE - 1);
     const int wave = tid >> 6;
     const int nwaves = blockDim.x >> 6;
     const int S = 1 << L.log_s;
-    float* part = hs + L.K;
+    float* part = hs + mv_staged_floats(WT, L.K);
+
+    // The residual value of this thread's first output unit, loaded now so
+    // that its latency passes while the activation is staged and the weights
+    // stream.
+    float resid0 = 0.f;
+    if constexpr (MODE == MV_RESID) {
+        if (tid < L.upb && st.unit0 + tid < L.n_out) resid0 = *gmem(out + st.unit0 + tid);
+    }
 
     float ss = 0.f;
     for (int k = tid * 4; k < L.K; k += blockDim.x * 4) {
-        float4 v = act_ld4<COH>(x, k);
+        float4 v = load4f(x + k);
         if constexpr (NORM) {
             ss = fmaf(v.x, v.x, ss);
             ss = fmaf(v.y, v.y, ss);
@@ -391,7 +375,7 @@ __device__ inline void mv_finish(const uint16_t* scales, const void* W, const Mv
             const float4 w = load4f(norm_w + k);
             v.x *= w.x; v.y *= w.y; v.z *= w.z; v.w *= w.w;
         }
-        *reinterpret_cast<float4*>(hs + k) = v;
+        *reinterpret_cast<float4*>(hs + lds_pos<WT>(k)) = v;
     }
     float r = 1.f;
     if constexpr (NORM) {
@@ -409,11 +393,12 @@ __device__ inline void mv_finish(const uint16_t* scales, const void* W, const Mv
         if constexpr (MODE == MV_SWIGLU) {
             const float g = acc[0] * r;
             const float u = acc[1] * r;
-            act_st<COH>(out + unit, gate_act(g, L.act) * u);
+            *gmem(out + unit) = gate_act(g, L.act) * u;
         } else if constexpr (MODE == MV_RESID) {
-            act_st<COH>(out + unit, act_ld<COH>(out + unit) + acc[0] * r);
+            const float old = unit == st.unit0 + tid ? resid0 : *gmem(out + unit);
+            *gmem(out + unit) = old + acc[0] * r;
         } else {
-            act_st<COH>(out + unit, acc[0] * r);
+            *gmem(out + unit) = acc[0] * r;
         }
     };
 
@@ -434,7 +419,9 @@ __device__ inline void mv_finish(const uint16_t* scales, const void* W, const Mv
                               int64_t(lane) * E;
             if (k < L.K) {
 #pragma unroll
-                for (int i = 0; i < NR; ++i) acc[i] += lane_dot<WT>(cb.w[u][i], hs, k, cb.s[WT == W_Q8 ? u : 0][i]);
+                for (int i = 0; i < NR; ++i)
+                    acc[i] += lane_dot<WT>(cb.w[u][i], hs + (k - int64_t(lane) * (E - 4)),
+                                           cb.s[WT == W_Q8 ? u : 0][i]);
             }
             if (st.uc.within == L.cps - 1) {
 #pragma unroll
@@ -450,36 +437,25 @@ __device__ inline void mv_finish(const uint16_t* scales, const void* W, const Mv
         }
     };
     // Batch i+1 is in flight while batch i is consumed; the last batch is
-    // consumed on its own (no fetch past the end). With ALT two named
-    // buffers alternate (copying one batch into the other would wait for its
-    // loads); without it, fewer registers and a copy per batch.
-    if constexpr (ALT) {
-        ChunkBatch<WT, NR, U> nb;
+    // consumed on its own (no fetch past the end). Two named buffers
+    // alternate: copying one batch into the other would wait for its loads.
+    ChunkBatch<WT, NR, U> nb;
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int r = 0; r < NR; ++r) {  // defined (see mv_begin)
-                nb.w[u][r] = make_uint4(0u, 0u, 0u, 0u);
-                if constexpr (WT == W_Q8) nb.s[u][r] = 0;
-            }
-        for (int q = 0; q < st.n_chunks;) {
-            if (q + U >= st.n_chunks) { consume(st.cur); break; }
-            fetch<WT, NR, U>(W, scales, L, st.unit0, st.fc, st.item_end, lane, nb);
-            consume(st.cur);
-            q += U;
-            if (q + U >= st.n_chunks) { consume(nb); break; }
-            fetch<WT, NR, U>(W, scales, L, st.unit0, st.fc, st.item_end, lane, st.cur);
-            consume(nb);
-            q += U;
+        for (int r2 = 0; r2 < NR; ++r2) {  // defined (see mv_begin)
+            nb.w[u][r2] = make_uint4(0u, 0u, 0u, 0u);
+            if constexpr (WT == W_Q8) nb.s[u][r2] = 0;
         }
-    } else {
-        for (int q = 0; q < st.n_chunks; q += U) {
-            ChunkBatch<WT, NR, U> nxt;
-            const bool more = q + U < st.n_chunks;
-            if (more) fetch<WT, NR, U>(W, scales, L, st.unit0, st.fc, st.item_end, lane, nxt);
-            consume(st.cur);
-            if (more) st.cur = nxt;
-        }
+    for (int q = 0; q < st.n_chunks;) {
+        if (q + U >= st.n_chunks) { consume(st.cur); break; }
+        fetch<WT, NR, U>(W, scales, L, st.unit0, st.fc, st.item_end, lane, nb);
+        consume(st.cur);
+        q += U;
+        if (q + U >= st.n_chunks) { consume(nb); break; }
+        fetch<WT, NR, U>(W, scales, L, st.unit0, st.fc, st.item_end, lane, st.cur);
+        consume(nb);
+        q += U;
     }
     __syncthreads();
     for (int j = tid; j < L.upb; j += blockDim.x) {

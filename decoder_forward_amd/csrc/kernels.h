@@ -75,6 +75,7 @@ struct MvLayout {
     int cps;
     int ipw;
     int act = ACT_SILU;  // MV_SWIGLU's gate activation
+    int wdtype = W_F16;  // weight dtype the layout was made for (chunk width)
 };
 // Layout for at most max_blocks blocks of nwaves waves; *blocks gets the
 // blocks it uses.
@@ -164,60 +165,6 @@ hipError_t launch_argmax(const float* v, int n, DevState* st, int* out_dev,
 
 hipError_t launch_set_state(DevState* st, int pos, int tok, int step,
                             hipStream_t s);
-
-// ---- persistent decode step -------------------------------------------------
-
-// One layer's device pointers for the persistent step kernel.
-struct StepLayer {
-    const void* wqkv; const uint16_t* sqkv;  // values; 8-bit scales (else null)
-    const void* wo; const uint16_t* so;
-    const void* wgu; const uint16_t* sgu;
-    const void* wd; const uint16_t* sd;
-    const float* attn_norm;
-    const float* ffn_norm;
-    const float* q_norm;                     // null for llama
-    const float* k_norm;
-    const float* bias;                       // q|k|v bias (qwen2), else null
-    float* kc;                               // layer K cache [n_kv][max_ctx][hd]
-    float* vc;
-};
-
-struct StepArgs {
-    const StepLayer* layers;
-    int n_layers, d, qd, kvd, F, V, hd, n_heads, n_kv, max_ctx;
-    float eps;
-    int adjacent;                            // rope pairing, as in AttnDecodeArgs
-    const void* embd;                        // token embedding (f16 or f32)
-    int embd_dtype;
-    const void* wout; const uint16_t* sout;  // logits matrix
-    const float* out_norm;
-    const float* cos_t;
-    const float* sin_t;
-    float* x; float* qkv; float* att; float* mid;
-    float* part;                             // attention partials [n_kv][splits][G][hd+2]
-    int max_splits;                          // split capacity per KV head
-    float* amax_val; int* amax_idx;          // argmax partials, one per block
-    DevState* st;                            // position, token, step
-    int* gen_out;                            // generated tokens
-    int* bar;                                // grid barrier words: [2] error flag, [3] launch count
-    int* bar_flags;                          // grid barrier: one flag per block
-    int* attn_cnt;                           // per KV head: splits finished (ticket)
-    MvLayout mv_qkv, mv_o, mv_gu, mv_down, mv_logits;
-};
-
-// The step kernel runs one block of STEP_THREADS threads per compute unit.
-constexpr int STEP_THREADS = 1024;
-// True if the configuration has a step kernel and one block with its LDS
-// fits on a compute unit; *lds gets the dynamic LDS bytes. The matvec
-// layouts in `a` must be made for one block per compute unit.
-bool step_fits(const StepArgs& a, int wdtype, int odtype, size_t* lds);
-// Launch one decode step (cooperative launch: every block resident). `a`
-// is the host copy of the step description, `a_dev` the same bytes in device
-// memory. With logits == nullptr the logits are not computed; with
-// `advance` the greedy token is written to gen_out[step] and becomes the
-// next step's token (position and step count move on by one).
-hipError_t launch_decode_step(const StepArgs& a, const StepArgs* a_dev, float* logits, int advance,
-                              int wdtype, int odtype, int blocks, size_t lds, hipStream_t s);
 
 // ---- bulk prefill ----------------------------------------------------------
 

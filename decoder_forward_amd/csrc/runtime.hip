@@ -213,20 +213,6 @@ struct df_model {
 
     FramePool pool;
 
-    // Persistent decode step: one cooperative launch per token covering all
-    // layers, the logits and the greedy token, when the configuration has a
-    // step kernel (else one launch per operation class).
-    int flags = 0;
-    bool step_on = false;
-    int step_blocks = 0;
-    size_t step_lds = 0;
-    int step_wdtype = 0, step_odtype = 0;
-    StepArgs step{};
-    StepArgs* step_dev = nullptr;
-    int* bar_words = nullptr;     // grid barrier (error flag, launch count, block flags), attention tickets
-    size_t bar_bytes = 0;
-    bool step_unchecked = false;  // step launches whose error flag is unread
-
     // Captured decode step (+ argmax) for df_generate, replayed once per
     // token; valid while its buffers are the ones the pool hands out.
     hipGraphExec_t gen_exec = nullptr;
@@ -759,112 +745,6 @@ bool build_conversation(df_model* m, Fail* e)
 }
 
 // ---------------------------------------------------------------------------
-// Persistent step set-up: fixed activation buffers, the per-layer pointer
-// table and the step description in device memory, barrier words.
-// ---------------------------------------------------------------------------
-bool setup_step(df_model* m, Fail* e)
-{
-    const df_config& c = m->cfg;
-    if (c.n_layers == 0) return true;
-    // The step kernel covers the llama / qwen3 / qwen2 step lists with full
-    // attention; gemma3's extra norms, gelu_tanh and windows run as separate
-    // launches.
-    if (c.arch == DF_ARCH_GEMMA3 || c.sliding_window > 0) return true;
-    hipDeviceProp_t prop;
-    if (!check(hipGetDeviceProperties(&prop, m->device), "device properties", e)) return false;
-    const int nb = prop.multiProcessorCount;
-    const int hd = c.head_dim;
-    const int64_t qd = int64_t(c.n_heads) * hd, kvd = int64_t(c.n_kv_heads) * hd;
-    const size_t kv_layer = size_t(c.n_kv_heads) * size_t(c.max_ctx) * size_t(hd);
-    const int wdt = m->layers[0].wqkv.dtype, odt = m->out.dtype;
-    StepArgs a{};
-    a.n_layers = c.n_layers;
-    a.d = c.d_model;
-    a.qd = int(qd);
-    a.kvd = int(kvd);
-    a.F = c.ffn_dim;
-    a.V = c.vocab;
-    a.hd = hd;
-    a.n_heads = c.n_heads;
-    a.n_kv = c.n_kv_heads;
-    a.max_ctx = c.max_ctx;
-    a.eps = float(c.rms_eps);
-    a.adjacent = c.rope_pairing == DF_ROPE_ADJACENT;
-    a.embd = m->embd.data;
-    a.embd_dtype = m->embd.dtype;
-    a.wout = m->out.data;
-    a.sout = m->out.scales;
-    a.out_norm = m->out_norm;
-    a.cos_t = m->cos_t;
-    a.sin_t = m->sin_t;
-    a.part = m->attn_part;
-    a.max_splits = ATTN_MAX_SPLIT;
-    a.st = m->state;
-    a.gen_out = m->gen_tokens;
-    int64_t used = 0;
-    a.mv_qkv = make_mv_layout(wdt, c.d_model, qd + 2 * kvd, 0, nb, STEP_THREADS / 64, &used);
-    a.mv_o = make_mv_layout(wdt, qd, c.d_model, 0, nb, STEP_THREADS / 64, &used);
-    a.mv_gu = make_mv_layout(wdt, c.d_model, c.ffn_dim, c.ffn_dim, nb, STEP_THREADS / 64, &used);
-    a.mv_down = make_mv_layout(wdt, c.ffn_dim, c.d_model, 0, nb, STEP_THREADS / 64, &used);
-    a.mv_logits = make_mv_layout(odt, c.d_model, c.vocab, 0, nb, STEP_THREADS / 64, &used);
-    size_t lds = 0;
-    if (!step_fits(a, wdt, odt, &lds)) return true;  // separate launches
-
-    auto A = [&](size_t bytes, const char* what) { return dev_alloc(m, bytes, what, e); };
-    a.x = static_cast<float*>(A(size_t(c.d_model) * 4, "step activations"));
-    a.qkv = static_cast<float*>(A(size_t(qd + 2 * kvd) * 4, "step activations"));
-    a.att = static_cast<float*>(A(size_t(qd) * 4, "step activations"));
-    a.mid = static_cast<float*>(A(size_t(c.ffn_dim) * 4, "step activations"));
-    a.amax_val = static_cast<float*>(A(size_t(nb) * 4, "argmax partials"));
-    a.amax_idx = static_cast<int*>(A(size_t(nb) * 4, "argmax partials"));
-    // barrier words, attention tickets, then one flag per block (padded to
-    // whole 16-byte groups: the barrier reads the flags four at a time)
-    const size_t flags_at = (4 + size_t(c.n_kv_heads) + 3) & ~size_t(3);
-    const size_t n_words = flags_at + ((size_t(nb) + 3) & ~size_t(3));
-    m->bar_words = static_cast<int*>(A(n_words * 4, "grid barrier and tickets"));
-    StepLayer* ly_dev = static_cast<StepLayer*>(A(size_t(c.n_layers) * sizeof(StepLayer), "layer table"));
-    m->step_dev = static_cast<StepArgs*>(A(sizeof(StepArgs), "step description"));
-    if (!a.x || !a.qkv || !a.att || !a.mid || !a.amax_val || !a.amax_idx || !m->bar_words ||
-        !ly_dev || !m->step_dev)
-        return false;
-    a.bar = m->bar_words;
-    a.attn_cnt = m->bar_words + 4;
-    a.bar_flags = m->bar_words + flags_at;
-    a.layers = ly_dev;
-    std::vector<StepLayer> ly(size_t(c.n_layers));
-    for (int l = 0; l < c.n_layers; ++l) {
-        const Layer& L = m->layers[size_t(l)];
-        StepLayer& s = ly[size_t(l)];
-        s.wqkv = L.wqkv.data; s.sqkv = L.wqkv.scales;
-        s.wo = L.wo.data; s.so = L.wo.scales;
-        s.wgu = L.wgu.data; s.sgu = L.wgu.scales;
-        s.wd = L.wd.data; s.sd = L.wd.scales;
-        s.attn_norm = L.attn_norm;
-        s.ffn_norm = L.ffn_norm;
-        s.bias = L.bqkv;
-        s.q_norm = L.q_norm;
-        s.k_norm = L.k_norm;
-        s.kc = m->kc + size_t(l) * kv_layer;
-        s.vc = m->vc + size_t(l) * kv_layer;
-    }
-    m->bar_bytes = n_words * 4;
-    if (!check(hipMemsetAsync(m->bar_words, 0, m->bar_bytes, m->stream), "grid barrier init", e) ||
-        !check(hipMemcpyAsync(ly_dev, ly.data(), ly.size() * sizeof(StepLayer), hipMemcpyHostToDevice,
-                              m->stream), "layer table upload", e) ||
-        !check(hipMemcpyAsync(m->step_dev, &a, sizeof a, hipMemcpyHostToDevice, m->stream),
-               "step description upload", e) ||
-        !check(hipStreamSynchronize(m->stream), "step set-up", e))
-        return false;
-    m->step = a;
-    m->step_blocks = nb;
-    m->step_lds = lds;
-    m->step_wdtype = wdt;
-    m->step_odtype = odt;
-    m->step_on = true;
-    return true;
-}
-
-// ---------------------------------------------------------------------------
 // The decode step: one token at position kv_len (state->pos), through the
 // step list. Per layer: [rms_norm + q/k/v matmul] -> [norm_heads + rope + KV
 // append + attention] -> [o matmul + add] -> [rms_norm + gate/up matmul +
@@ -1038,53 +918,10 @@ void collect_event_time(df_model* m)
     m->ev_kind = 0;
 }
 
-// The step kernel's barriers are bounded waits: one that runs out of spins
-// sets the error flag and every block leaves. Read the flag once the
-// launches have completed and clear the barrier words if it is set.
-df_status step_check(df_model* m, const char* who)
-{
-    if (!m->step_unchecked) return DF_OK;
-    m->step_unchecked = false;
-    int flag = 0;
-    hipError_t r = hipMemcpyAsync(&flag, m->bar_words + 2, 4, hipMemcpyDeviceToHost, m->stream);
-    if (r == hipSuccess) r = hipStreamSynchronize(m->stream);
-    if (r != hipSuccess) {
-        (void)hipGetLastError();
-        return set_err(m, DF_ERR_DEVICE, fmt("%s: %s", who, hipGetErrorString(r)));
-    }
-    if (flag != 0) {
-        (void)hipMemsetAsync(m->bar_words, 0, m->bar_bytes, m->stream);
-        (void)hipStreamSynchronize(m->stream);
-        (void)hipGetLastError();
-        return set_err(m, DF_ERR_DEVICE,
-                       fmt("%s: a grid barrier of the decode step ran out of spins; "
-                           "the outputs of this call are invalid", who));
-    }
-    return DF_OK;
-}
-
-hipError_t launch_step_kernel(df_model* m, float* logits, int advance)
-{
-    ProfScope ps(m, DF_K_STEP);
-    m->step_unchecked = true;
-    return launch_decode_step(m->step, m->step_dev, logits, advance, m->step_wdtype, m->step_odtype,
-                              m->step_blocks, m->step_lds, m->stream);
-}
-
 df_status decode_one(df_model* m, int32_t tok, float* logits)
 {
     Fail e{DF_OK, ""};
     const int pos = m->kv_len;
-    if (m->step_on) {
-        hipError_t r = launch_set_state(m->state, pos, tok, 0, m->stream);
-        if (r == hipSuccess) r = launch_step_kernel(m, logits, 0);
-        if (r != hipSuccess) {
-            (void)hipGetLastError();
-            return set_err(m, DF_ERR_DEVICE, fmt("decode step launch failed: %s", hipGetErrorString(r)));
-        }
-        m->kv_len = pos + 1;
-        return DF_OK;
-    }
     m->pool.reset();
     StepBufs b{};
     if (!step_buffers(m, &b, &e)) return set_err(m, e.code, e.msg);
@@ -1277,8 +1114,8 @@ df_status df_load(const df_config* cfg, const df_tensor* tensors, size_t n_tenso
     }
     *out = nullptr;
     Fail e{DF_OK, ""};
-    if (opt && (opt->flags & ~DF_FLAG_PERSISTENT_STEP)) {
-        g_load_error = fmt("df_load: unknown option flags 0x%x", unsigned(opt->flags));
+    if (opt && opt->flags) {
+        g_load_error = fmt("df_load: option flags 0x%x: none are defined", unsigned(opt->flags));
         return DF_ERR_INVALID_ARGUMENT;
     }
     std::map<std::string, const df_tensor*> found;
@@ -1344,14 +1181,12 @@ df_status df_load(const df_config* cfg, const df_tensor* tensors, size_t n_tenso
         g_load_error = "backend init: hipEventCreate failed";
         return DF_ERR_BACKEND_INIT;
     }
-    m->flags = opt ? opt->flags : 0;
     m->wstore = std::make_shared<WeightStore>();
     m->wstore->device = dev;
     m->alloc_to = &m->wstore->allocs;
     const bool weights_ok = build_weights(m, found, &e);
     m->alloc_to = nullptr;
-    if (!weights_ok || !build_conversation(m, &e) ||
-        ((m->flags & DF_FLAG_PERSISTENT_STEP) && !setup_step(m, &e))) {
+    if (!weights_ok || !build_conversation(m, &e)) {
         release(m);
         delete m;
         g_load_error = e.msg;
@@ -1381,8 +1216,7 @@ df_status df_session(const df_model* base, int32_t max_ctx, const df_options* op
         return DF_ERR_INVALID_ARGUMENT;
     }
     if (opt && opt->flags) {
-        g_load_error = fmt("df_session: option flags 0x%x: sessions take none (the persistent "
-                           "step is per model)", unsigned(opt->flags));
+        g_load_error = fmt("df_session: option flags 0x%x: none are defined", unsigned(opt->flags));
         return DF_ERR_INVALID_ARGUMENT;
     }
     if (hipSetDevice(base->device) != hipSuccess) {
@@ -1467,8 +1301,6 @@ df_status df_forward(df_model* m, const int32_t* tokens, int32_t n, float* logit
     }
     (void)hipEventRecord(m->ev1, m->stream);
     m->ev_kind = n == 1 ? 1 : 2;
-    const df_status chk = step_check(m, "df_forward");
-    if (st == DF_OK) st = chk;
     if (st == DF_OK) m->n_forward++;
     return st;
 }
@@ -1578,24 +1410,6 @@ df_status df_generate(df_model* m, int32_t first_token, int32_t n_steps, int32_t
     float* lg = static_cast<float*>(m->pool.alloc(size_t(m->cfg.vocab) * 4, USAGE_DEVICE, &e));
     if (!lg) return set_err(m, e.code, e.msg);
     hipError_t r = launch_set_state(m->state, m->kv_len, first_token, 0, m->stream);
-    if (m->step_on) {
-        // One launch per token; position and token live in device state.
-        for (int32_t i = 0; i < n_steps && r == hipSuccess; ++i) r = launch_step_kernel(m, lg, 1);
-        if (r == hipSuccess)
-            r = hipMemcpyAsync(tokens_dev, m->gen_tokens, size_t(n_steps) * 4, hipMemcpyDeviceToDevice,
-                               m->stream);
-        if (r == hipSuccess && logits_dev)
-            r = hipMemcpyAsync(logits_dev, lg, size_t(m->cfg.vocab) * 4, hipMemcpyDeviceToDevice,
-                               m->stream);
-        if (r != hipSuccess) {
-            (void)hipGetLastError();
-            (void)step_check(m, "df_generate");
-            return set_err(m, DF_ERR_DEVICE, fmt("df_generate: launch failed: %s", hipGetErrorString(r)));
-        }
-        m->kv_len += n_steps;
-        m->n_forward += n_steps;
-        return step_check(m, "df_generate");
-    }
     // One decode step + greedy argmax, position and token read from device
     // state: the same launches serve every step, so they are captured into a
     // graph once and replayed (unless a kernel class is being profiled).
@@ -1686,8 +1500,6 @@ df_status df_get_timings(df_model* m, df_timings* out)
     out->weight_bytes = m->weight_bytes;
     out->kv_bytes = m->kv_bytes;
     out->pool_bytes = int64_t(m->pool.bytes());
-    out->persistent_step = m->step_on ? 1 : 0;
-    out->step_blocks = m->step_on ? m->step_blocks : 0;
     return DF_OK;
 }
 
@@ -1781,17 +1593,13 @@ df_status df_time_kernel(df_model* m, int32_t kernel, int32_t reps, double* mean
     if (!step_buffers(m, &b, &e)) return set_err(m, e.code, e.msg);
     float* lg = static_cast<float*>(m->pool.alloc(size_t(m->cfg.vocab) * 4, USAGE_DEVICE, &e));
     if (!lg) return set_err(m, e.code, e.msg);
-    if (kernel == DF_K_STEP && !m->step_on)
-        return set_err(m, DF_ERR_UNSUPPORTED_OP,
-                       "df_time_kernel: this model runs its decode step as separate launches");
     // The attention launch appends this step's K / V row at kv_len: on a full
     // cache that row is live, so the replay is refused rather than clamped.
-    if ((kernel == DF_K_ATTN || kernel == DF_K_STEP) && m->kv_len >= m->cfg.max_ctx)
+    if (kernel == DF_K_ATTN && m->kv_len >= m->cfg.max_ctx)
         return set_err(m, DF_ERR_CONTEXT_FULL,
                        fmt("df_time_kernel: the cache is full (kv_len %d == max_ctx); the replay "
                            "would overwrite its last row", m->kv_len));
-    const bool per_layer = kernel != DF_K_EMBED && kernel != DF_K_LOGITS && kernel != DF_K_ARGMAX &&
-                           kernel != DF_K_STEP;
+    const bool per_layer = kernel != DF_K_EMBED && kernel != DF_K_LOGITS && kernel != DF_K_ARGMAX;
     const int nl = per_layer ? m->cfg.n_layers : 1;
     if (nl == 0) return set_err(m, DF_ERR_INVALID_ARGUMENT, "df_time_kernel: no layers");
     // position of the replayed step: kv_len (the attention classes need a
@@ -1804,8 +1612,7 @@ df_status df_time_kernel(df_model* m, int32_t kernel, int32_t reps, double* mean
         for (int l = 0; l < nl && r == hipSuccess; ++l)
             r = kernel == DF_K_ARGMAX
                     ? launch_argmax(lg, m->cfg.vocab, m->state, m->argmax_out, 0, nullptr, m->stream)
-                : kernel == DF_K_STEP ? launch_step_kernel(m, lg, 0)
-                                      : launch_class(m, b, kernel, l, splits, lg);
+                : launch_class(m, b, kernel, l, splits, lg);
     if (r == hipSuccess) r = hipEventRecord(m->ev1, m->stream);
     if (r == hipSuccess) r = hipEventSynchronize(m->ev1);
     float ms = 0.f;
@@ -1816,7 +1623,7 @@ df_status df_time_kernel(df_model* m, int32_t kernel, int32_t reps, double* mean
     }
     m->ev_kind = 0;
     *mean_us = double(ms) * 1e3 / double(reps * nl);
-    return step_check(m, "df_time_kernel");
+    return DF_OK;
 }
 
 df_status df_time_prefill(df_model* m, int32_t kernel, int32_t rows, int32_t reps, double* mean_us)

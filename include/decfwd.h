@@ -143,17 +143,8 @@ typedef struct df_tensor {
 typedef struct df_options {
     void* stream;        /* hipStream_t to order all work on; NULL: the library makes one */
     int32_t device;      /* HIP device ordinal; used when stream is NULL */
-    int32_t flags;       /* DF_FLAG_* bits; other bits are rejected */
+    int32_t flags;       /* reserved: must be 0 (no flags are defined) */
 } df_options;
-
-/* Run every decode step as one persistent cooperative launch (all layers,
- * logits and greedy token; phases separated by grid barriers) instead of one
- * launch per operation class (DF_K_EMBED .. DF_K_ATTN_MERGE). Taken where the
- * configuration has a step kernel (f16 or 8-bit block weights, head_dim 64
- * or 128); otherwise the separate launches run. Results agree with the
- * separate launches within rounding; on MI355X it is slower today, so it is
- * not the default. */
-#define DF_FLAG_PERSISTENT_STEP 1
 
 typedef struct df_timings {
     double load_ms;          /* wall time of df_load, upload included */
@@ -163,8 +154,6 @@ typedef struct df_timings {
     int64_t weight_bytes;    /* device bytes held for weights */
     int64_t kv_bytes;        /* device bytes held for the KV cache */
     int64_t pool_bytes;      /* device bytes held by the activation frame pool */
-    int32_t persistent_step; /* 1: a decode step is one persistent launch; 0: separate launches */
-    int32_t step_blocks;     /* blocks of the persistent launch (0 without it) */
 } df_timings;
 
 typedef struct df_model df_model;
@@ -202,9 +191,7 @@ df_status df_session(const df_model* model, int32_t max_ctx, const df_options* o
  * way into the GEMM; f32 weights run the decode path n times), which matches
  * n single calls within the prefill tolerance. Arguments are
  * checked before any launch; on error kv_len is unchanged. Stream-ordered:
- * the host may reuse `tokens` on return. When decode steps ran as the
- * persistent launch, the call returns after they complete, so that a grid
- * barrier that ran out of spins is reported here (DF_ERR_DEVICE). */
+ * the host may reuse `tokens` on return. */
 df_status df_forward(df_model* m, const int32_t* tokens, int32_t n,
                      float* logits_dev);
 
@@ -212,8 +199,7 @@ df_status df_forward(df_model* m, const int32_t* tokens, int32_t n,
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same
  * result as n df_forward calls of one token each, with no allocation in the
  * call. The n tokens run through the decode kernels one position at a time
- * (never the bulk matrix-core path, whose buffers grow with n; never the
- * persistent step). The activations that pass between the step's kernels
+ * (never the bulk matrix-core path, whose buffers grow with n). The activations that pass between the step's kernels
  * live in one fixed device array of DF_NOALLOC_SCRATCH_BYTES bytes per GPU,
  * held by the library until the process ends and shared by every call on
  * that GPU: calls that overlap on one GPU (two models, or two sessions, on
@@ -234,8 +220,7 @@ df_status df_forward_noalloc(df_model* m, const int32_t* tokens, int32_t n,
  * computes the logits, takes t_{i+1} = argmax (lowest index on ties) and
  * writes it to tokens_dev[i], for i < n_steps, with no host round trip.
  * The last step's logits go to logits_dev unless it is NULL. Equivalent to
- * n_steps df_forward(n = 1) + df_argmax calls. Synchronises when the steps
- * run as the persistent launch (see df_forward). */
+ * n_steps df_forward(n = 1) + df_argmax calls. */
 df_status df_generate(df_model* m, int32_t first_token, int32_t n_steps,
                       int32_t* tokens_dev, float* logits_dev);
 
@@ -285,8 +270,7 @@ void* df_stream(const df_model* m);
 #define DF_K_LOGITS 6       /* final rms_norm + logits matvec */
 #define DF_K_ARGMAX 7       /* greedy token */
 #define DF_K_ATTN_MERGE 8   /* merge of the attention splits */
-#define DF_K_STEP 9         /* the whole decode step as one persistent launch */
-#define DF_K_COUNT 10
+#define DF_K_COUNT 9
 /* Bulk-prefill launch classes, for df_time_prefill. */
 #define DF_K_PF_QKV 10      /* rms_norm rows + q/k/v GEMM */
 #define DF_K_PF_ATTN 11     /* bias / norm_heads / rope / KV append + causal attention */
@@ -311,9 +295,8 @@ df_status df_profile_read(df_model* m, int32_t kernel, int64_t* launches,
  * between. Activation buffers and the cache row at kv_len are overwritten
  * (the next df_forward / df_generate starts from its own inputs as always).
  * The row at kv_len is free, so the cached context stays intact; on a full
- * cache (kv_len == max_ctx) DF_K_ATTN and DF_K_STEP return
- * DF_ERR_CONTEXT_FULL. DF_K_STEP needs a model that runs the persistent step
- * (else DF_ERR_UNSUPPORTED_OP). Synchronises. */
+ * cache (kv_len == max_ctx) DF_K_ATTN returns DF_ERR_CONTEXT_FULL.
+ * Synchronises. */
 df_status df_time_kernel(df_model* m, int32_t kernel, int32_t reps,
                          double* mean_us);
 

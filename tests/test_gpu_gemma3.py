@@ -132,15 +132,6 @@ def test_tiny_bulk_then_decode(dfa, wdtype):
     m.close()
 
 
-def test_persistent_flag_falls_back_for_gemma3(dfa):
-    cfg, W = tiny(wdtype="f16", d_model=192, n_heads=8, n_kv_heads=4, head_dim=64,
-                  ffn_dim=416, vocab=1000, max_ctx=64)
-    say("[small gemma3 f16] persistent flag: separate launches, same results")
-    m = decode_case(dfa, cfg, W, 20, 6, 1e-4, persistent_step=True)
-    assert m.timings()["persistent_step"] == 0
-    m.close()
-
-
 def test_gemma3_4b_shape_two_layers_bulk(dfa):
     # the 4B layer shape (d 2560, 8/4 heads of 256, ffn 10240) with a local
     # and a global layer; the window shortened to 128 so that a 300-token

@@ -202,7 +202,7 @@ def test_session_argument_errors(dfa):
     with pytest.raises(dfa.DecFwdError):
         dfa.df_session(m.h, 0)
     import ctypes as C
-    opt = dfa.df_options(None, 0, dfa.DF_FLAG_PERSISTENT_STEP)
+    opt = dfa.df_options(None, 0, 1)  # no option flags are defined
     out = C.c_void_p()
     rc = dfa.lib().df_session(m.h, 16, C.byref(opt), C.byref(out))
     assert dfa.STATUS_NAMES[rc] == "INVALID_ARGUMENT" and not out.value
@@ -210,18 +210,11 @@ def test_session_argument_errors(dfa):
     m.close()
 
 
-def test_session_of_a_persistent_model_uses_separate_launches(dfa):
-    cfg = synth.config("tiny", arch="llama", wdtype="f16", d_model=192, n_heads=8,
-                       n_kv_heads=4, head_dim=64, ffn_dim=416, vocab=1000, max_ctx=64)
+def test_load_rejects_option_flags(dfa):
+    import ctypes as C
+    cfg = synth.config("tiny", wdtype="f16", max_ctx=16)
     W = synth.make_weights(cfg)
-    say("[small llama f16] session of a model loaded with the persistent step")
-    m = dfa.Model(cfg, W, persistent_step=True)
-    s = m.session()
-    assert m.timings()["persistent_step"] == 1 and s.timings()["persistent_step"] == 0
-    fed, ref = oracle_greedy(cfg, W, synth.make_prompt(cfg, 10), 4)
-    gm = [m.forward([t]).cpu().numpy().copy() for t in fed]
-    gs = [s.forward([t]).cpu().numpy().copy() for t in fed]
-    check_steps(gm, ref, 1e-4, "model")
-    check_steps(gs, ref, 1e-4, "session")
-    s.close()
-    m.close()
+    for bit in (1, 2, 1 << 30):
+        with pytest.raises(dfa.DecFwdError) as e:
+            dfa.df_load(cfg, W, flags=bit)
+        assert e.value.status == "INVALID_ARGUMENT" and "flags" in str(e.value)
