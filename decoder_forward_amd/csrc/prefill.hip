@@ -196,6 +196,68 @@ __device__ inline void gemm_epilogue(const GemmArgs& g, const f32x16 (&acc)[MI][
 }
 
 
+// MFMAs of one LDS stage: KS steps of 16 along K over an MI x NI grid of
+// 32 x 32 tiles. afrag(kk, mi) / bfrag(kk, ni) give the LDS address of the
+// lane's A / B fragment for step kk. The fragments of step kk+1 are read
+// into a second register set while the MFMAs of step kk run, one read
+// between two MFMAs (fixed by scheduling groups), so each MFMA waits only on
+// reads issued a step earlier. PIPE = false: one register set, reads and
+// MFMAs left to the compiler's schedule (for kernels with no registers to
+// spare).
+template <int MI, int NI, int KS, bool PIPE, class FA, class FB>
+__device__ inline void mma_stage(f32x16 (&acc)[MI][NI], FA afrag, FB bfrag)
+{
+    constexpr int NRD = MI + NI;
+    if constexpr (!PIPE) {
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            half8 af[MI], bf[NI];
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi) af[mi] = *reinterpret_cast<const half8*>(afrag(kk, mi));
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni) bf[ni] = *reinterpret_cast<const half8*>(bfrag(kk, ni));
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < NI; ++ni)
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
+        }
+        return;
+    }
+    half8 af[2][MI], bf[2][NI];
+    auto rd = [&](int kk, int slot) {
+#pragma unroll
+        for (int i = 0; i < NRD; ++i) {
+            // B fragments first: the first MFMAs need B 0.. and A 0
+            if (i < NI) bf[slot][i] = *reinterpret_cast<const half8*>(bfrag(kk, i));
+            else af[slot][i - NI] = *reinterpret_cast<const half8*>(afrag(kk, i - NI));
+        }
+    };
+    rd(0, 0);
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+        const int c = kk & 1;
+        if (kk + 1 < KS) rd(kk + 1, c ^ 1);
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni)
+                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[c][mi], bf[c][ni], acc[mi][ni], 0, 0, 0);
+        if (kk == 0) __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);  // step 0's reads
+        if (kk + 1 < KS) {
+#pragma unroll
+            for (int i = 0; i < NRD && i < MI * NI; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+            }
+            if (MI * NI > NRD) __builtin_amdgcn_sched_group_barrier(0x008, MI * NI - NRD, 0);
+            if (NRD > MI * NI) __builtin_amdgcn_sched_group_barrier(0x100, NRD - MI * NI, 0);
+        } else {
+            __builtin_amdgcn_sched_group_barrier(0x008, MI * NI, 0);
+        }
+    }
+}
+
 template <int BM, int BN, int WN, int MODE, bool WQ8>
 __global__ void __launch_bounds__(128 * WN)
 gemm_kernel(GemmArgs g)
@@ -329,21 +391,12 @@ gemm_kernel(GemmArgs g)
 
     auto compute = [&](auto buf_c) {
         constexpr int buf = decltype(buf_c)::value;
-#pragma unroll
-        for (int kk = 0; kk < GBK / 16; ++kk) {
-            half8 af[MI], bf[NI];
-#pragma unroll
-            for (int mi = 0; mi < MI; ++mi)
-                af[mi] = *reinterpret_cast<const half8*>(&As[buf][wm * WTM + mi * 32 + (l & 31)][kk * 16 + (l >> 5) * 8]);
-#pragma unroll
-            for (int ni = 0; ni < NI; ++ni)
-                bf[ni] = *reinterpret_cast<const half8*>(&Bs[buf][wn * WTN + ni * 32 + (l & 31)][kk * 16 + (l >> 5) * 8]);
-#pragma unroll
-            for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-                for (int ni = 0; ni < NI; ++ni)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
-        }
+        // 8-bit blocks: the dequantising stores already fill the slots between
+        // the MFMAs; a second fragment set measured slower there
+        mma_stage<MI, NI, GBK / 16, !WQ8>(
+            acc,
+            [&](int kk, int mi) { return &As[buf][wm * WTM + mi * 32 + (l & 31)][kk * 16 + (l >> 5) * 8]; },
+            [&](int kk, int ni) { return &Bs[buf][wn * WTN + ni * 32 + (l & 31)][kk * 16 + (l >> 5) * 8]; });
     };
 
     // Stage s lives in LDS buffer s & 1. A register set is stored to LDS two
@@ -492,22 +545,10 @@ gemm_dma_kernel(GemmArgs g)
     auto compute = [&](int buf) {
         const _Float16* a_lds = gsm + buf * (SA + SB);
         const _Float16* b_lds = a_lds + SA;
-#pragma unroll
-        for (int kk = 0; kk < GDK / 16; ++kk) {
-            const int pos = ((kk * 2 + (l >> 5)) ^ (l & 7)) * 8;
-            half8 af[MI], bf[NI];
-#pragma unroll
-            for (int mi = 0; mi < MI; ++mi)
-                af[mi] = *reinterpret_cast<const half8*>(a_lds + (wm * WTM + mi * 32 + (l & 31)) * GDK + pos);
-#pragma unroll
-            for (int ni = 0; ni < NI; ++ni)
-                bf[ni] = *reinterpret_cast<const half8*>(b_lds + (wn * WTN + ni * 32 + (l & 31)) * GDK + pos);
-#pragma unroll
-            for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-                for (int ni = 0; ni < NI; ++ni)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
-        }
+        auto pos = [&](int kk) { return ((kk * 2 + (l >> 5)) ^ (l & 7)) * 8; };
+        mma_stage<MI, NI, GDK / 16, true>(
+            acc, [&](int kk, int mi) { return a_lds + (wm * WTM + mi * 32 + (l & 31)) * GDK + pos(kk); },
+            [&](int kk, int ni) { return b_lds + (wn * WTN + ni * 32 + (l & 31)) * GDK + pos(kk); });
     };
 
     // Prologue: stages 0 .. NB-2 in flight.
