@@ -208,7 +208,7 @@ enum GemmPlan {
     GEMM_PLAN_Q8_IN_GEMM = 16,  // weight tiles dequantised on their way into LDS
     GEMM_PLAN_DEQUANT_FIRST = 32,  // 8-bit weights converted to f16 before the GEMM (runtime)
 };
-int gemm_plan(int64_t M, int64_t N, int mode, bool q8);
+int gemm_plan(int64_t M, int64_t N, int64_t K, int64_t up_rows, int mode, bool q8);
 
 // 8-bit block rows to f16 rows: out[r][k] = f16(scale[r][k / 32] * q[r][k]),
 // the values the 8-bit GEMM stores in LDS; cols a multiple of 32.

@@ -143,19 +143,27 @@ constexpr int GBM_ = 128, GBN_ = 128;
 template <int BM, int BN>
 constexpr size_t gemm_lds_bytes() { return size_t(2) * (BM + BN) * GPAD * sizeof(_Float16); }
 
-// Tile (tm, tn) of block b. XCD-aware order: blocks b, b+8, b+16, ... run on
-// one XCD; give them the same n tile (weights) so its rows are reused from
-// that XCD's L2.
+// Tile (tm, tn) of block b. Blocks are dispatched to the 8 XCDs in turn
+// (block b to XCD b % 8), each XCD running about 32 at a time, one per
+// compute unit, and the tiles that run together on an XCD share its L2:
+// every stage, each distinct A row block and B row block among them is
+// fetched into that L2 once. The tiles are therefore numbered in groups of
+// up to 8 row blocks (tm) by all column blocks (tn), tm fastest, so 32
+// consecutive tiles cover 8 tm x 4 tn (12 distinct operand blocks; taking
+// every tm of one tn pair would need 18), and XCD x takes the x-th eighth
+// of that numbering, its blocks in dispatch order.
 __device__ inline void gemm_tile_of(int b, int ntm, int ntn, int& tm, int& tn)
 {
-    if (ntn % 8 == 0) {
-        const int x = b & 7, y = b >> 3;
-        tn = (y / ntm) * 8 + x;
-        tm = y % ntm;
-    } else {
-        tn = b / ntm;
-        tm = b % ntm;
-    }
+    const int total = ntm * ntn;
+    const int x = b & 7, y = b >> 3;
+    const int base = total >> 3, rem = total & 7;
+    const int g = x * base + min(x, rem) + y;  // XCD x's tiles are consecutive
+    constexpr int GM = 8;
+    const int grp = g / (GM * ntn);
+    const int gm = min(GM, ntm - grp * GM);    // row blocks in this group
+    const int r = g - grp * GM * ntn;
+    tn = r / gm;
+    tm = grp * GM + r % gm;
 }
 
 // Epilogue of a wave's (MI*32) x (NI*32) accumulator tile at rows m0 + wm*WTM,
@@ -195,6 +203,19 @@ __device__ inline void gemm_epilogue(const GemmArgs& g, const f32x16 (&acc)[MI][
     }
 }
 
+
+// Scheduling groups: one MFMA, then RPM LDS reads, until LEFT reads are
+// placed.
+template <int LEFT, int RPM>
+__device__ inline void sched_mfma_reads()
+{
+    if constexpr (LEFT > 0) {
+        constexpr int n = LEFT < RPM ? LEFT : RPM;
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, n, 0);
+        sched_mfma_reads<LEFT - n, RPM>();
+    }
+}
 
 // MFMAs of one LDS stage: KS steps of 16 along K over an MI x NI grid of
 // 32 x 32 tiles. afrag(kk, mi) / bfrag(kk, ni) give the LDS address of the
@@ -245,13 +266,11 @@ __device__ inline void mma_stage(f32x16 (&acc)[MI][NI], FA afrag, FB bfrag)
                 acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[c][mi], bf[c][ni], acc[mi][ni], 0, 0, 0);
         if (kk == 0) __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);  // step 0's reads
         if (kk + 1 < KS) {
-#pragma unroll
-            for (int i = 0; i < NRD && i < MI * NI; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-            }
-            if (MI * NI > NRD) __builtin_amdgcn_sched_group_barrier(0x008, MI * NI - NRD, 0);
-            if (NRD > MI * NI) __builtin_amdgcn_sched_group_barrier(0x100, NRD - MI * NI, 0);
+            // one read after each of the first MFMAs (reading earlier, two
+            // per MFMA, measured slower)
+            constexpr int NG = NRD < MI * NI ? NRD : MI * NI;
+            sched_mfma_reads<NRD, 1>();
+            if (MI * NI > NG) __builtin_amdgcn_sched_group_barrier(0x008, MI * NI - NG, 0);
         } else {
             __builtin_amdgcn_sched_group_barrier(0x008, MI * NI, 0);
         }
@@ -438,14 +457,24 @@ gemm_kernel(GemmArgs g)
 // The same GEMM for f16 weights with the operand tiles loaded straight into
 // LDS (global_load_lds_dwordx4: lane i of a wave writes 16 bytes at LDS base
 // + 16 i), no register staging. A stage holds A rows [BM][64] and B rows
-// [BN][64] unpadded; the 16-byte chunk at position p of row r is K chunk
-// p ^ (r & 7), so a load instruction fills 8 whole rows and the fragment
-// reads (32 rows of one chunk column per half-wave) fall in distinct banks.
+// [BN][64] unpadded, each row's 16-byte K chunks permuted (gemm_swz), so a
+// load instruction fills 8 whole rows and the fragment reads (32 rows of one
+// chunk column per half-wave) fall in distinct banks.
 // NB stage buffers (3 where they fit in LDS, else 2): the loads of stage
 // s + NB - 1 are issued right after the barrier that opens stage s, and a
 // wave waits only for the loads of the stage it is about to read.
 // ---------------------------------------------------------------------------
 constexpr int GDK = 64;  // K depth of a stage
+
+// Position of K chunk c of tile row r in its 128-byte LDS row: c ^ gemm_swz(r).
+// A 16-byte-per-lane LDS read is served 16 lanes at a time from 256 bytes
+// of banks (on gfx950 the swizzle c ^ (r & 7), which separates only 8 rows,
+// left the bank-conflict counter at half of the LDS-active cycles). The 16
+// lanes of a fragment read take 16 consecutive rows of one K chunk; rows 2j
+// and 2j+1 lie in different halves of a 256-byte bank line, and
+// gemm_swz(r) = (r >> 1) & 7 gives the 8 rows of each half 8 different
+// positions, so the 16 reads hit 16 different bank groups.
+__device__ inline int gemm_swz(int r) { return (r >> 1) & 7; }
 
 template <int BM, int BN>
 constexpr int gemm_dma_stages() { return size_t(3) * (BM + BN) * GDK * 2 <= 160 * 1024 ? 3 : 2; }
@@ -458,6 +487,26 @@ __device__ inline void wait_vmcnt()
 {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Buffer descriptors of the direct-to-LDS loads: raw (stride 0) over
+// DMA_RANGE bytes from the matrix base; an offset at or past DMA_OOB is out
+// of range and reads zeros. Matrices of DMA_RANGE bytes or more take the
+// register-staged kernel (gemm_dma_fits).
+constexpr int DMA_RANGE = 0x7fffffff;
+constexpr uint32_t DMA_OOB = 0x80000000u;
+constexpr int BUF_RSRC_W3 = 0x00020000;
+
+__device__ inline __amdgpu_buffer_rsrc_t dma_rsrc(const uint16_t* base)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, DMA_RANGE, BUF_RSRC_W3);
+}
+
+// 16 bytes per lane from byte offset voff + soff of the buffer into LDS at
+// dst + 16 * lane.
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t r, _Float16* dst, uint32_t voff, uint32_t soff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst), 16, voff, soff, 0, 0);
 }
 
 template <int BM, int BN, int WN, int MODE>
@@ -484,20 +533,28 @@ gemm_dma_kernel(GemmArgs g)
     const int m0 = tm * BM;
     const int n0 = tn * ncols;
 
-    // This lane's source rows: load instruction q of the wave fills rows
-    // (wave*I + q)*8 .. +7; lane l takes row + l/8, position l%8, which holds
-    // K chunk (l%8) ^ (l/8) (the row's low three bits are l/8).
-    const int kc = ((l & 7) ^ (l >> 3)) * 8;  // K offset of this lane's chunk in a stage
-    const uint16_t* asrc[IA];
-    const uint16_t* bsrc[IB];
+    // This lane's source rows: load instruction q of the wave fills tile
+    // rows r = (wave*I + q)*8 .. +7; lane l takes row r + l/8, position l%8,
+    // which holds K chunk (l%8) ^ gemm_swz(row). The loads are buffer loads
+    // into LDS: a per-lane byte offset fixed for the whole K loop plus a
+    // per-stage scalar offset, one instruction per load. A row past the end
+    // gets an offset beyond the buffer's range (DMA_OOB), which reads zeros.
+    // g.zeros is not needed here.
+    const __amdgpu_buffer_rsrc_t ra = dma_rsrc(g.A);
+    const __amdgpu_buffer_rsrc_t rb = dma_rsrc(g.B);
+    uint32_t voa[IA], vob[IB];  // byte offsets of this lane's chunks at k = 0
+    int kca[IA], kcb[IB];       // K offset of this lane's chunk in a stage
 #pragma unroll
     for (int q = 0; q < IA; ++q) {
-        const int am = m0 + (wave * IA + q) * 8 + (l >> 3);
-        asrc[q] = am < g.M ? g.A + int64_t(am) * g.lda + kc : nullptr;
+        const int row = (wave * IA + q) * 8 + (l >> 3);
+        kca[q] = ((l & 7) ^ gemm_swz(row)) * 8;
+        const int am = m0 + row;
+        voa[q] = am < g.M ? uint32_t((int64_t(am) * g.lda + kca[q]) * 2) : DMA_OOB;
     }
 #pragma unroll
     for (int q = 0; q < IB; ++q) {
         const int row = (wave * IB + q) * 8 + (l >> 3);
+        kcb[q] = ((l & 7) ^ gemm_swz(row)) * 8;
         int bn;
         bool ok;
         if constexpr (MODE == GEMM_SWIGLU_F16) {
@@ -509,26 +566,20 @@ gemm_dma_kernel(GemmArgs g)
             bn = n0 + row;
             ok = bn < g.N;
         }
-        bsrc[q] = ok ? g.B + int64_t(bn) * g.ldb + kc : nullptr;
+        vob[q] = ok ? uint32_t((int64_t(bn) * g.ldb + kcb[q]) * 2) : DMA_OOB;
     }
-    const int nst = (g.K + GDK - 1) / GDK;
-    // Loads of stage st into buffer buf; rows or K chunks past the end read
-    // 16 zero bytes.
+    const int nst = g.K / GDK;  // K is a multiple of GDK here (gemm_dma_fits)
+    // Loads of stage st into buffer buf.
     auto issue = [&](int st, int buf) {
-        const int k0 = st * GDK;
-        const bool kin = k0 + kc < g.K;
+        const uint32_t so = uint32_t(st * GDK) * 2;
         _Float16* a_lds = gsm + buf * (SA + SB);
         _Float16* b_lds = a_lds + SA;
 #pragma unroll
-        for (int q = 0; q < IA; ++q) {
-            const void* src = (asrc[q] && kin) ? static_cast<const void*>(asrc[q] + k0) : g.zeros;
-            __builtin_amdgcn_global_load_lds(src, a_lds + (wave * IA + q) * 8 * GDK, 16, 0, 0);
-        }
+        for (int q = 0; q < IA; ++q)
+            dma16(ra, a_lds + (wave * IA + q) * 8 * GDK, voa[q], so);
 #pragma unroll
-        for (int q = 0; q < IB; ++q) {
-            const void* src = (bsrc[q] && kin) ? static_cast<const void*>(bsrc[q] + k0) : g.zeros;
-            __builtin_amdgcn_global_load_lds(src, b_lds + (wave * IB + q) * 8 * GDK, 16, 0, 0);
-        }
+        for (int q = 0; q < IB; ++q)
+            dma16(rb, b_lds + (wave * IB + q) * 8 * GDK, vob[q], so);
     };
 
     f32x16 acc[MI][NI];
@@ -540,12 +591,12 @@ gemm_dma_kernel(GemmArgs g)
             for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.f;
 
     // Fragment rows: A rows wm*WTM + mi*32 + l%32, B rows wn*WTN + ni*32 +
-    // l%32; K chunk kk*2 + l/32 sits at position chunk ^ (row & 7), and
-    // row & 7 == l & 7 for every fragment row.
+    // l%32 (every fragment's first row is a multiple of 32); K chunk
+    // kk*2 + l/32 sits at position chunk ^ gemm_swz(row) = chunk ^ ((l/2) & 7).
     auto compute = [&](int buf) {
         const _Float16* a_lds = gsm + buf * (SA + SB);
         const _Float16* b_lds = a_lds + SA;
-        auto pos = [&](int kk) { return ((kk * 2 + (l >> 5)) ^ (l & 7)) * 8; };
+        auto pos = [&](int kk) { return ((kk * 2 + (l >> 5)) ^ ((l >> 1) & 7)) * 8; };
         mma_stage<MI, NI, GDK / 16, true>(
             acc, [&](int kk, int mi) { return a_lds + (wm * WTM + mi * 32 + (l & 31)) * GDK + pos(kk); },
             [&](int kk, int ni) { return b_lds + (wn * WTN + ni * 32 + (l & 31)) * GDK + pos(kk); });
@@ -607,11 +658,13 @@ hipError_t launch_gemm_dma(const GemmArgs& g, hipStream_t s)
 // for 8-bit blocks (dequantised on the way into LDS), the register-staged
 // kernel.
 template <int BM, int BN, int WN, int MODE>
-hipError_t launch_gemm_t(const GemmArgs& g, hipStream_t s)
+hipError_t launch_gemm_t(const GemmArgs& g, bool dma, hipStream_t s)
 {
     if (g.Bsc) return launch_gemm_q<BM, BN, WN, MODE, true>(g, s);
-    if constexpr (BM == 256) return launch_gemm_dma<BM, BN, WN, MODE>(g, s);
-    else return launch_gemm_q<BM, BN, WN, MODE, false>(g, s);
+    if constexpr (BM == 256) {
+        if (dma) return launch_gemm_dma<BM, BN, WN, MODE>(g, s);
+    }
+    return launch_gemm_q<BM, BN, WN, MODE, false>(g, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -1107,7 +1160,16 @@ int gemm_cu_count()
     return v;
 }
 
-int gemm_plan(int64_t M, int64_t N, int mode, bool q8)
+// The direct-to-LDS kernel runs whole 64-deep stages and addresses each
+// operand with 32-bit byte offsets below DMA_RANGE; A is [M][lda],
+// B [N (+ up_rows)][ldb], f16.
+static bool gemm_dma_fits(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t up_rows, int mode)
+{
+    const int64_t brows = N + (mode == GEMM_SWIGLU_F16 ? up_rows : 0);
+    return K % GDK == 0 && M * lda * 2 < DMA_RANGE && brows * ldb * 2 < DMA_RANGE;
+}
+
+int gemm_plan(int64_t M, int64_t N, int64_t K, int64_t up_rows, int mode, bool q8)
 {
     if (M <= 0 || N <= 0) return 0;
     // Tile by grid size (measured on the 8B shapes at 2048 and 4096 rows):
@@ -1127,10 +1189,12 @@ int gemm_plan(int64_t M, int64_t N, int mode, bool q8)
         const double r2 = double((t2 + cu - 1) / cu), r1 = double((t1 + cu - 1) / cu);
         if (r1 * 0.61 < r2 * 0.95) shape = 1;
     }
-    // f16 weights on 256-row tiles load straight into LDS; 8-bit blocks
-    // (dequantised on their way into LDS) and the smaller tiles use the
-    // register-staged kernel.
-    const int tile = shape == 2 ? (q8 ? GEMM_PLAN_256x256 : GEMM_PLAN_256x256_LDS)
+    // f16 weights on 256-row tiles load straight into LDS (where K is a
+    // multiple of 64 and the operands fit its 32-bit offsets; the operands
+    // are contiguous, K elements per row); 8-bit blocks (dequantised on their way into LDS)
+    // and the smaller tiles use the register-staged kernel.
+    const bool dma = !q8 && gemm_dma_fits(M, N, K, K, K, up_rows, mode);
+    const int tile = shape == 2 ? (dma ? GEMM_PLAN_256x256_LDS : GEMM_PLAN_256x256)
                      : shape == 1 ? GEMM_PLAN_128x256 : GEMM_PLAN_128x128;
     return tile | (q8 ? GEMM_PLAN_Q8_IN_GEMM : 0);
 }
@@ -1138,12 +1202,15 @@ int gemm_plan(int64_t M, int64_t N, int mode, bool q8)
 hipError_t launch_gemm(const GemmArgs& g, int mode, hipStream_t s)
 {
     if (g.M <= 0 || g.N <= 0) return hipSuccess;
-    const int plan = gemm_plan(g.M, g.N, mode, g.Bsc != nullptr) & GEMM_PLAN_TILE_MASK;
+    const int plan = gemm_plan(g.M, g.N, g.K, g.up_rows, mode, g.Bsc != nullptr) & GEMM_PLAN_TILE_MASK;
     const int shape = plan == GEMM_PLAN_128x128 ? 0 : plan == GEMM_PLAN_128x256 ? 1 : 2;
+    // the plan assumes contiguous operands; other strides are checked here
+    const bool dma = plan == GEMM_PLAN_256x256_LDS &&
+                     gemm_dma_fits(g.M, g.N, g.K, g.lda, g.ldb, g.up_rows, mode);
 #define DF_GEMM_BY_SHAPE(MODE_)                                                  \
-    return shape == 2   ? launch_gemm_t<256, 256, 4, MODE_>(g, s)                \
-           : shape == 1 ? launch_gemm_t<128, 256, 4, MODE_>(g, s)                \
-                        : launch_gemm_t<GBM_, GBN_, 2, MODE_>(g, s);
+    return shape == 2   ? launch_gemm_t<256, 256, 4, MODE_>(g, dma, s)           \
+           : shape == 1 ? launch_gemm_t<128, 256, 4, MODE_>(g, false, s)         \
+                        : launch_gemm_t<GBM_, GBN_, 2, MODE_>(g, false, s);
     switch (mode) {
     case GEMM_STORE_F32: DF_GEMM_BY_SHAPE(GEMM_STORE_F32)
     case GEMM_ADD_F32: DF_GEMM_BY_SHAPE(GEMM_ADD_F32)

@@ -1688,10 +1688,12 @@ df_status df_prefill_plan(const df_model* m, int32_t rows, int32_t* plan)
     const bool in_gemm = q8 && !first;
     const bool gemma = c.arch == DF_ARCH_GEMMA3;
     const int64_t N[4] = {qd + 2 * kvd, c.d_model, c.ffn_dim, c.d_model};
+    const int64_t K[4] = {c.d_model, qd, c.d_model, c.ffn_dim};
     const int mode[4] = {GEMM_STORE_F32, gemma ? GEMM_STORE_F32 : GEMM_ADD_F32, GEMM_SWIGLU_F16,
                          gemma ? GEMM_STORE_F32 : GEMM_ADD_F32};
     for (int i = 0; i < 4; ++i)
-        plan[i] = gemm_plan(rows, N[i], mode[i], in_gemm) | (first ? GEMM_PLAN_DEQUANT_FIRST : 0);
+        plan[i] = gemm_plan(rows, N[i], K[i], i == 2 ? c.ffn_dim : 0, mode[i], in_gemm) |
+                  (first ? GEMM_PLAN_DEQUANT_FIRST : 0);
     return DF_OK;
 }
 
