@@ -46,6 +46,9 @@ struct AttnItem {
     const float* sin_row;
     float* kc;             // this KV head's cache rows [max_ctx][hd]
     float* vc;
+    uint16_t* k16;         // this KV head's f16 copies (or null): rows [max_ctx][hd] and
+    uint16_t* vt16;        // V transposed [hd][max_ctx]
+    int ctx;               // max_ctx: the row stride of vt16
     int qd, kvd;           // widths of q and of k (= v) inside qkv
     int g;                 // KV head
     int p;                 // position of this step's row
@@ -217,6 +220,10 @@ __device__ void attn_run(const AttnItem& a, float* lds, int tid, AttnRows<HD, IT
                 if (j == G) {  // append k at slot p
                     *gmem(a.kc + int64_t(p) * HD + i0[r]) = y0;
                     *gmem(a.kc + int64_t(p) * HD + i1[r]) = y1;
+                    if (a.k16) {
+                        *gmem(a.k16 + int64_t(p) * HD + i0[r]) = f32_to_f16_bits(y0);
+                        *gmem(a.k16 + int64_t(p) * HD + i1[r]) = f32_to_f16_bits(y1);
+                    }
                 }
             }
         }
@@ -228,6 +235,7 @@ __device__ void attn_run(const AttnItem& a, float* lds, int tid, AttnRows<HD, IT
             if (a.bias) v += *gmem(a.bias + voff + i);
             vnew[i] = v;
             *gmem(a.vc + int64_t(p) * HD + i) = v;  // append v at slot p
+            if (a.vt16) *gmem(a.vt16 + int64_t(i) * a.ctx + p) = f32_to_f16_bits(v);
         }
     }
     __syncthreads();

@@ -169,6 +169,9 @@ attn_decode_kernel(AttnDecodeArgs a)
     it.sin_row = a.sin_t + int64_t(p) * (HD / 2);
     it.kc = a.kc + int64_t(g) * a.max_ctx * HD;
     it.vc = a.vc + int64_t(g) * a.max_ctx * HD;
+    it.k16 = a.k16 ? a.k16 + int64_t(g) * a.max_ctx * HD : nullptr;
+    it.vt16 = a.vt16 ? a.vt16 + int64_t(g) * HD * a.max_ctx : nullptr;
+    it.ctx = a.max_ctx;
     it.qd = a.n_heads * HD;
     it.kvd = a.n_kv * HD;
     it.g = g;

@@ -51,6 +51,9 @@ __device__ inline float f16_bits_to_f32(uint16_t b)
     return static_cast<float>(__builtin_bit_cast(_Float16, b));
 }
 
+// f16 bits of v, rounded to nearest even.
+__device__ inline uint16_t f32_to_f16_bits(float v) { return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v)); }
+
 // 2^x on the hardware exponential (v_exp_f32); softmax weights only, where
 // results below the normal range may flush to zero.
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }

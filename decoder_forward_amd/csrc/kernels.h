@@ -147,6 +147,8 @@ struct AttnDecodeArgs {
     const float* sin_t;
     float* kc;                 // this layer's K cache [n_kv][max_ctx][hd]
     float* vc;
+    uint16_t* k16;             // f16 copies for bulk prefill, or null: K [n_kv][max_ctx][hd],
+    uint16_t* vt16;            // V transposed [n_kv][hd][max_ctx]; the step's row p goes to both
     int max_ctx, n_heads, n_kv, head_dim;
     const int* state_pos;      // device int: position p
     float* part;               // [n_kv][ATTN_MAX_SPLIT] items of attn_part_stride floats
@@ -239,11 +241,31 @@ struct AttnPrefillArgs {
     const uint16_t* q16;  // [S][n_heads][hd] f16 (after RoPE)
     const float* kc;      // layer K cache [n_kv][max_ctx][hd]
     const float* vc;
+    const uint16_t* k16;  // the layer's f16 copies (KvShadowArgs), or null: then K and V are
+    const uint16_t* vt16; // read from kc / vc and rounded to f16 in the kernel
     uint16_t* out16;      // [S][n_heads * hd] f16
     int S, p0, n_heads, n_kv, head_dim, max_ctx;
     int window;           // > 0: each query sees the keys p - window < t <= p only
 };
 hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t s);
+
+// f16 copies of cache rows [pos0, pos0 + n) of one layer for the bulk-prefill
+// attention: k16[g][t][d] = f16(kc[g][t][d]) and vt16[g][d][t] =
+// f16(vc[g][t][d]) (V transposed, so that a tile of keys is contiguous per
+// dim); do_k / do_v select the halves. The same rounding as the conversion
+// the attention would otherwise do in LDS.
+struct KvShadowArgs {
+    const float* kc;
+    const float* vc;
+    uint16_t* k16;
+    uint16_t* vt16;
+    int pos0, n, n_kv, head_dim, max_ctx;
+    int do_k, do_v;
+};
+hipError_t launch_kv_shadow(const KvShadowArgs& a, hipStream_t s);
+// True when the bulk-prefill attention reads the f16 copies for this head
+// dim (the copies are then kept for every layer).
+inline bool kv_shadow_head_dim(int hd) { return hd == 64 || hd == 128; }
 
 // Deterministic pseudo-random values in [-1, 1) (f32, or f16 when f16 is
 // set): inputs for timing replays, whose power draw, and so clocks, depend

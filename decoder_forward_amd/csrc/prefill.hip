@@ -1099,15 +1099,337 @@ attn_prefill_kernel(AttnPrefillArgs a)
     }
 }
 
+// ---------------------------------------------------------------------------
+// The same causal flash attention for head_dim 64 and 128, reading the f16
+// copies of the cache (KvShadowArgs) with loads straight into LDS: no
+// conversion, no transposition and no staging registers in the kernel. A
+// 64-key tile holds K rows [64][hd] (16-byte chunks permuted by pf_swz_k) and
+// V transposed [hd][64] (chunks permuted by (d >> 1) & 7); two tile buffers,
+// the next tile's loads issued right after the barrier that opens the
+// current tile. Inside S^T = K Q^T the 16 K rows of key block kb are
+// permuted (pf_key) so that each lane's 8 P values of a 32-key half are 8
+// consecutive keys: the V operand of P V is then one 16-byte read per lane.
+// Everything else (work split, lazy maximum, masks, output) is as in
+// attn_prefill_kernel.
+// ---------------------------------------------------------------------------
+constexpr int PFD_TK = 64;  // keys per tile
+
+// Key (within the tile) of row m of key block kb in S^T: block kb = 2h + b
+// takes, for lane group j = m / 4, keys 32h + 8j + 4b .. +3.
+__device__ inline int pf_key(int kb, int m)
+{
+    return 32 * (kb >> 1) + (m >> 2) * 8 + (kb & 1) * 4 + (m & 3);
+}
+
+// Position of K chunk c of tile row r in its LDS row: c ^ pf_swz_k(r). The 16
+// lanes of a fragment read take the 16 rows pf_key(kb, 0..15) at one chunk;
+// a 16-byte-per-lane read is served 16 lanes at a time from 256 bytes of
+// banks. hd 128 (one 256-byte row per bank line): the 16 rows get 16
+// different positions. hd 64 (two rows per line): the 8 rows of each half
+// get 8 different positions.
+template <int HD>
+__device__ inline int pf_swz_k(int r)
+{
+    if constexpr (HD == 128) return ((r >> 1) & 12) | (r & 3);
+    else return ((r >> 1) & 1) | ((r >> 2) & 6);
+}
+
+// Raw buffer descriptor over `bytes` bytes from base (offsets at or past it
+// read zeros).
+__device__ inline __amdgpu_buffer_rsrc_t dma_rsrc_n(const uint16_t* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, int(bytes), BUF_RSRC_W3);
+}
+
+template <int HD, int G>
+__global__ void __launch_bounds__(attn_pf_threads<G>())
+attn_prefill_dma_kernel(AttnPrefillArgs a)
+{
+    static_assert(HD == 64 || HD == 128, "head_dim of the f16-copy attention");
+    constexpr int TK = PFD_TK;
+    constexpr int KB = TK / 16;             // 16-key blocks of a tile
+    constexpr int NP = TK / 32;             // 32-key halves: P V steps
+    constexpr int DB = HD / 16;             // 16-wide output blocks
+    constexpr int QB = attn_pf_rows<HD, G>();  // query rows per block
+    constexpr int RT = attn_pf_rt<HD>();    // 16-row tiles per wave
+    constexpr int WPH = attn_pf_wph<G>();   // waves per head
+    constexpr int NW = G * WPH;             // waves
+    constexpr int CPR = HD / 8;             // 16-byte chunks of a K row
+    constexpr int RPI = 64 / CPR;           // K rows one load instruction fills
+    constexpr int NK = TK / RPI;            // K load instructions per tile
+    constexpr int NV = HD / 8;              // V^T load instructions per tile (8 dims each)
+    constexpr int NI = NK + NV;
+    constexpr int MI = (NI + NW - 1) / NW;  // per wave, at most
+    constexpr int TILE = 2 * TK * HD;       // halves per tile buffer: K, then V^T
+    extern __shared__ _Float16 pfs[];
+    const int qb = gridDim.x - 1 - blockIdx.x;
+    const int g = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int l = tid & 63;
+    const int lg = l >> 4;    // lane group: keys 8 lg .. 8 lg + 7 of each 32
+    const int lq = l & 15;    // this lane's query within a row tile
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = g * G + w % G;  // query head
+    const int s0 = qb * QB;
+    const int r0 = (w / G) * (16 * RT);  // this wave's first row within the block
+    const uint16_t* khead = a.k16 + int64_t(g) * a.max_ctx * HD;
+    const uint16_t* vhead = a.vt16 + int64_t(g) * HD * a.max_ctx;
+
+    // Q fragments (the B operand of S^T), as in attn_prefill_kernel.
+    half8 qa[RT][HD / 32];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int s = s0 + r0 + rt * 16 + lq;
+#pragma unroll
+        for (int kq = 0; kq < HD / 32; ++kq) {
+            const int d = kq * 32 + lg * 8;
+            qa[rt][kq] = s < a.S ? *reinterpret_cast<const half8*>(a.q16 + (int64_t(s) * a.n_heads + j) * HD + d)
+                                 : half8{};
+        }
+    }
+    f32x4 o[RT][DB];
+    float mq[RT], lsum[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[rt][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+        mq[rt] = -INFINITY;
+        lsum[rt] = 0.f;
+    }
+
+    const int s_last = min(a.S, s0 + QB) - 1;
+    const int n_keys = a.p0 + s_last + 1;
+    const int tiles = (n_keys + TK - 1) / TK;
+    const int key_lo = a.window > 0 ? max(0, a.p0 + s0 - a.window + 1) : 0;
+    const int kt0 = key_lo / TK;
+    const int free_hi = a.p0 + s0 - (TK - 1);
+    const int free_lo = a.window > 0 ? a.p0 + s0 + QB - a.window : 0;
+
+    // This wave's load instructions q = w, w + NW, ...: q < NK fills K rows
+    // q*RPI .. +RPI-1 (lane l: row + l / CPR, position l % CPR); the others
+    // fill V^T dims 8 (q - NK) .. +7 (lane l: dim + l / 8, position l % 8).
+    // Byte offsets from the tile's first key, fixed for every tile.
+    uint32_t voff[MI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+        const int q = w + i * NW;
+        if (q < NK) {
+            const int row = q * RPI + l / CPR;
+            const int c = (l % CPR) ^ pf_swz_k<HD>(row);
+            voff[i] = uint32_t(row * HD + c * 8) * 2;
+        } else {
+            const int d = (q - NK) * 8 + (l >> 3);
+            const int c = (l & 7) ^ ((d >> 1) & 7);
+            voff[i] = uint32_t(int64_t(d) * a.max_ctx + c * 8) * 2;
+        }
+    }
+    // Loads of tile kt into buffer buf. K rows at or past n_keys read zeros
+    // (the descriptor ends there); V^T reads stop at the head's end, and keys
+    // past n_keys are weighted by exactly 0.
+    auto issue = [&](int kt, int buf) {
+        const int t0 = kt * TK;
+        const __amdgpu_buffer_rsrc_t rk = dma_rsrc_n(khead + int64_t(t0) * HD, uint32_t(n_keys - t0) * HD * 2);
+        const __amdgpu_buffer_rsrc_t rv = dma_rsrc_n(vhead + t0, uint32_t(int64_t(HD) * a.max_ctx - t0) * 2);
+        _Float16* base = pfs + buf * TILE;
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+            const int q = w + i * NW;
+            if (q < NK) dma16(rk, base + q * 512, voff[i], 0);
+            else if (q < NI) dma16(rv, base + TK * HD + (q - NK) * 512, voff[i], 0);
+        }
+    };
+
+    if (kt0 < tiles) issue(kt0, kt0 & 1);
+    for (int kt = kt0; kt < tiles; ++kt) {
+        const int t0 = kt * TK;
+        wait_vmcnt<0>();  // this wave's loads of tile kt
+        __syncthreads();  // every wave's: tile kt in LDS, and tile kt-1's buffer no longer read
+        if (kt + 1 < tiles) issue(kt + 1, (kt + 1) & 1);
+        const _Float16* Kl = pfs + (kt & 1) * TILE;
+        const _Float16* Vl = Kl + TK * HD;
+        // S^T[key = pf_key(kb, lg*4 + i)][query = rt*16 + l%16]
+        f32x4 st[RT][KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const int row = pf_key(kb, lq);
+            half8 kf[HD / 32];
+#pragma unroll
+            for (int kq = 0; kq < HD / 32; ++kq)
+                kf[kq] = *reinterpret_cast<const half8*>(Kl + row * HD + (((kq * 4 + lg) ^ pf_swz_k<HD>(row)) * 8));
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                st[rt][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kq = 0; kq < HD / 32; ++kq)
+                    st[rt][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[kq], qa[rt][kq], st[rt][kb], 0, 0, 0);
+            }
+        }
+        const bool masked = t0 > free_hi || t0 < free_lo;  // uniform
+        bool grow = false;
+        float vmax[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            if (masked) {
+                const int qpos = a.p0 + s0 + r0 + rt * 16 + lq;
+                const int kmin = a.window > 0 ? qpos - a.window + 1 : 0;
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int key = t0 + pf_key(kb, lg * 4 + i);
+                        if (key > qpos || key < kmin) st[rt][kb][i] = -INFINITY;
+                    }
+            }
+            float vm = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+                vm = fmaxf(vm, fmaxf(fmaxf(st[rt][kb][0], st[rt][kb][1]), fmaxf(st[rt][kb][2], st[rt][kb][3])));
+            vmax[rt] = vm;
+            grow |= vmax[rt] > mq[rt] + RESCALE_SLACK;
+        }
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                float rm = fmaxf(vmax[rt], __shfl_xor(vmax[rt], 16, WAVE));
+                rm = fmaxf(rm, __shfl_xor(rm, 32, WAVE));
+                const float mn = fmaxf(mq[rt], rm);
+                const float alpha = (mq[rt] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mq[rt] - mn);
+                lsum[rt] *= alpha;
+                mq[rt] = mn;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float ai = __shfl(alpha, lg * 4 + i, WAVE);
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) o[rt][db][i] *= ai;
+                }
+            }
+        }
+        // P in registers as the A operand of P V: step h, slot 4b + i holds
+        // key 32h + 8 lg + 4b + i, which is row lg*4 + i of key block 2h + b.
+        half8 pa[RT][NP];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const float mref = fmaxf(mq[rt], -1e30f);
+            float ps = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float pv = __builtin_amdgcn_exp2f(st[rt][kb][i] - mref);
+                    ps += pv;
+                    pa[rt][kb >> 1][(kb & 1) * 4 + i] = static_cast<_Float16>(pv);
+                }
+            lsum[rt] += ps;
+        }
+        // V fragments: B[slot][d = db*16 + l%16] = V^T[d][32h + 8 lg .. +7].
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const int d = db * 16 + lq;
+#pragma unroll
+            for (int h = 0; h < NP; ++h) {
+                const half8 vb = *reinterpret_cast<const half8*>(Vl + d * TK + (((h * 4 + lg) ^ ((d >> 1) & 7)) * 8));
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+                    o[rt][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[rt][h], vb, o[rt][db], 0, 0, 0);
+            }
+        }
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        float lt = lsum[rt] + __shfl_xor(lsum[rt], 16, WAVE);
+        lt += __shfl_xor(lt, 32, WAVE);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float li = __shfl(lt, lg * 4 + i, WAVE);
+            const int s = s0 + r0 + rt * 16 + lg * 4 + i;
+            if (s >= a.S) continue;
+            const float inv = 1.0f / li;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const int d = db * 16 + lq;
+                a.out16[int64_t(s) * a.n_heads * HD + j * HD + d] = f2h(o[rt][db][i] * inv);
+            }
+        }
+    }
+}
+
+// f16 copies of cache rows (KvShadowArgs): block (tile, g) takes 64 rows of
+// KV head g. K rows are converted in place, coalesced; V rows are converted
+// into LDS and written out transposed, 64 consecutive positions per dim (one
+// 128-byte run per wave store).
+constexpr int KVS_ROWS = 64;
+__global__ void __launch_bounds__(256)
+kv_shadow_kernel(KvShadowArgs a)
+{
+    __shared__ uint16_t vs[KVS_ROWS][256 + 2];  // [row][dim]; the pad puts a column's rows in distinct banks
+    const int g = blockIdx.y;
+    const int hd = a.head_dim;
+    const int r0 = a.pos0 + blockIdx.x * KVS_ROWS;
+    const int nr = min(KVS_ROWS, a.pos0 + a.n - r0);
+    const int64_t head = int64_t(g) * a.max_ctx * hd;
+    const int tid = threadIdx.x;
+    const int q4 = hd / 4;
+    for (int e = tid; e < nr * q4; e += 256) {
+        const int r = e / q4, c = (e % q4) * 4;
+        const int64_t off = head + int64_t(r0 + r) * hd + c;
+        if (a.do_k) {
+            const float4 k = *reinterpret_cast<const float4*>(a.kc + off);
+            *reinterpret_cast<uint2*>(a.k16 + off) = make_uint2(pack_h2(k.x, k.y), pack_h2(k.z, k.w));
+        }
+        if (a.do_v) {
+            const float4 v = *reinterpret_cast<const float4*>(a.vc + off);
+            *reinterpret_cast<uint32_t*>(&vs[r][c]) = pack_h2(v.x, v.y);
+            *reinterpret_cast<uint32_t*>(&vs[r][c + 2]) = pack_h2(v.z, v.w);
+        }
+    }
+    if (!a.do_v) return;  // uniform
+    __syncthreads();
+    const int lane = tid & 63, wv = tid >> 6;
+    if (lane < nr) {
+        uint16_t* vt = a.vt16 + int64_t(g) * hd * a.max_ctx + r0 + lane;
+        for (int d = wv; d < hd; d += 4) vt[int64_t(d) * a.max_ctx] = vs[lane][d];
+    }
+}
+
 template <int HD, int G>
 dim3 pf_grid(const AttnPrefillArgs& a)
 {
     return dim3((a.S + attn_pf_rows<HD, G>() - 1) / attn_pf_rows<HD, G>(), a.n_kv);
 }
 
+template <int HD, int G>
+hipError_t launch_attn_prefill_dma(const AttnPrefillArgs& a, hipStream_t s)
+{
+    constexpr size_t lds = size_t(2) * 2 * PFD_TK * HD * 2;
+    static std::atomic<bool> attr_set{false};  // sessions may launch from several threads
+    if (!attr_set.load(std::memory_order_acquire)) {
+        const hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_prefill_dma_kernel<HD, G>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+        if (r != hipSuccess) return r;
+        attr_set.store(true, std::memory_order_release);
+    }
+    DFK_LAUNCH((attn_prefill_dma_kernel<HD, G>), (pf_grid<HD, G>(a)), dim3(attn_pf_threads<G>()), lds, s, a);
+    return hipGetLastError();
+}
+
 template <int HD>
 hipError_t launch_attn_prefill_hd(const AttnPrefillArgs& a, hipStream_t s)
 {
+    if constexpr (HD == 64 || HD == 128) {
+        if (a.k16 && a.vt16) {
+            switch (a.n_heads / a.n_kv) {
+            case 1: return launch_attn_prefill_dma<HD, 1>(a, s);
+            case 2: return launch_attn_prefill_dma<HD, 2>(a, s);
+            case 3: return launch_attn_prefill_dma<HD, 3>(a, s);
+            case 4: return launch_attn_prefill_dma<HD, 4>(a, s);
+            case 5: return launch_attn_prefill_dma<HD, 5>(a, s);
+            case 6: return launch_attn_prefill_dma<HD, 6>(a, s);
+            case 7: return launch_attn_prefill_dma<HD, 7>(a, s);
+            case 8: return launch_attn_prefill_dma<HD, 8>(a, s);
+            default: return hipErrorInvalidValue;
+            }
+        }
+    }
     switch (a.n_heads / a.n_kv) {
     case 1: DFK_LAUNCH((attn_prefill_kernel<HD, 1>), (pf_grid<HD, 1>(a)), dim3(attn_pf_threads<1>()), 0, s, a); break;
     case 2: DFK_LAUNCH((attn_prefill_kernel<HD, 2>), (pf_grid<HD, 2>(a)), dim3(attn_pf_threads<2>()), 0, s, a); break;
@@ -1226,6 +1548,14 @@ hipError_t launch_qk_post_rows(const QkPostArgs& a, hipStream_t s)
     if (a.S <= 0) return hipSuccess;
     if (a.head_dim > 4 * WAVE) return hipErrorInvalidValue;  // two rope pairs per lane at most
     DFK_LAUNCH(qk_post_rows_kernel, dim3(a.S), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_shadow(const KvShadowArgs& a, hipStream_t s)
+{
+    if (a.n <= 0) return hipSuccess;
+    if (a.head_dim > 256 || a.head_dim % 4 != 0) return hipErrorInvalidValue;
+    DFK_LAUNCH(kv_shadow_kernel, dim3((a.n + KVS_ROWS - 1) / KVS_ROWS, a.n_kv), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -201,6 +201,10 @@ struct df_model {
     std::vector<Layer> layers;
     float* kc = nullptr;  // [L][n_kv][max_ctx][hd]
     float* vc = nullptr;
+    // f16 copies for the bulk-prefill attention (null where it reads kc / vc):
+    // K [L][n_kv][max_ctx][hd], V transposed [L][n_kv][hd][max_ctx]
+    uint16_t* k16 = nullptr;
+    uint16_t* vt16 = nullptr;
     float* cos_t = nullptr;  // [max_ctx][hd/2]
     float* sin_t = nullptr;
     float* cos_l = nullptr;  // local layers' table (rope_theta_local), else cos_t
@@ -716,9 +720,12 @@ bool build_weights(df_model* m, const std::map<std::string, const df_tensor*>& T
     return check(hipStreamSynchronize(m->stream), "upload", e);
 }
 
+bool bulk_supported(const df_model* m);
+
 // One conversation's device state (section "Memory lifecycle": the KV cache
-// is per conversation, sized to its max context): the KV cache, the decode
-// state, attention partials, argmax result and generated-token buffer.
+// is per conversation, sized to its max context): the KV cache (with its f16
+// copies where the bulk-prefill attention reads them), the decode state,
+// attention partials, argmax result and generated-token buffer.
 bool build_conversation(df_model* m, Fail* e)
 {
     const df_config& c = m->cfg;
@@ -729,6 +736,18 @@ bool build_conversation(df_model* m, Fail* e)
     m->vc = static_cast<float*>(dev_alloc(m, kv_elems * 4, "V cache", e));
     if (!m->vc) return false;
     m->kv_bytes = int64_t(kv_elems) * 8;
+    if (bulk_supported(m) && kv_shadow_head_dim(int(hd))) {
+        // zeroed: a tile's keys past the last written position are read (and
+        // weighted by 0), so they must hold finite values
+        m->k16 = static_cast<uint16_t*>(dev_alloc(m, kv_elems * 2, "K cache f16 copy", e));
+        if (!m->k16) return false;
+        m->vt16 = static_cast<uint16_t*>(dev_alloc(m, kv_elems * 2, "V cache f16 copy", e));
+        if (!m->vt16) return false;
+        if (!check(hipMemsetAsync(m->k16, 0, kv_elems * 2, m->stream), "K copy init", e) ||
+            !check(hipMemsetAsync(m->vt16, 0, kv_elems * 2, m->stream), "V copy init", e))
+            return false;
+        m->kv_bytes += int64_t(kv_elems) * 4;
+    }
     m->state = static_cast<DevState*>(dev_alloc(m, sizeof(DevState), "decode state", e));
     if (!m->state) return false;
     const int G = c.n_heads / c.n_kv_heads;
@@ -821,6 +840,8 @@ hipError_t launch_class(df_model* m, const StepBufs& b, int kernel, int l, int g
         a.window = L->local ? c.sliding_window : 0;
         a.kc = m->kc + size_t(l) * kv_layer;
         a.vc = m->vc + size_t(l) * kv_layer;
+        a.k16 = m->k16 ? m->k16 + size_t(l) * kv_layer : nullptr;
+        a.vt16 = m->vt16 ? m->vt16 + size_t(l) * kv_layer : nullptr;
         a.max_ctx = c.max_ctx;
         a.n_heads = c.n_heads;
         a.n_kv = c.n_kv_heads;
@@ -1037,6 +1058,17 @@ hipError_t pf_launch(df_model* m, const PfBufs& b, int kernel, int l, int S, int
         r = launch_qk_post_rows(qa, m->stream);
         if (r != hipSuccess) return r;
         AttnPrefillArgs aa{};
+        if (m->k16) {
+            // the f16 copies of the rows just appended
+            KvShadowArgs ka{};
+            ka.kc = qa.kc; ka.vc = qa.vc;
+            aa.k16 = ka.k16 = m->k16 + size_t(l) * kv_layer;
+            aa.vt16 = ka.vt16 = m->vt16 + size_t(l) * kv_layer;
+            ka.pos0 = p0; ka.n = S; ka.n_kv = c.n_kv_heads; ka.head_dim = hd; ka.max_ctx = c.max_ctx;
+            ka.do_k = ka.do_v = 1;
+            r = launch_kv_shadow(ka, m->stream);
+            if (r != hipSuccess) return r;
+        }
         aa.q16 = b.q16; aa.kc = qa.kc; aa.vc = qa.vc; aa.out16 = b.att16;
         aa.S = S; aa.p0 = p0; aa.n_heads = c.n_heads; aa.n_kv = c.n_kv_heads;
         aa.head_dim = hd; aa.max_ctx = c.max_ctx;
@@ -1543,6 +1575,23 @@ static df_status kv_copy(df_model* m, int32_t layer, int32_t which, int32_t pos0
         const size_t bytes = size_t(n) * c.head_dim * 4;
         hipError_t r = to_host ? hipMemcpyAsync(h, dev, bytes, hipMemcpyDeviceToHost, m->stream)
                                : hipMemcpyAsync(dev, h, bytes, hipMemcpyHostToDevice, m->stream);
+        if (r != hipSuccess) {
+            (void)hipGetLastError();
+            return set_err(m, DF_ERR_DEVICE, fmt("kv copy: %s", hipGetErrorString(r)));
+        }
+    }
+    if (!to_host && m->k16 && n > 0) {
+        // keep the f16 copies of the written rows current
+        const size_t kv_layer = size_t(c.n_kv_heads) * size_t(c.max_ctx) * size_t(c.head_dim);
+        KvShadowArgs ka{};
+        ka.kc = m->kc + size_t(layer) * kv_layer;
+        ka.vc = m->vc + size_t(layer) * kv_layer;
+        ka.k16 = m->k16 + size_t(layer) * kv_layer;
+        ka.vt16 = m->vt16 + size_t(layer) * kv_layer;
+        ka.pos0 = pos0; ka.n = n; ka.n_kv = c.n_kv_heads; ka.head_dim = c.head_dim; ka.max_ctx = c.max_ctx;
+        ka.do_k = which == 0;
+        ka.do_v = which == 1;
+        hipError_t r = launch_kv_shadow(ka, m->stream);
         if (r != hipSuccess) {
             (void)hipGetLastError();
             return set_err(m, DF_ERR_DEVICE, fmt("kv copy: %s", hipGetErrorString(r)));
