@@ -278,20 +278,24 @@ __device__ inline void fetch(const void* W, const uint16_t* scales, const MvLayo
     const int smask = (1 << L.log_s) - 1;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int64_t k = (int64_t((c.item & smask) * L.cps + c.within)) * CH + int64_t(lane) * E;
+        // the chunk's unit and row offsets are wave-uniform (scalar); only
+        // the lane's K offset (32-bit: K < 2^31) is per lane
+        const int k = ((c.item & smask) * L.cps + c.within) * int(CH) + lane * E;
         const int64_t unit = unit0 + (c.item >> L.log_s);
         // Chunks past the end are loaded from the start of W (a valid
-        // address) and never consumed: the loads stay unconditional, so the
-        // wait before consuming a batch can leave the next batch in flight
-        // (a branch around each load makes the compiler wait for all).
-        const bool ok = c.item < item_end && unit < L.n_out && k < L.K;
+        // address) and never consumed; lanes past K load from their row's
+        // start. The loads stay unconditional, so the wait before consuming
+        // a batch can leave the next batch in flight (a branch around each
+        // load makes the compiler wait for all).
+        const bool ok = c.item < item_end && unit < L.n_out;  // uniform
+        const int kl = (ok && k < int(L.K)) ? k : 0;
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
             const int64_t row = unit + (r == 1 ? L.up_rows : 0);
-            b.w[u][r] = load_w<WT>(W, ok ? row * L.K + k : 0);
+            b.w[u][r] = load_w<WT>(W, (ok ? row * L.K : 0) + kl);
             // the scale travels with its weights, so that no dependent load
             // is left for the consuming step
-            if constexpr (WT == W_Q8) b.s[u][r] = *gmem(scales + (ok ? row * (L.K >> 5) + (k >> 5) : 0));
+            if constexpr (WT == W_Q8) b.s[u][r] = *gmem(scales + (ok ? row * (L.K >> 5) : 0) + (kl >> 5));
         }
         advance(c, L.cps);
     }
@@ -418,13 +422,16 @@ __device__ inline void mv_finish(const uint16_t* scales, const void* W, const Mv
             if (st.uc.item >= st.item_end) break;
             const int64_t unit = st.unit0 + (st.uc.item >> L.log_s);
             if (unit >= L.n_out) break;
-            const int64_t k = (int64_t((st.uc.item & smask) * L.cps + st.uc.within)) * CH +
-                              int64_t(lane) * E;
-            if (k < L.K) {
+            // 32-bit: K < 2^31. A lane past K (only in a row's last chunk)
+            // reads the staged region's padding (whole chunks are
+            // allocated), and its product is dropped by a select rather than
+            // a branch around the dot.
+            const int k = ((st.uc.item & smask) * L.cps + st.uc.within) * int(CH) + lane * E;
+            const bool kin = k < int(L.K);
 #pragma unroll
-                for (int i = 0; i < NR; ++i)
-                    acc[i] += lane_dot<WT>(cb.w[u][i], hs + (k - int64_t(lane) * (E - 4)),
-                                           cb.s[WT == W_Q8 ? u : 0][i]);
+            for (int i = 0; i < NR; ++i) {
+                const float dv = lane_dot<WT>(cb.w[u][i], hs + (k - lane * (E - 4)), cb.s[WT == W_Q8 ? u : 0][i]);
+                acc[i] += kin ? dv : 0.f;
             }
             if (st.uc.within == L.cps - 1) {
 #pragma unroll
