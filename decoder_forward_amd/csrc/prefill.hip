@@ -1162,8 +1162,22 @@ attn_prefill_dma_kernel(AttnPrefillArgs a)
     constexpr int MI = (NI + NW - 1) / NW;  // per wave, at most
     constexpr int TILE = 2 * TK * HD;       // halves per tile buffer: K, then V^T
     extern __shared__ _Float16 pfs[];
-    const int qb = gridDim.x - 1 - blockIdx.x;
-    const int g = blockIdx.y;
+    // Blocks are dispatched to the 8 XCDs in turn (block b to XCD b % 8);
+    // XCD x takes the x-th eighth of the (head, query block) pairs in head
+    // order, so that its L2 holds one head's copies (2 MiB at 4096 rows and
+    // head_dim 128) rather than tiles of every head. Within a head, the
+    // latest query blocks (the most tiles) run first.
+    const int nqb = gridDim.x;
+    int qb, g;
+    {
+        const int total = nqb * int(gridDim.y);
+        const int b = blockIdx.x + blockIdx.y * nqb;
+        const int x = b & 7, y = b >> 3;
+        const int base = total >> 3, rem = total & 7;
+        const int t = x * base + min(x, rem) + y;
+        g = t / nqb;
+        qb = nqb - 1 - (t - g * nqb);
+    }
     const int tid = threadIdx.x;
     const int l = tid & 63;
     const int lg = l >> 4;    // lane group: keys 8 lg .. 8 lg + 7 of each 32
