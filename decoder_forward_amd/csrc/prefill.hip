@@ -1261,23 +1261,29 @@ attn_prefill_dma_kernel(AttnPrefillArgs a)
         if (kt + 1 < tiles) issue(kt + 1, (kt + 1) & 1);
         const _Float16* Kl = pfs + (kt & 1) * TILE;
         const _Float16* Vl = Kl + TK * HD;
-        // S^T[key = pf_key(kb, lg*4 + i)][query = rt*16 + l%16]
+        // S^T[key = pf_key(kb, lg*4 + i)][query = rt*16 + l%16]. Depth step
+        // kq outermost: the KB * RT accumulators in flight are independent,
+        // so no MFMA waits for the previous one's result.
         f32x4 st[RT][KB];
+        half8 kf[KB][HD / 32];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             const int row = pf_key(kb, lq);
-            half8 kf[HD / 32];
 #pragma unroll
             for (int kq = 0; kq < HD / 32; ++kq)
-                kf[kq] = *reinterpret_cast<const half8*>(Kl + row * HD + (((kq * 4 + lg) ^ pf_swz_k<HD>(row)) * 8));
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                st[rt][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kq = 0; kq < HD / 32; ++kq)
-                    st[rt][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[kq], qa[rt][kq], st[rt][kb], 0, 0, 0);
-            }
+                kf[kb][kq] = *reinterpret_cast<const half8*>(Kl + row * HD + (((kq * 4 + lg) ^ pf_swz_k<HD>(row)) * 8));
         }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) st[rt][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kq = 0; kq < HD / 32; ++kq)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+                    st[rt][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[kb][kq], qa[rt][kq], st[rt][kb], 0, 0, 0);
         const bool masked = t0 > free_hi || t0 < free_lo;  // uniform
         bool grow = false;
         float vmax[RT];
@@ -1336,11 +1342,12 @@ attn_prefill_dma_kernel(AttnPrefillArgs a)
             lsum[rt] += ps;
         }
         // V fragments: B[slot][d = db*16 + l%16] = V^T[d][32h + 8 lg .. +7].
+        // Half h outermost: consecutive MFMAs update different accumulators.
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            const int d = db * 16 + lq;
+        for (int h = 0; h < NP; ++h) {
 #pragma unroll
-            for (int h = 0; h < NP; ++h) {
+            for (int db = 0; db < DB; ++db) {
+                const int d = db * 16 + lq;
                 const half8 vb = *reinterpret_cast<const half8*>(Vl + d * TK + (((h * 4 + lg) ^ ((d >> 1) & 7)) * 8));
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
