@@ -1277,6 +1277,10 @@ attn_prefill_dma_kernel(AttnPrefillArgs a)
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) st[rt][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // The matrix sections run at raised wave priority: of the two waves
+        // of a SIMD, the one that reaches its MFMAs first keeps the matrix
+        // unit, and the other's softmax overlaps them.
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int kq = 0; kq < HD / 32; ++kq)
 #pragma unroll
@@ -1284,6 +1288,7 @@ attn_prefill_dma_kernel(AttnPrefillArgs a)
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
                     st[rt][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[kb][kq], qa[rt][kq], st[rt][kb], 0, 0, 0);
+        __builtin_amdgcn_s_setprio(0);
         const bool masked = t0 > free_hi || t0 < free_lo;  // uniform
         bool grow = false;
         float vmax[RT];
@@ -1343,6 +1348,7 @@ attn_prefill_dma_kernel(AttnPrefillArgs a)
         }
         // V fragments: B[slot][d = db*16 + l%16] = V^T[d][32h + 8 lg .. +7].
         // Half h outermost: consecutive MFMAs update different accumulators.
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int h = 0; h < NP; ++h) {
 #pragma unroll
@@ -1354,6 +1360,7 @@ attn_prefill_dma_kernel(AttnPrefillArgs a)
                     o[rt][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[rt][h], vb, o[rt][db], 0, 0, 0);
             }
         }
+        __builtin_amdgcn_s_setprio(0);
     }
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
