@@ -196,16 +196,30 @@ def prefill_classes(dfa, m, cfg, S):
     """Per-layer device time of each bulk-prefill launch class at S rows
     (df_time_prefill: every layer's launches once, back to back between HIP
     events) and the algorithmic flops of its GEMM (2 S N K; the causal
-    attention 2 S^2 hd n_heads, QK^T and PV over the lower triangle), then
-    the MFMA roofline of the dominant class, the gate/up GEMM. Runs after
-    decode timing, on an emptied cache (the replays write rows 0..S-1)."""
+    attention kernel 2 S^2 hd n_heads, QK^T and PV over the lower triangle)
+    against the MFMA peak, or for the row pass before the attention (bias /
+    norm_heads / rope, KV append, f16 copies of the new rows) its algorithmic
+    bytes against HBM; then the MFMA roofline of the dominant class, the
+    gate/up GEMM. Runs after decode timing, on an emptied cache (the replays
+    write rows 0..S-1)."""
     d, F, hd = cfg["d_model"], cfg["ffn_dim"], cfg["head_dim"]
     qd, kvd = cfg["n_heads"] * hd, cfg["n_kv_heads"] * hd
     flops = {"qkv": 2 * S * (qd + 2 * kvd) * d, "attn": 2 * S * S * hd * cfg["n_heads"],
              "o": 2 * S * d * qd, "gate_up": 2 * S * 2 * F * d, "down": 2 * S * d * F}
+    # row pass: read q|k|v f32, write q f16 and the K, V cache rows f32; the
+    # f16 copies (head_dim 64 and 128) read the new K, V rows and write them
+    # in f16
+    rows_bytes = S * (qd + 2 * kvd) * 4 + S * qd * 2 + 2 * S * kvd * 4
+    if hd in (64, 128):
+        rows_bytes += 2 * S * kvd * 4 + 2 * S * kvd * 2
     out = {}
-    for k in ("qkv", "attn", "o", "gate_up", "down"):
+    for k in ("qkv", "rows", "attn", "o", "gate_up", "down"):
         us = dfa.df_time_prefill(m.h, k, S, reps=1)
+        if k == "rows":
+            gbps = rows_bytes / (us * 1e-6) / 1e9
+            out[k] = {"mean_us_per_layer": round(us, 1), "gbps": round(gbps, 1),
+                      "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4), "bytes": rows_bytes}
+            continue
         out[k] = {"mean_us_per_layer": round(us, 1), "tflops": round(flops[k] / (us * 1e-6) / 1e12, 1),
                   "mfma_frac": round(flops[k] / (us * 1e-6) / 1e12 / PEAK_MFMA_F16_TFLOPS, 4)}
     log(f"[bench] prefill classes at S={S}: {json.dumps(out)}")

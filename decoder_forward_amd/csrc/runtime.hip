@@ -1011,7 +1011,8 @@ bool pf_buffers(df_model* m, int S, PfBufs* b, Fail* e)
 // The bulk-prefill launches of layer l for S rows at positions p0.., one
 // class at a time (the classes in step-list order):
 //   DF_K_PF_QKV     rms_norm rows -> f16, q/k/v GEMM
-//   DF_K_PF_ATTN    bias + norm_heads + rope + KV append, causal attention
+//   DF_K_PF_ROWS    bias + norm_heads + rope + KV append (+ the f16 copies)
+//   DF_K_PF_ATTN    causal attention
 //   DF_K_PF_O       o GEMM + residual add (gemma3: + rms_norm of o)
 //   DF_K_PF_GATE_UP rms_norm rows -> f16, gate/up GEMM + gate activation * up
 //   DF_K_PF_DOWN    down GEMM + residual add (gemma3: + rms_norm of down)
@@ -1047,7 +1048,7 @@ hipError_t pf_launch(df_model* m, const PfBufs& b, int kernel, int l, int S, int
         g.C = b.qkv; g.ldc = qd + 2 * kvd; g.N = qd + 2 * kvd; g.K = d;
         if (r == hipSuccess) r = launch_gemm(g, GEMM_STORE_F32, m->stream);
         return r;
-    case DF_K_PF_ATTN: {
+    case DF_K_PF_ROWS: {
         QkPostArgs qa{};
         qa.qkv = b.qkv; qa.q_norm = L.q_norm; qa.k_norm = L.k_norm; qa.eps = eps;
         qa.bias = L.bqkv; qa.adjacent = c.rope_pairing == DF_ROPE_ADJACENT;
@@ -1056,20 +1057,22 @@ hipError_t pf_launch(df_model* m, const PfBufs& b, int kernel, int l, int S, int
         qa.q16 = b.q16; qa.S = S; qa.p0 = p0; qa.n_heads = c.n_heads; qa.n_kv = c.n_kv_heads;
         qa.head_dim = hd; qa.max_ctx = c.max_ctx;
         r = launch_qk_post_rows(qa, m->stream);
-        if (r != hipSuccess) return r;
+        if (r != hipSuccess || !m->k16) return r;
+        // the f16 copies of the rows just appended
+        KvShadowArgs ka{};
+        ka.kc = qa.kc; ka.vc = qa.vc;
+        ka.k16 = m->k16 + size_t(l) * kv_layer;
+        ka.vt16 = m->vt16 + size_t(l) * kv_layer;
+        ka.pos0 = p0; ka.n = S; ka.n_kv = c.n_kv_heads; ka.head_dim = hd; ka.max_ctx = c.max_ctx;
+        ka.do_k = ka.do_v = 1;
+        return launch_kv_shadow(ka, m->stream);
+    }
+    case DF_K_PF_ATTN: {
         AttnPrefillArgs aa{};
-        if (m->k16) {
-            // the f16 copies of the rows just appended
-            KvShadowArgs ka{};
-            ka.kc = qa.kc; ka.vc = qa.vc;
-            aa.k16 = ka.k16 = m->k16 + size_t(l) * kv_layer;
-            aa.vt16 = ka.vt16 = m->vt16 + size_t(l) * kv_layer;
-            ka.pos0 = p0; ka.n = S; ka.n_kv = c.n_kv_heads; ka.head_dim = hd; ka.max_ctx = c.max_ctx;
-            ka.do_k = ka.do_v = 1;
-            r = launch_kv_shadow(ka, m->stream);
-            if (r != hipSuccess) return r;
-        }
-        aa.q16 = b.q16; aa.kc = qa.kc; aa.vc = qa.vc; aa.out16 = b.att16;
+        aa.k16 = m->k16 ? m->k16 + size_t(l) * kv_layer : nullptr;
+        aa.vt16 = m->vt16 ? m->vt16 + size_t(l) * kv_layer : nullptr;
+        aa.q16 = b.q16; aa.kc = m->kc + size_t(l) * kv_layer; aa.vc = m->vc + size_t(l) * kv_layer;
+        aa.out16 = b.att16;
         aa.S = S; aa.p0 = p0; aa.n_heads = c.n_heads; aa.n_kv = c.n_kv_heads;
         aa.head_dim = hd; aa.max_ctx = c.max_ctx;
         aa.window = L.local ? c.sliding_window : 0;
@@ -1109,7 +1112,8 @@ df_status prefill(df_model* m, const int32_t* tokens, int32_t n, float* logits)
     m->pool.reset();
     PfBufs b{};
     if (!pf_buffers(m, S, &b, &e)) return set_err(m, e.code, e.msg);
-    static const int classes[] = {DF_K_PF_QKV, DF_K_PF_ATTN, DF_K_PF_O, DF_K_PF_GATE_UP, DF_K_PF_DOWN};
+    static const int classes[] = {DF_K_PF_QKV, DF_K_PF_ROWS, DF_K_PF_ATTN, DF_K_PF_O, DF_K_PF_GATE_UP,
+                                  DF_K_PF_DOWN};
     hipError_t r = hipMemcpyAsync(b.toks, tokens, size_t(S) * 4, hipMemcpyHostToDevice, m->stream);
     if (r == hipSuccess) r = launch_embed(m->embd, b.toks, nullptr, S, b.x, m->stream, embed_scale(c));
     for (int l = 0; l < c.n_layers && r == hipSuccess; ++l)
@@ -1677,7 +1681,7 @@ df_status df_time_kernel(df_model* m, int32_t kernel, int32_t reps, double* mean
 
 df_status df_time_prefill(df_model* m, int32_t kernel, int32_t rows, int32_t reps, double* mean_us)
 {
-    if (!m || !mean_us || reps <= 0 || kernel < DF_K_PF_QKV || kernel > DF_K_PF_DOWN)
+    if (!m || !mean_us || reps <= 0 || kernel < DF_K_PF_QKV || kernel > DF_K_PF_ROWS)
         return DF_ERR_INVALID_ARGUMENT;
     if (rows < 1 || rows > m->cfg.max_ctx - m->kv_len)
         return set_err(m, DF_ERR_INVALID_ARGUMENT,
@@ -1704,8 +1708,11 @@ df_status df_time_prefill(df_model* m, int32_t kernel, int32_t rows, int32_t rep
     if (r == hipSuccess) r = launch_fill_random(b.qkv, int64_t(rows) * int64_t(qd + 2 * kvd), 0, 3u, m->stream);
     if (r == hipSuccess) r = launch_fill_random(b.att16, int64_t(rows) * int64_t(qd), 1, 4u, m->stream);
     if (r == hipSuccess) r = launch_fill_random(b.mid16, int64_t(rows) * c.ffn_dim, 1, 5u, m->stream);
-    if (r == hipSuccess) r = hipEventRecord(m->ev0, m->stream);
     const int nl = c.n_layers;
+    // the attention reads q and the cache rows the row pass writes
+    if (kernel == DF_K_PF_ATTN)
+        for (int l = 0; l < nl && r == hipSuccess; ++l) r = pf_launch(m, b, DF_K_PF_ROWS, l, rows, m->kv_len);
+    if (r == hipSuccess) r = hipEventRecord(m->ev0, m->stream);
     for (int rep = 0; rep < reps && r == hipSuccess; ++rep)
         for (int l = 0; l < nl && r == hipSuccess; ++l) r = pf_launch(m, b, kernel, l, rows, m->kv_len);
     if (r == hipSuccess) r = hipEventRecord(m->ev1, m->stream);

@@ -273,10 +273,12 @@ void* df_stream(const df_model* m);
 #define DF_K_COUNT 9
 /* Bulk-prefill launch classes, for df_time_prefill. */
 #define DF_K_PF_QKV 10      /* rms_norm rows + q/k/v GEMM */
-#define DF_K_PF_ATTN 11     /* bias / norm_heads / rope / KV append + causal attention */
+#define DF_K_PF_ATTN 11     /* causal attention */
 #define DF_K_PF_O 12        /* o GEMM + residual add */
 #define DF_K_PF_GATE_UP 13  /* rms_norm rows + gate/up GEMM + gate activation * up */
 #define DF_K_PF_DOWN 14     /* down GEMM + residual add */
+#define DF_K_PF_ROWS 15     /* row pass before the attention: bias / norm_heads / rope of q and k,
+                               KV append, and the cache's f16 copies of the new rows */
 
 /* Time every launch of one kernel class (enable = 1) with start / end
  * stamps taken by the kernel dispatch itself, or stop (enable = 0). The
@@ -301,13 +303,14 @@ df_status df_time_kernel(df_model* m, int32_t kernel, int32_t reps,
                          double* mean_us);
 
 /* Mean device time of one layer's launches of a bulk-prefill class
- * (DF_K_PF_QKV .. DF_K_PF_DOWN) for `rows` rows (1 .. max_ctx - kv_len) at
+ * (DF_K_PF_QKV .. DF_K_PF_ROWS) for `rows` rows (1 .. max_ctx - kv_len) at
  * positions kv_len .. kv_len+rows-1: each layer's launches in turn, `reps`
  * times, back to back between one pair of HIP events, on activation buffers
  * filled with pseudo-random values in [-1, 1) (the clocks depend on the
- * operands). DF_K_PF_ATTN writes the cache rows kv_len .. kv_len+rows-1,
+ * operands). DF_K_PF_ROWS writes the cache rows kv_len .. kv_len+rows-1,
  * which no later call reads before overwriting them, and kv_len is left as
- * it was, so the cached context stays intact. Needs f16 or 8-bit block
+ * it was, so the cached context stays intact; DF_K_PF_ATTN first runs the
+ * row pass once per layer, untimed, so that it attends over those rows. Needs f16 or 8-bit block
  * weights (else DF_ERR_UNSUPPORTED_OP). Synchronises. */
 df_status df_time_prefill(df_model* m, int32_t kernel, int32_t rows, int32_t reps,
                           double* mean_us);

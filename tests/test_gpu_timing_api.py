@@ -65,7 +65,7 @@ def test_time_kernel_then_forward_matches(dfa, kernel):
     m.close()
 
 
-@pytest.mark.parametrize("kernel", ["qkv", "attn", "o", "gate_up", "down"])
+@pytest.mark.parametrize("kernel", ["qkv", "rows", "attn", "o", "gate_up", "down"])
 def test_time_prefill_then_bulk_matches(dfa, kernel):
     cfg = synth.config("tiny", arch="qwen3", wdtype="f16", max_ctx=160)
     W = synth.make_weights(cfg)
