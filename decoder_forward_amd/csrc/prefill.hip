@@ -597,9 +597,11 @@ gemm_dma_kernel(GemmArgs g)
         const _Float16* a_lds = gsm + buf * (SA + SB);
         const _Float16* b_lds = a_lds + SA;
         auto pos = [&](int kk) { return ((kk * 2 + (l >> 5)) ^ ((l >> 1) & 7)) * 8; };
+        __builtin_amdgcn_s_setprio(1);
         mma_stage<MI, NI, GDK / 16, true>(
             acc, [&](int kk, int mi) { return a_lds + (wm * WTM + mi * 32 + (l & 31)) * GDK + pos(kk); },
             [&](int kk, int ni) { return b_lds + (wn * WTN + ni * 32 + (l & 31)) * GDK + pos(kk); });
+        __builtin_amdgcn_s_setprio(0);
     };
 
     // Prologue: stages 0 .. NB-2 in flight.
