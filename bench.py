@@ -111,20 +111,55 @@ def measured_traffic() -> dict | None:
         return None
 
 
-def pmc_summary(path: str, pattern: str) -> None:
+# MI355X: GRBM_GUI_ACTIVE counts cycles on each of the 8 XCDs (summed);
+# SQ_VALU_MFMA_BUSY_CYCLES sums the busy cycles of the 1024 SIMDs.
+N_XCD, N_SIMD = 8, 1024
+
+
+def pmc_summary(path: str, pattern: str, us_range=None) -> None:
     """Mean of each counter per dispatch over the kernels whose name contains
-    `pattern`, from a rocprofv3 --pmc csv output directory."""
+    `pattern` (and, with us_range, whose duration lies in [lo, hi] us), from
+    a rocprofv3 --pmc csv output directory, with the mean dispatch duration
+    and, where the counters are there, the clock (GRBM_GUI_ACTIVE per XCD over
+    the duration), the fraction of cycles the matrix cores are busy, and the
+    LDS bank-conflict share of LDS-active cycles."""
     import csv
     import glob
     files = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
-    acc: dict = {}
+    disp: dict = {}
     for f in files:
         for r in csv.DictReader(open(f)):
             if pattern in r["Kernel_Name"]:
-                acc.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+                d = disp.setdefault((f, r["Dispatch_Id"]), {
+                    "us": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3})
+                d[r["Counter_Name"]] = float(r["Counter_Value"])
+    if us_range:
+        lo, hi = us_range
+        disp = {k: d for k, d in disp.items() if lo <= d["us"] <= hi}
+    if not disp:
+        print("no dispatches")
+        return
+    acc: dict = {}
+    for d in disp.values():
+        for k, v in d.items():
+            acc.setdefault(k, []).append(v)
+    mean = {k: sum(v) / len(v) for k, v in acc.items()}
     for k, v in sorted(acc.items()):
-        print(f"{k}: dispatches {len(v)}, mean {sum(v) / len(v):.1f}, "
-              f"min {min(v):.1f}, max {max(v):.1f}")
+        if k != "us":
+            print(f"{k}: dispatches {len(v)}, mean {mean[k]:.1f}, min {min(v):.1f}, max {max(v):.1f}")
+    us = mean["us"]
+    print(f"duration: dispatches {len(acc['us'])}, mean {us:.2f} us, min {min(acc['us']):.2f}, "
+          f"max {max(acc['us']):.2f}")
+    gui = mean.get("GRBM_GUI_ACTIVE")
+    if gui:
+        cyc = gui / N_XCD
+        print(f"clock: {cyc / us / 1e3:.2f} GHz (GRBM_GUI_ACTIVE / {N_XCD} XCDs / duration)")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+            print(f"MFMA busy: {mean['SQ_VALU_MFMA_BUSY_CYCLES'] / (cyc * N_SIMD):.3f} of the cycles of "
+                  f"{N_SIMD} SIMDs")
+    if mean.get("SQ_LDS_IDX_ACTIVE"):
+        print(f"LDS bank conflicts: {mean.get('SQ_LDS_BANK_CONFLICT', 0.0) / mean['SQ_LDS_IDX_ACTIVE']:.3f} "
+              f"of LDS-active cycles")
 
 
 def copy_probe(mib: int) -> None:
@@ -476,9 +511,11 @@ def main():
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("DIR", "KERNEL"),
                     help="only summarise a rocprofv3 --pmc output directory")
+    ap.add_argument("--pmc-us", nargs=2, type=float, metavar=("LO", "HI"),
+                    help="with --pmc-summary: only dispatches lasting LO..HI us")
     args = ap.parse_args()
     if args.pmc_summary:
-        pmc_summary(*args.pmc_summary)
+        pmc_summary(*args.pmc_summary, us_range=args.pmc_us)
         return
     if args.copy_probe:
         copy_probe(args.copy_probe)

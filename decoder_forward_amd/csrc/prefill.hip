@@ -1240,8 +1240,9 @@ attn_prefill_dma_kernel(AttnPrefillArgs a)
         }
     }
     // Loads of tile kt into buffer buf. K rows at or past n_keys read zeros
-    // (the descriptor ends there); V^T reads stop at the head's end, and keys
-    // past n_keys are weighted by exactly 0.
+    // (the descriptor ends there); V^T reads stop at the head's end, so the
+    // last tile's V of keys past n_keys is whatever the copies hold there
+    // (earlier contents, possibly not finite) and is set to 0 in LDS.
     auto issue = [&](int kt, int buf) {
         const int t0 = kt * TK;
         const __amdgpu_buffer_rsrc_t rk = dma_rsrc_n(khead + int64_t(t0) * HD, uint32_t(n_keys - t0) * HD * 2);
@@ -1260,7 +1261,19 @@ attn_prefill_dma_kernel(AttnPrefillArgs a)
         const int t0 = kt * TK;
         wait_vmcnt<0>();  // this wave's loads of tile kt
         __syncthreads();  // every wave's: tile kt in LDS, and tile kt-1's buffer no longer read
-        if (kt + 1 < tiles) issue(kt + 1, (kt + 1) & 1);
+        if (kt + 1 < tiles) {
+            issue(kt + 1, (kt + 1) & 1);
+        } else if (t0 + TK > n_keys) {  // uniform
+            // The last tile's V of keys at or past n_keys: their P is 0, but
+            // 0 times a stale infinity is not, so they are set to 0 first.
+            _Float16* vz = pfs + (kt & 1) * TILE + TK * HD;
+            const int k0 = n_keys - t0;
+            for (int e = tid; e < HD * TK; e += NW * 64) {
+                const int d = e / TK, k = e % TK;
+                if (k >= k0) vz[d * TK + (((k >> 3) ^ ((d >> 1) & 7)) * 8) + (k & 7)] = static_cast<_Float16>(0.f);
+            }
+            __syncthreads();
+        }
         const _Float16* Kl = pfs + (kt & 1) * TILE;
         const _Float16* Vl = Kl + TK * HD;
         // S^T[key = pf_key(kb, lg*4 + i)][query = rt*16 + l%16]. Depth step
