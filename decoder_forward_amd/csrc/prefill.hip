@@ -6,8 +6,10 @@
 // matmuls are dense contractions, so they run on the CDNA4 matrix cores
 // (v_mfma_f32_32x32x16_f16: f16 operands, f32 accumulation); the activation
 // operands are rounded to f16 once, by the kernel that produces them.
-// Attention is a causal flash attention on v_mfma_f32_16x16x32_f16 that
-// reads the f32 KV cache and rounds K and V to f16 in LDS.
+// Attention is a causal flash attention on v_mfma_f32_16x16x32_f16. At
+// head_dim 64 and 128 it reads f16 copies of the KV cache (kept beside the
+// f32 cache by every path that writes a cache row) straight into LDS; at
+// other head sizes it reads the f32 cache and rounds K and V to f16 in LDS.
 #include "kernels.h"
 
 #include <atomic>
