@@ -44,7 +44,7 @@ KERNELS = {"embed": 0, "qkv": 1, "attn": 2, "o": 3, "gate_up": 4, "down": 5,
            "logits": 6, "argmax": 7, "attn_merge": 8}
 PREFILL_KERNELS = {"qkv": 10, "attn": 11, "o": 12, "gate_up": 13, "down": 14, "rows": 15}
 # df_prefill_plan tile codes and flags.
-GEMM_TILES = {1: "128x128", 2: "128x256", 3: "256x256", 4: "256x256_lds"}
+GEMM_TILES = {1: "128x128", 2: "128x256", 3: "256x256", 4: "256x256_lds", 5: "256x192_lds"}
 DF_GEMM_TILE_MASK, DF_GEMM_Q8_IN_GEMM, DF_GEMM_Q8_DEQUANT_FIRST = 15, 16, 32
 
 

@@ -206,6 +206,7 @@ enum GemmPlan {
     GEMM_PLAN_128x256 = 2,      // 8 waves, register-staged
     GEMM_PLAN_256x256 = 3,      // 8 waves, register-staged (8-bit weights)
     GEMM_PLAN_256x256_LDS = 4,  // 8 waves, operand tiles loaded straight into LDS
+    GEMM_PLAN_256x192_LDS = 5,  // 8 waves (64 x 96 each), loaded straight into LDS
     GEMM_PLAN_TILE_MASK = 15,
     GEMM_PLAN_Q8_IN_GEMM = 16,  // weight tiles dequantised on their way into LDS
     GEMM_PLAN_DEQUANT_FIRST = 32,  // 8-bit weights converted to f16 before the GEMM (runtime)

@@ -12,6 +12,7 @@
 // other head sizes it reads the f32 cache and rounds K and V to f16 in LDS.
 #include "kernels.h"
 
+#include <algorithm>
 #include <atomic>
 #include <type_traits>
 
@@ -511,12 +512,12 @@ __device__ inline void dma16(__amdgpu_buffer_rsrc_t r, _Float16* dst, uint32_t v
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst), 16, voff, soff, 0, 0);
 }
 
-template <int BM, int BN, int WN, int MODE>
-__global__ void __launch_bounds__(128 * WN)
+template <int BM, int BN, int WM, int WN, int MODE>
+__global__ void __launch_bounds__(64 * WM * WN)
 gemm_dma_kernel(GemmArgs g)
 {
-    constexpr int NW = 2 * WN;                 // waves: 2 x WN grid
-    constexpr int WTM = BM / 2, WTN = BN / WN;
+    constexpr int NW = WM * WN;                // waves: WM x WN grid
+    constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int MI = WTM / 32, NI = WTN / 32;
     constexpr int NB = gemm_dma_stages<BM, BN>();
     constexpr int IA = BM / (8 * NW), IB = BN / (8 * NW);  // 8-row load instructions per wave per stage
@@ -639,20 +640,21 @@ hipError_t launch_gemm_q(const GemmArgs& g, hipStream_t s)
     return hipGetLastError();
 }
 
-template <int BM, int BN, int WN, int MODE>
+template <int BM, int BN, int WM, int WN, int MODE>
 hipError_t launch_gemm_dma(const GemmArgs& g, hipStream_t s)
 {
     constexpr size_t lds = gemm_dma_lds_bytes<BM, BN>();
     static std::atomic<bool> attr_set{false};  // sessions may launch from several threads
     if (!attr_set.load(std::memory_order_acquire)) {
-        const hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_dma_kernel<BM, BN, WN, MODE>),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+        const hipError_t r = hipFuncSetAttribute(
+            reinterpret_cast<const void*>(&gemm_dma_kernel<BM, BN, WM, WN, MODE>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
         if (r != hipSuccess) return r;
         attr_set.store(true, std::memory_order_release);
     }
     constexpr int ncols = (MODE == GEMM_SWIGLU_F16) ? BN / 2 : BN;
     const int blocks = ((g.N + ncols - 1) / ncols) * ((g.M + BM - 1) / BM);
-    DFK_LAUNCH((gemm_dma_kernel<BM, BN, WN, MODE>), dim3(blocks), dim3(128 * WN), lds, s, g);
+    DFK_LAUNCH((gemm_dma_kernel<BM, BN, WM, WN, MODE>), dim3(blocks), dim3(64 * WM * WN), lds, s, g);
     return hipGetLastError();
 }
 
@@ -666,7 +668,7 @@ hipError_t launch_gemm_t(const GemmArgs& g, bool dma, hipStream_t s)
 {
     if (g.Bsc) return launch_gemm_q<BM, BN, WN, MODE, true>(g, s);
     if constexpr (BM == 256) {
-        if (dma) return launch_gemm_dma<BM, BN, WN, MODE>(g, s);
+        if (dma) return launch_gemm_dma<BM, BN, 2, WN, MODE>(g, s);
     }
     return launch_gemm_q<BM, BN, WN, MODE, false>(g, s);
 }
@@ -1539,30 +1541,36 @@ static bool gemm_dma_fits(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t 
 int gemm_plan(int64_t M, int64_t N, int64_t K, int64_t up_rows, int mode, bool q8)
 {
     if (M <= 0 || N <= 0) return 0;
-    // Tile by grid size (measured on the 8B shapes at 2048 and 4096 rows):
-    // 256 x 256 on 8 waves (two per SIMD, 128 x 64 wave tiles) from about
-    // 160 tiles up; 128 x 256 on 8 waves (64 x 64 wave tiles) below that;
-    // 128 x 128 on 4 waves for small problems.
+    // Every large tile runs one block per compute unit, so a GEMM takes
+    // ceil(tiles / units) rounds of its tile's time. Tile times relative to
+    // a 256 x 256 tile (8 waves of 128 x 64), measured on the 8B shapes:
+    // 128 x 256 (8 waves of 64 x 64) 0.68, 256 x 192 (8 waves of 64 x 96,
+    // operands loaded straight into LDS; not with the SwiGLU epilogue) 0.88.
+    // The fewest estimated tile-times win, 256 x 256 unless another is 5%
+    // faster; 128 x 128 on 4 waves for small problems. E.g. q/k/v of the 8B
+    // shapes (N 6144) at 4096 rows: 384 tiles of 256 x 256 in 2 rounds (2),
+    // 768 of 128 x 256 in 3 (2.04), 512 of 256 x 192 in 2 full rounds (1.76).
     const int64_t cols = mode == GEMM_SWIGLU_F16 ? 128 : 256;  // output columns of a 256-wide B tile
     const int64_t nt = (N + cols - 1) / cols;
-    int shape = int64_t((M + 255) / 256) * nt >= 160 ? 2 : int64_t((M + 127) / 128) * nt >= 64 ? 1 : 0;
-    // Both large shapes run one block per compute unit. A 256 x 256 grid
-    // whose last round of tiles is part-empty can finish sooner as 128 x 256
-    // tiles, which take about 0.61 of the time of a 256 x 256 tile here
-    // (q/k/v at 4096 rows of the 8B shapes: 384 tiles in 2 rounds, 768 in 3).
-    if (shape == 2) {
-        const int64_t cu = gemm_cu_count();
-        const int64_t t2 = ((M + 255) / 256) * nt, t1 = ((M + 127) / 128) * nt;
-        const double r2 = double((t2 + cu - 1) / cu), r1 = double((t1 + cu - 1) / cu);
-        if (r1 * 0.61 < r2 * 0.95) shape = 1;
-    }
+    const int64_t cu = gemm_cu_count();
+    const int64_t t2 = ((M + 255) / 256) * nt, t1 = ((M + 127) / 128) * nt;
     // f16 weights on 256-row tiles load straight into LDS (where K is a
     // multiple of 64 and the operands fit its 32-bit offsets; the operands
     // are contiguous, K elements per row); 8-bit blocks (dequantised on their way into LDS)
     // and the smaller tiles use the register-staged kernel.
     const bool dma = !q8 && gemm_dma_fits(M, N, K, K, K, up_rows, mode);
-    const int tile = shape == 2 ? (dma ? GEMM_PLAN_256x256_LDS : GEMM_PLAN_256x256)
-                     : shape == 1 ? GEMM_PLAN_128x256 : GEMM_PLAN_128x128;
+    int tile = GEMM_PLAN_128x128;
+    if (t1 >= 64) {
+        const double r2 = double((t2 + cu - 1) / cu);
+        const double r1 = double((t1 + cu - 1) / cu) * 0.68;
+        double r3 = 1e30;
+        if (dma && mode != GEMM_SWIGLU_F16) {
+            const int64_t t3 = ((M + 255) / 256) * ((N + 191) / 192);
+            r3 = double((t3 + cu - 1) / cu) * 0.88;
+        }
+        if (std::min(r1, r3) >= r2 * 0.95) tile = dma ? GEMM_PLAN_256x256_LDS : GEMM_PLAN_256x256;
+        else tile = r3 < r1 ? GEMM_PLAN_256x192_LDS : GEMM_PLAN_128x256;
+    }
     return tile | (q8 ? GEMM_PLAN_Q8_IN_GEMM : 0);
 }
 
@@ -1572,8 +1580,21 @@ hipError_t launch_gemm(const GemmArgs& g, int mode, hipStream_t s)
     const int plan = gemm_plan(g.M, g.N, g.K, g.up_rows, mode, g.Bsc != nullptr) & GEMM_PLAN_TILE_MASK;
     const int shape = plan == GEMM_PLAN_128x128 ? 0 : plan == GEMM_PLAN_128x256 ? 1 : 2;
     // the plan assumes contiguous operands; other strides are checked here
-    const bool dma = plan == GEMM_PLAN_256x256_LDS &&
-                     gemm_dma_fits(g.M, g.N, g.K, g.lda, g.ldb, g.up_rows, mode);
+    const bool fits = gemm_dma_fits(g.M, g.N, g.K, g.lda, g.ldb, g.up_rows, mode);
+    const bool dma = plan == GEMM_PLAN_256x256_LDS && fits;
+    if (plan == GEMM_PLAN_256x192_LDS && mode != GEMM_SWIGLU_F16) {
+        switch (mode) {
+        case GEMM_STORE_F32:
+            return fits ? launch_gemm_dma<256, 192, 4, 2, GEMM_STORE_F32>(g, s)
+                        : launch_gemm_t<128, 256, 4, GEMM_STORE_F32>(g, false, s);
+        case GEMM_ADD_F32:
+            return fits ? launch_gemm_dma<256, 192, 4, 2, GEMM_ADD_F32>(g, s)
+                        : launch_gemm_t<128, 256, 4, GEMM_ADD_F32>(g, false, s);
+        case GEMM_STORE_F16:
+            return fits ? launch_gemm_dma<256, 192, 4, 2, GEMM_STORE_F16>(g, s)
+                        : launch_gemm_t<128, 256, 4, GEMM_STORE_F16>(g, false, s);
+        }
+    }
 #define DF_GEMM_BY_SHAPE(MODE_)                                                  \
     return shape == 2   ? launch_gemm_t<256, 256, 4, MODE_>(g, dma, s)           \
            : shape == 1 ? launch_gemm_t<128, 256, 4, MODE_>(g, false, s)         \

@@ -16,6 +16,7 @@ static_assert(dfk::MAX_WIDTH == DF_MAX_WIDTH, "kernel width limit matches the he
 static_assert(dfk::GEMM_PLAN_128x128 == DF_GEMM_T128x128 && dfk::GEMM_PLAN_128x256 == DF_GEMM_T128x256 &&
                   dfk::GEMM_PLAN_256x256 == DF_GEMM_T256x256 &&
                   dfk::GEMM_PLAN_256x256_LDS == DF_GEMM_T256x256_LDS &&
+                  dfk::GEMM_PLAN_256x192_LDS == DF_GEMM_T256x192_LDS &&
                   dfk::GEMM_PLAN_TILE_MASK == DF_GEMM_TILE_MASK &&
                   dfk::GEMM_PLAN_Q8_IN_GEMM == DF_GEMM_Q8_IN_GEMM &&
                   dfk::GEMM_PLAN_DEQUANT_FIRST == DF_GEMM_Q8_DEQUANT_FIRST,

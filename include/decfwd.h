@@ -189,8 +189,10 @@ df_status df_session(const df_model* model, int32_t max_ctx, const df_options* o
  * n == 1 runs the decode path; n > 1 runs bulk prefill on matrix cores
  * (f16 or 8-bit block weights; 8-bit blocks are dequantised to f16 on the
  * way into the GEMM; f32 weights run the decode path n times), which matches
- * n single calls within the prefill tolerance. Arguments are
- * checked before any launch; on error kv_len is unchanged. Stream-ordered:
+ * n single calls within the prefill tolerance. Arguments are checked
+ * before any launch (n < 1 or a NULL `tokens` is DF_ERR_INVALID_ARGUMENT,
+ * kv_len + n > max_ctx DF_ERR_CONTEXT_FULL, an id outside [0, vocab)
+ * DF_ERR_INVALID_ARGUMENT); on error kv_len is unchanged. Stream-ordered:
  * the host may reuse `tokens` on return. */
 df_status df_forward(df_model* m, const int32_t* tokens, int32_t n,
                      float* logits_dev);
@@ -324,6 +326,7 @@ df_status df_time_prefill(df_model* m, int32_t kernel, int32_t rows, int32_t rep
 #define DF_GEMM_T128x256 2        /* 8 waves, staged through registers */
 #define DF_GEMM_T256x256 3        /* 8 waves, staged through registers */
 #define DF_GEMM_T256x256_LDS 4    /* 8 waves, operand tiles loaded straight into LDS */
+#define DF_GEMM_T256x192_LDS 5    /* 8 waves of 64 x 96, loaded straight into LDS */
 #define DF_GEMM_TILE_MASK 15
 #define DF_GEMM_Q8_IN_GEMM 16     /* 8-bit weight tiles dequantised on their way into LDS */
 #define DF_GEMM_Q8_DEQUANT_FIRST 32 /* 8-bit matrices converted to f16 before the GEMM */

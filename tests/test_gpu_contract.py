@@ -9,6 +9,10 @@
   failed load took given back.
 * "Shutdown": no leaks; free device memory is the same after every one of
   20 load / forward / free cycles.
+* positions run up to max_ctx - 1: the cache filled by one bulk call, and
+  by a bulk call plus decode steps, matches the oracle; one more token is
+  DF_ERR_CONTEXT_FULL with the cache unchanged; an empty call is
+  DF_ERR_INVALID_ARGUMENT.
 * the greedy token (page "Local inference and architectures", "Choosing the
   engine": temperature 0): df_argmax on crafted vectors takes the lowest
   index among equal maxima wherever they sit in the per-block partition,
@@ -187,3 +191,50 @@ def test_argmax_ties_and_nans(dfa):
         got = dfa.df_argmax(h, torch.from_numpy(v).to("cuda"))
         assert got == int(np.argmax(v)), k
     dfa.df_free(h)
+
+
+@pytest.mark.parametrize("arch,hd", [("qwen3", 128), ("llama", 64)])
+def test_filling_the_cache_to_max_ctx(dfa, arch, hd):
+    """Positions up to max_ctx - 1 (reading 6: overflow is an error, nothing
+    wraps): a bulk prefill that fills the whole cache in one call, and a
+    bulk prefill plus decode steps that reach the last slot, against the
+    oracle; one more token is CONTEXT_FULL and leaves the cache as it was;
+    an empty call is INVALID_ARGUMENT."""
+    import oracle
+    from parity import first_argmax, rel_l2
+    P = 130  # two 64-key tiles and a ragged third
+    cfg = synth.config("tiny", arch=arch, wdtype="f16", head_dim=hd, n_heads=4, n_kv_heads=2, max_ctx=P)
+    W = synth.make_weights(cfg)
+    toks = synth.make_prompt(cfg, P, stream=5)
+    say(f"[tiny {arch} f16, head_dim {hd}, max_ctx {P}] bulk of {P}; bulk of {P - 3} + 3 decode steps")
+    om = oracle.Model(cfg, W, max_ctx=P)
+    refs = [om.forward([t]) for t in toks]
+    m = dfa.Model(cfg, W)
+    got = m.forward(toks).cpu().numpy().copy()
+    assert m.kv_len == P
+    e = rel_l2(got, refs[-1])
+    say(f"  bulk of {P}: rel-L2 {e:.2e}")
+    assert e <= 5e-3 and first_argmax(got) == first_argmax(refs[-1])
+    before = m.read_kv(0, 0, 0, P)
+    with pytest.raises(dfa.DecFwdError) as ei:
+        m.forward([int(toks[0])])
+    assert ei.value.status == "CONTEXT_FULL"
+    assert m.kv_len == P and np.array_equal(m.read_kv(0, 0, 0, P), before)
+    m.reset()
+    got = m.forward(toks[:P - 3]).cpu().numpy().copy()
+    assert rel_l2(got, refs[P - 4]) <= 5e-3
+    for i in range(P - 3, P):
+        got = m.forward([int(toks[i])]).cpu().numpy().copy()
+        e = rel_l2(got, refs[i])
+        say(f"  decode at position {i}: rel-L2 {e:.2e}")
+        assert e <= 5e-3 and first_argmax(got) == first_argmax(refs[i])
+    assert m.kv_len == P
+    with pytest.raises(dfa.DecFwdError) as ei:
+        m.forward(toks[:2])
+    assert ei.value.status == "CONTEXT_FULL"
+    with pytest.raises(dfa.DecFwdError) as ei:
+        m.forward(np.zeros(0, np.int32))
+    assert ei.value.status == "INVALID_ARGUMENT"
+    assert m.kv_len == P
+    m.close()
+    om.close()
