@@ -46,6 +46,7 @@ PREFILL_KERNELS = {"qkv": 10, "attn": 11, "o": 12, "gate_up": 13, "down": 14, "r
 # df_prefill_plan tile codes and flags.
 GEMM_TILES = {1: "128x128", 2: "128x256", 3: "256x256", 4: "256x256_lds", 5: "256x192_lds"}
 DF_GEMM_TILE_MASK, DF_GEMM_Q8_IN_GEMM, DF_GEMM_Q8_DEQUANT_FIRST = 15, 16, 32
+DF_GEMM_SPLIT_SHIFT, DF_GEMM_SPLIT_MASK = 8, 0xF00
 
 
 class DecFwdError(RuntimeError):
@@ -293,13 +294,13 @@ def df_time_prefill(h, kernel: str, rows: int, reps: int = 2) -> float:
 def df_prefill_plan(h, rows: int) -> dict:
     """The GEMM kernels a bulk prefill of `rows` rows runs: for each of
     qkv / o / gate_up / down, (tile name, 8-bit in-GEMM dequantisation,
-    8-bit dequantised first)."""
+    8-bit dequantised first, work-groups per tile along K)."""
     plan = (C.c_int32 * 4)()
     _check(lib().df_prefill_plan(h, rows, plan), h)
     out = {}
     for k, v in zip(("qkv", "o", "gate_up", "down"), plan):
         out[k] = (GEMM_TILES.get(v & DF_GEMM_TILE_MASK), bool(v & DF_GEMM_Q8_IN_GEMM),
-                  bool(v & DF_GEMM_Q8_DEQUANT_FIRST))
+                  bool(v & DF_GEMM_Q8_DEQUANT_FIRST), (v & DF_GEMM_SPLIT_MASK) >> DF_GEMM_SPLIT_SHIFT)
     return out
 
 

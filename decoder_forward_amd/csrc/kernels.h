@@ -196,6 +196,14 @@ struct GemmArgs {
     // f16 (scale * q) on their way into LDS. Null for f16 weights.
     const uint16_t* Bsc;
     int act;                   // GEMM_SWIGLU_F16's gate activation (GateAct)
+    // K split of small grids (register-staged tiles; launch_gemm fills split
+    // from gemm_plan when ws and tickets are given): `split` work-groups per
+    // tile, each on a contiguous range of K stages, store their partial sums
+    // in ws; the last of a tile's work-groups to finish adds them in split
+    // order and runs the epilogue.
+    float* ws;                 // gemm_split_ws_bytes(...) bytes (device)
+    int* tickets;              // >= GEMM_SPLIT_TICKETS ints, zero (device); left zero
+    int split;
 };
 hipError_t launch_gemm(const GemmArgs& g, int mode, hipStream_t s);
 // The GEMM kernel launch_gemm runs for an M x N problem in `mode` (q8:
@@ -210,8 +218,13 @@ enum GemmPlan {
     GEMM_PLAN_TILE_MASK = 15,
     GEMM_PLAN_Q8_IN_GEMM = 16,  // weight tiles dequantised on their way into LDS
     GEMM_PLAN_DEQUANT_FIRST = 32,  // 8-bit weights converted to f16 before the GEMM (runtime)
+    GEMM_PLAN_SPLIT_SHIFT = 8,  // bits 8..11: work-groups per tile along K (1: no split)
+    GEMM_PLAN_SPLIT_MASK = 0xF00,
 };
 int gemm_plan(int64_t M, int64_t N, int64_t K, int64_t up_rows, int mode, bool q8);
+constexpr int GEMM_SPLIT_TICKETS = 1024;
+// Bytes of partial sums the plan's split needs (0 without a split).
+size_t gemm_split_ws_bytes(int64_t M, int64_t N, int64_t K, int64_t up_rows, int mode, bool q8);
 
 // 8-bit block rows to f16 rows: out[r][k] = f16(scale[r][k / 32] * q[r][k]),
 // the values the 8-bit GEMM stores in LDS; cols a multiple of 32.

@@ -31,6 +31,43 @@ __device__ inline uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, st
 // Two floats rounded to f16, a in the low half.
 __device__ inline uint32_t pack_h2(float a, float b) { return uint32_t(f2h(a)) | (uint32_t(f2h(b)) << 16); }
 
+// Hand-off between the work-groups of a split GEMM tile, which may run on
+// different XCDs (whose L2s are not coherent with each other): partial sums
+// are stored and loaded 16 bytes per lane with the cache policy of an
+// agent-scope atomic (sc1: at the coherence point, past the XCD's L2), and a
+// work-group takes its ticket only after every wave's stores are
+// acknowledged. No fence writes back or invalidates a whole L2.
+constexpr int CPOL_SC1 = 16;
+__device__ inline __amdgpu_buffer_rsrc_t ws_rsrc(float* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, int(bytes), 0x00020000);
+}
+__device__ inline void st_agent16(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, int(off), 0, CPOL_SC1);
+}
+__device__ inline f32x4 ld_agent16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, CPOL_SC1));
+}
+// True in the last of `n` work-groups to call it on `counter` (in all their
+// threads), which also resets the counter to 0. Call after every thread
+// has issued its hand-off stores.
+__device__ inline bool last_of(int* counter, int n, int* flag_lds)
+{
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        typedef __attribute__((address_space(1))) int gint;
+        const int prev = __hip_atomic_fetch_add((gint*)counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = prev == n - 1;
+        if (last) __hip_atomic_store((gint*)counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *flag_lds = last;
+    }
+    __syncthreads();
+    return *flag_lds != 0;
+}
+
 template <int CTRL>
 __device__ inline float dpp_f(float v)
 {
@@ -139,6 +176,7 @@ dequant_q8_kernel(const int8_t* __restrict__ q, const uint16_t* __restrict__ sc,
 // sums, and writes f16(silu(g) * u).
 // ---------------------------------------------------------------------------
 constexpr int GBK = 64, GPAD = GBK + 8;
+constexpr int GEMM_SPLIT_MAX = 4;  // work-groups per tile along K, at most
 // Work-group tile of the prefill GEMMs for small problems (fewer than about
 // one 256 x 256 tile per compute unit): 128 x 128 on 4 waves.
 constexpr int GBM_ = 128, GBN_ = 128;
@@ -280,6 +318,70 @@ __device__ inline void mma_stage(f32x16 (&acc)[MI][NI], FA afrag, FB bfrag)
     }
 }
 
+// Byte offset of floats 4q .. 4q+3 of accumulator (mi, ni) of thread tid in
+// slot j of a split tile's partial sums: one wave's 16-byte accesses of a
+// given (j, mi, ni, q) are 1 KiB contiguous.
+template <int MI, int NI, int NT>
+__device__ inline uint32_t split_off(int j, int mi, int ni, int q, int tid)
+{
+    return uint32_t((((j * MI + mi) * NI + ni) * 4 + q) * NT + tid) * 16u;
+}
+
+// acc = slot 0 + slot 1 + ... + slot S-1 of a split tile's partial sums,
+// added in that order; one accumulator block at a time, all S slots' loads
+// issued before the first add (one round trip per block, not per slot).
+template <int S, int MI, int NI, int NT>
+__device__ inline void split_sum(f32x16 (&acc)[MI][NI], __amdgpu_buffer_rsrc_t rw, int tid)
+{
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+            f32x4 v[S][4];
+#pragma unroll
+            for (int j = 0; j < S; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) v[j][q] = ld_agent16(rw, split_off<MI, NI, NT>(j, mi, ni, q, tid));
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                f32x4 sum = v[0][q];
+#pragma unroll
+                for (int j = 1; j < S; ++j) sum += v[j][q];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[mi][ni][4 * q + e] = sum[e];
+            }
+        }
+}
+
+// A split tile's partial sums: this work-group's into slot `part`; then the
+// last of the tile's `split` work-groups sets acc = slot 0 + slot 1 + ...,
+// added in that order (its own slot read back like the others), so the
+// result does not depend on which one finishes last. Returns false in the
+// others.
+template <int MI, int NI, int NT>
+__device__ inline bool split_reduce(f32x16 (&acc)[MI][NI], float* ws, int* ticket, int split, int part, int tid,
+                                    int* flag_lds)
+{
+    constexpr int SLOT = MI * NI * 16 * NT;  // floats
+    const __amdgpu_buffer_rsrc_t rw = ws_rsrc(ws, uint32_t(split) * SLOT * 4);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                st_agent16(rw, split_off<MI, NI, NT>(part, mi, ni, q, tid),
+                           f32x4{acc[mi][ni][4 * q], acc[mi][ni][4 * q + 1], acc[mi][ni][4 * q + 2],
+                                 acc[mi][ni][4 * q + 3]});
+    if (!last_of(ticket, split, flag_lds)) return false;
+    switch (split) {
+    case 2: split_sum<2, MI, NI, NT>(acc, rw, tid); break;
+    case 3: split_sum<3, MI, NI, NT>(acc, rw, tid); break;
+    default: split_sum<GEMM_SPLIT_MAX, MI, NI, NT>(acc, rw, tid); break;
+    }
+    return true;
+}
+
 template <int BM, int BN, int WN, int MODE, bool WQ8>
 __global__ void __launch_bounds__(128 * WN)
 gemm_kernel(GemmArgs g)
@@ -298,8 +400,14 @@ gemm_kernel(GemmArgs g)
     constexpr int ncols = (MODE == GEMM_SWIGLU_F16) ? BN / 2 : BN;  // outputs per tile
     const int ntn = (g.N + ncols - 1) / ncols;
     const int ntm = (g.M + BM - 1) / BM;
+    // split > 1 (128-row tiles only): work-group b takes part b % split of
+    // tile b / split
+    constexpr bool SPLITS = BM == 128;
+    const int nsplit = SPLITS ? max(g.split, 1) : 1;
+    const int tile = SPLITS ? int(blockIdx.x) / nsplit : int(blockIdx.x);
+    const int part = SPLITS ? int(blockIdx.x) - tile * nsplit : 0;
     int tn, tm;
-    gemm_tile_of(blockIdx.x, ntm, ntn, tm, tn);
+    gemm_tile_of(tile, ntm, ntn, tm, tn);
     const int m0 = tm * BM;
     const int n0 = tn * ncols;
 
@@ -427,12 +535,16 @@ gemm_kernel(GemmArgs g)
     // s+3, and the other set holds stage s+2 in flight.
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
-    const int nst = (g.K + GBK - 1) / GBK;
+    // This work-group's stages: st0 .. st0 + nst - 1 of the K loop's
+    // (all of them without a split; the caller keeps nst >= 1).
+    const int kst = (g.K + GBK - 1) / GBK;
+    const int st0 = SPLITS ? kst * part / nsplit : 0;
+    const int nst = SPLITS ? kst * (part + 1) / nsplit - st0 : kst;
     // Loads and stores run unconditionally (past the last stage they repeat
     // the last stage into a buffer nobody reads again), so every path keeps
     // the same loads in flight and the waits stay exact.
-    auto kof = [&](int stage) { return min(stage, nst - 1) * GBK; };
-    load_stage(S0{}, 0);
+    auto kof = [&](int stage) { return (SPLITS ? st0 + min(stage, nst - 1) : min(stage, nst - 1)) * GBK; };
+    load_stage(S0{}, kof(0));
     load_stage(S1{}, kof(1));
     store_stage(S0{});
     load_stage(S0{}, kof(2));
@@ -452,6 +564,14 @@ gemm_kernel(GemmArgs g)
     }
     if (st < nst) compute(S0{});  // odd number of stages: the last one
 
+    if constexpr (SPLITS) {
+        if (nsplit > 1) {
+            // the flag goes in the operand buffers, no longer read
+            if (!split_reduce<MI, NI, NT>(acc, g.ws + int64_t(tile) * nsplit * (MI * NI * 16 * NT),
+                                          g.tickets + tile, nsplit, part, tid, reinterpret_cast<int*>(gsm)))
+                return;
+        }
+    }
     gemm_epilogue<MODE, MI, NI, WTM, WTN>(g, acc, m0, n0, wm, wn, l);
 }
 
@@ -635,7 +755,7 @@ hipError_t launch_gemm_q(const GemmArgs& g, hipStream_t s)
         attr_set.store(true, std::memory_order_release);
     }
     constexpr int ncols = (MODE == GEMM_SWIGLU_F16) ? BN / 2 : BN;
-    const int blocks = ((g.N + ncols - 1) / ncols) * ((g.M + BM - 1) / BM);
+    const int blocks = ((g.N + ncols - 1) / ncols) * ((g.M + BM - 1) / BM) * max(g.split, 1);
     DFK_LAUNCH((gemm_kernel<BM, BN, WN, MODE, WQ8>), dim3(blocks), dim3(128 * WN), lds, s, g);
     return hipGetLastError();
 }
@@ -1538,8 +1658,10 @@ static bool gemm_dma_fits(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t 
     return K % GDK == 0 && M * lda * 2 < DMA_RANGE && brows * ldb * 2 < DMA_RANGE;
 }
 
-int gemm_plan(int64_t M, int64_t N, int64_t K, int64_t up_rows, int mode, bool q8)
+// Tile code and K split of an M x N x K problem.
+static int gemm_tile_plan(int64_t M, int64_t N, int64_t K, int64_t up_rows, int mode, bool q8, int* split)
 {
+    *split = 1;
     if (M <= 0 || N <= 0) return 0;
     // Every large tile runs one block per compute unit, so a GEMM takes
     // ceil(tiles / units) rounds of its tile's time. Tile times relative to
@@ -1571,34 +1693,82 @@ int gemm_plan(int64_t M, int64_t N, int64_t K, int64_t up_rows, int mode, bool q
         if (std::min(r1, r3) >= r2 * 0.95) tile = dma ? GEMM_PLAN_256x256_LDS : GEMM_PLAN_256x256;
         else tile = r3 < r1 ? GEMM_PLAN_256x192_LDS : GEMM_PLAN_128x256;
     }
-    return tile | (q8 ? GEMM_PLAN_Q8_IN_GEMM : 0);
+    // A grid of the register-staged 128-row tiles that fills at most half of
+    // the compute units splits each tile's K loop over up to GEMM_SPLIT_MAX
+    // work-groups; their partial sums (64 or 128 KiB per work-group) are
+    // stored and added by the last one, which costs about 25 us whatever
+    // the split (measured), against a tile's 1.0 us (128 x 128) or 1.7 us
+    // (128 x 256) per 64-deep stage: split where that saves over a tenth.
+    // E.g. the 8B shapes at 1024 rows (8-bit blocks): o and down on 128
+    // tiles of 128 x 256 in 2 (o 109 -> 84 us, down 327 -> 201); qwen3-0.6B
+    // at 512 rows: down (K 3072) in 4 (51 -> 39 us), o (K 2048) not (4
+    // measured 32 -> 36 us).
+    if (tile == GEMM_PLAN_128x128 || tile == GEMM_PLAN_128x256) {
+        const int64_t tiles = tile == GEMM_PLAN_128x256 ? t1 : ((M + 127) / 128) * ((N + (cols / 2) - 1) / (cols / 2));
+        const int64_t nst = (K + GBK - 1) / GBK;
+        if (tiles > 0 && tiles * 2 <= cu && tiles <= GEMM_SPLIT_TICKETS) {
+            const double t = double(nst) * (tile == GEMM_PLAN_128x256 ? 1.7 : 1.0);
+            double best = 0.1 * t;
+            for (int sp = 2; sp <= GEMM_SPLIT_MAX && sp <= cu / tiles && nst / sp >= 8; ++sp) {
+                const double save = t * (1.0 - 1.0 / sp) - 25.0;
+                if (save > best) {
+                    best = save;
+                    *split = sp;
+                }
+            }
+        }
+    }
+    return tile;
+}
+
+int gemm_plan(int64_t M, int64_t N, int64_t K, int64_t up_rows, int mode, bool q8)
+{
+    int split;
+    const int tile = gemm_tile_plan(M, N, K, up_rows, mode, q8, &split);
+    if (!tile) return 0;
+    return tile | (q8 ? GEMM_PLAN_Q8_IN_GEMM : 0) | (split << GEMM_PLAN_SPLIT_SHIFT);
+}
+
+size_t gemm_split_ws_bytes(int64_t M, int64_t N, int64_t K, int64_t up_rows, int mode, bool q8)
+{
+    int split;
+    const int tile = gemm_tile_plan(M, N, K, up_rows, mode, q8, &split);
+    if (split <= 1) return 0;
+    const int64_t bn = tile == GEMM_PLAN_128x256 ? 256 : 128;
+    const int64_t ncols = mode == GEMM_SWIGLU_F16 ? bn / 2 : bn;
+    const int64_t tiles = ((M + 127) / 128) * ((N + ncols - 1) / ncols);
+    return size_t(tiles) * size_t(split) * 128 * size_t(bn) * sizeof(float);
 }
 
 hipError_t launch_gemm(const GemmArgs& g, int mode, hipStream_t s)
 {
     if (g.M <= 0 || g.N <= 0) return hipSuccess;
-    const int plan = gemm_plan(g.M, g.N, g.K, g.up_rows, mode, g.Bsc != nullptr) & GEMM_PLAN_TILE_MASK;
+    int split;
+    const int plan = gemm_tile_plan(g.M, g.N, g.K, g.up_rows, mode, g.Bsc != nullptr, &split);
     const int shape = plan == GEMM_PLAN_128x128 ? 0 : plan == GEMM_PLAN_128x256 ? 1 : 2;
+    // the split needs the caller's partial-sum space and tickets
+    GemmArgs ga = g;
+    ga.split = split > 1 && g.ws && g.tickets ? split : 1;
     // the plan assumes contiguous operands; other strides are checked here
     const bool fits = gemm_dma_fits(g.M, g.N, g.K, g.lda, g.ldb, g.up_rows, mode);
     const bool dma = plan == GEMM_PLAN_256x256_LDS && fits;
     if (plan == GEMM_PLAN_256x192_LDS && mode != GEMM_SWIGLU_F16) {
         switch (mode) {
         case GEMM_STORE_F32:
-            return fits ? launch_gemm_dma<256, 192, 4, 2, GEMM_STORE_F32>(g, s)
-                        : launch_gemm_t<128, 256, 4, GEMM_STORE_F32>(g, false, s);
+            return fits ? launch_gemm_dma<256, 192, 4, 2, GEMM_STORE_F32>(ga, s)
+                        : launch_gemm_t<128, 256, 4, GEMM_STORE_F32>(ga, false, s);
         case GEMM_ADD_F32:
-            return fits ? launch_gemm_dma<256, 192, 4, 2, GEMM_ADD_F32>(g, s)
-                        : launch_gemm_t<128, 256, 4, GEMM_ADD_F32>(g, false, s);
+            return fits ? launch_gemm_dma<256, 192, 4, 2, GEMM_ADD_F32>(ga, s)
+                        : launch_gemm_t<128, 256, 4, GEMM_ADD_F32>(ga, false, s);
         case GEMM_STORE_F16:
-            return fits ? launch_gemm_dma<256, 192, 4, 2, GEMM_STORE_F16>(g, s)
-                        : launch_gemm_t<128, 256, 4, GEMM_STORE_F16>(g, false, s);
+            return fits ? launch_gemm_dma<256, 192, 4, 2, GEMM_STORE_F16>(ga, s)
+                        : launch_gemm_t<128, 256, 4, GEMM_STORE_F16>(ga, false, s);
         }
     }
 #define DF_GEMM_BY_SHAPE(MODE_)                                                  \
-    return shape == 2   ? launch_gemm_t<256, 256, 4, MODE_>(g, dma, s)           \
-           : shape == 1 ? launch_gemm_t<128, 256, 4, MODE_>(g, false, s)         \
-                        : launch_gemm_t<GBM_, GBN_, 2, MODE_>(g, false, s);
+    return shape == 2   ? launch_gemm_t<256, 256, 4, MODE_>(ga, dma, s)          \
+           : shape == 1 ? launch_gemm_t<128, 256, 4, MODE_>(ga, false, s)        \
+                        : launch_gemm_t<GBM_, GBN_, 2, MODE_>(ga, false, s);
     switch (mode) {
     case GEMM_STORE_F32: DF_GEMM_BY_SHAPE(GEMM_STORE_F32)
     case GEMM_ADD_F32: DF_GEMM_BY_SHAPE(GEMM_ADD_F32)

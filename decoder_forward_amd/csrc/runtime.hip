@@ -19,7 +19,8 @@ static_assert(dfk::GEMM_PLAN_128x128 == DF_GEMM_T128x128 && dfk::GEMM_PLAN_128x2
                   dfk::GEMM_PLAN_256x192_LDS == DF_GEMM_T256x192_LDS &&
                   dfk::GEMM_PLAN_TILE_MASK == DF_GEMM_TILE_MASK &&
                   dfk::GEMM_PLAN_Q8_IN_GEMM == DF_GEMM_Q8_IN_GEMM &&
-                  dfk::GEMM_PLAN_DEQUANT_FIRST == DF_GEMM_Q8_DEQUANT_FIRST,
+                  dfk::GEMM_PLAN_DEQUANT_FIRST == DF_GEMM_Q8_DEQUANT_FIRST &&
+                  dfk::GEMM_PLAN_SPLIT_SHIFT == DF_GEMM_SPLIT_SHIFT && dfk::GEMM_PLAN_SPLIT_MASK == DF_GEMM_SPLIT_MASK,
               "GEMM plan codes match the header");
 
 #include <atomic>
@@ -205,6 +206,7 @@ struct df_model {
     // f16 copies for the bulk-prefill attention (null where it reads kc / vc):
     // K [L][n_kv][max_ctx][hd], V transposed [L][n_kv][hd][max_ctx]
     uint16_t* k16 = nullptr;
+    int* gemm_tickets = nullptr;  // GEMM_SPLIT_TICKETS counters, zero between GEMMs (split tiles)
     uint16_t* vt16 = nullptr;
     float* cos_t = nullptr;  // [max_ctx][hd/2]
     float* sin_t = nullptr;
@@ -757,6 +759,14 @@ bool build_conversation(df_model* m, Fail* e)
     if (!m->attn_part) return false;
     m->argmax_out = static_cast<int*>(dev_alloc(m, 4, "argmax result", e));
     if (!m->argmax_out) return false;
+    if (bulk_supported(m)) {
+        // per conversation: two conversations' GEMMs may run at once
+        m->gemm_tickets = static_cast<int*>(dev_alloc(m, GEMM_SPLIT_TICKETS * sizeof(int), "GEMM split tickets", e));
+        if (!m->gemm_tickets ||
+            !check(hipMemsetAsync(m->gemm_tickets, 0, GEMM_SPLIT_TICKETS * sizeof(int), m->stream),
+                   "GEMM split tickets init", e))
+            return false;
+    }
     m->gen_tokens = static_cast<int*>(dev_alloc(m, size_t(c.max_ctx) * 4, "generated tokens", e));
     if (!m->gen_tokens) return false;
     if (!check(hipMemsetAsync(m->state, 0, sizeof(DevState), m->stream), "state init", e)) return false;
@@ -983,6 +993,7 @@ struct PfBufs {
     float* tmp;        // gemma3: [S][d] o / down outputs before their rms_norm
     int* toks;         // [S]
     uint16_t* wdq;     // 8-bit weights, S >= PF_DEQUANT_MIN_ROWS: one matrix dequantised to f16
+    float* gws;        // partial sums of split GEMM tiles (null when no GEMM splits)
 };
 
 bool pf_buffers(df_model* m, int S, PfBufs* b, Fail* e)
@@ -1000,6 +1011,23 @@ bool pf_buffers(df_model* m, int S, PfBufs* b, Fail* e)
     b->toks = static_cast<int*>(A(size_t(S) * 4));
     b->tmp = c.arch == DF_ARCH_GEMMA3 ? static_cast<float*>(A(size_t(S) * d * 4)) : nullptr;
     b->wdq = nullptr;
+    b->gws = nullptr;
+    if (c.n_layers > 0) {
+        // the largest partial-sum space of the four GEMMs (as planned for S rows)
+        const bool q8_in_gemm = m->layers[0].wqkv.scales && S < PF_DEQUANT_MIN_ROWS;
+        const bool gemma = c.arch == DF_ARCH_GEMMA3;
+        const int64_t N[4] = {int64_t(qd + 2 * kvd), int64_t(d), int64_t(F), int64_t(d)};
+        const int64_t K[4] = {int64_t(d), int64_t(qd), int64_t(d), int64_t(F)};
+        const int mode[4] = {GEMM_STORE_F32, gemma ? GEMM_STORE_F32 : GEMM_ADD_F32, GEMM_SWIGLU_F16,
+                             gemma ? GEMM_STORE_F32 : GEMM_ADD_F32};
+        size_t ws = 0;
+        for (int i = 0; i < 4; ++i)
+            ws = std::max(ws, gemm_split_ws_bytes(S, N[i], K[i], i == 2 ? int64_t(F) : 0, mode[i], q8_in_gemm));
+        if (ws) {
+            b->gws = static_cast<float*>(A(ws));
+            if (!b->gws) return false;
+        }
+    }
     if (c.n_layers > 0 && m->layers[0].wqkv.scales && S >= PF_DEQUANT_MIN_ROWS) {
         const size_t most = std::max(std::max((qd + 2 * kvd) * d, d * qd), std::max(2 * F * d, d * F));
         b->wdq = static_cast<uint16_t*>(A(most * 2));
@@ -1028,6 +1056,8 @@ hipError_t pf_launch(df_model* m, const PfBufs& b, int kernel, int l, int S, int
     const size_t kv_layer = size_t(c.n_kv_heads) * size_t(c.max_ctx) * size_t(hd);
     GemmArgs g{};
     g.zeros = m->zeros;
+    g.ws = b.gws;
+    g.tickets = m->gemm_tickets;
     g.M = S;
     hipError_t r = hipSuccess;
     // The GEMM's B operand: the weight as stored, or (8-bit blocks with a

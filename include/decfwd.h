@@ -319,9 +319,11 @@ df_status df_time_prefill(df_model* m, int32_t kernel, int32_t rows, int32_t rep
 
 /* Debug query: the matrix-core kernels a bulk prefill of `rows` rows runs
  * for the q/k/v, o, gate/up and down GEMMs (plan[0..3]), each a tile code
- * DF_GEMM_* with the DF_GEMM_Q8_* flags or'ed in; all 0 when the model has
- * no layers or no bulk path (f32 weights). The same host function picks the
- * kernel at launch, so tests can check which kernels a run exercises. */
+ * DF_GEMM_* with the DF_GEMM_Q8_* flags or'ed in, and in bits 8..11
+ * (DF_GEMM_SPLIT_MASK) the number of work-groups each tile's K loop is split
+ * over (1: none); all 0 when the model has no layers or no bulk path (f32
+ * weights). The same host function picks the kernel at launch, so tests can
+ * check which kernels a run exercises. */
 #define DF_GEMM_T128x128 1        /* 4 waves, operands staged through registers */
 #define DF_GEMM_T128x256 2        /* 8 waves, staged through registers */
 #define DF_GEMM_T256x256 3        /* 8 waves, staged through registers */
@@ -330,6 +332,8 @@ df_status df_time_prefill(df_model* m, int32_t kernel, int32_t rows, int32_t rep
 #define DF_GEMM_TILE_MASK 15
 #define DF_GEMM_Q8_IN_GEMM 16     /* 8-bit weight tiles dequantised on their way into LDS */
 #define DF_GEMM_Q8_DEQUANT_FIRST 32 /* 8-bit matrices converted to f16 before the GEMM */
+#define DF_GEMM_SPLIT_SHIFT 8
+#define DF_GEMM_SPLIT_MASK 0xF00
 df_status df_prefill_plan(const df_model* m, int32_t rows, int32_t* plan);
 
 #ifdef __cplusplus
