@@ -1235,8 +1235,12 @@ attn_prefill_kernel(AttnPrefillArgs a)
 // current tile. Inside S^T = K Q^T the 16 K rows of key block kb are
 // permuted (pf_key) so that each lane's 8 P values of a 32-key half are 8
 // consecutive keys: the V operand of P V is then one 16-byte read per lane.
-// Everything else (work split, lazy maximum, masks, output) is as in
-// attn_prefill_kernel.
+// Each wave takes one 16-row query tile, so a block has 16 x (waves per
+// head) query rows: twice the blocks of two tiles per wave, which evens out
+// the causal imbalance where those would fill the compute units only once
+// (2048 rows of 8 KV heads: 512 blocks instead of 256, the latest query
+// blocks dispatched first), and four waves per SIMD fit in registers.
+// Everything else (lazy maximum, masks, output) is as in attn_prefill_kernel.
 // ---------------------------------------------------------------------------
 constexpr int PFD_TK = 64;  // keys per tile
 
@@ -1268,7 +1272,7 @@ __device__ inline __amdgpu_buffer_rsrc_t dma_rsrc_n(const uint16_t* base, uint32
 }
 
 template <int HD, int G>
-__global__ void __launch_bounds__(attn_pf_threads<G>())
+__global__ void __launch_bounds__(attn_pf_threads<G>()) __attribute__((amdgpu_waves_per_eu(4)))
 attn_prefill_dma_kernel(AttnPrefillArgs a)
 {
     static_assert(HD == 64 || HD == 128, "head_dim of the f16-copy attention");
@@ -1276,8 +1280,8 @@ attn_prefill_dma_kernel(AttnPrefillArgs a)
     constexpr int KB = TK / 16;             // 16-key blocks of a tile
     constexpr int NP = TK / 32;             // 32-key halves: P V steps
     constexpr int DB = HD / 16;             // 16-wide output blocks
-    constexpr int QB = attn_pf_rows<HD, G>();  // query rows per block
-    constexpr int RT = attn_pf_rt<HD>();    // 16-row tiles per wave
+    constexpr int RT = 1;                   // 16-row tiles per wave
+    constexpr int QB = 16 * attn_pf_wph<G>();  // query rows per block
     constexpr int WPH = attn_pf_wph<G>();   // waves per head
     constexpr int NW = G * WPH;             // waves
     constexpr int CPR = HD / 8;             // 16-byte chunks of a K row
@@ -1404,29 +1408,31 @@ attn_prefill_dma_kernel(AttnPrefillArgs a)
         // kq outermost: the KB * RT accumulators in flight are independent,
         // so no MFMA waits for the previous one's result.
         f32x4 st[RT][KB];
-        half8 kf[KB][HD / 32];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            const int row = pf_key(kb, lq);
-#pragma unroll
-            for (int kq = 0; kq < HD / 32; ++kq)
-                kf[kb][kq] = *reinterpret_cast<const half8*>(Kl + row * HD + (((kq * 4 + lg) ^ pf_swz_k<HD>(row)) * 8));
-        }
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) st[rt][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // The matrix sections run at raised wave priority: of the two waves
-        // of a SIMD, the one that reaches its MFMAs first keeps the matrix
-        // unit, and the other's softmax overlaps them.
+        // Each K fragment feeds one MFMA (one row tile per wave), so they
+        // are read one depth step at a time: 16 registers rather than the
+        // tile's 64, which keeps four waves per SIMD in registers. The
+        // matrix sections run at raised wave priority: of the waves of a
+        // SIMD, the one that reaches its MFMAs first keeps the matrix unit,
+        // and the others' softmax overlaps them.
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int kq = 0; kq < HD / 32; ++kq)
+        for (int kq = 0; kq < HD / 32; ++kq) {
+            half8 kf[KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const int row = pf_key(kb, lq);
+                kf[kb] = *reinterpret_cast<const half8*>(Kl + row * HD + (((kq * 4 + lg) ^ pf_swz_k<HD>(row)) * 8));
+            }
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
-                    st[rt][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[kb][kq], qa[rt][kq], st[rt][kb], 0, 0, 0);
+                    st[rt][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[kb], qa[rt][kq], st[rt][kb], 0, 0, 0);
+        }
         __builtin_amdgcn_s_setprio(0);
         const bool masked = t0 > free_hi || t0 < free_lo;  // uniform
         bool grow = false;
@@ -1568,6 +1574,7 @@ template <int HD, int G>
 hipError_t launch_attn_prefill_dma(const AttnPrefillArgs& a, hipStream_t s)
 {
     constexpr size_t lds = size_t(2) * 2 * PFD_TK * HD * 2;
+    constexpr int QB = 16 * attn_pf_wph<G>();
     static std::atomic<bool> attr_set{false};  // sessions may launch from several threads
     if (!attr_set.load(std::memory_order_acquire)) {
         const hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_prefill_dma_kernel<HD, G>),
@@ -1575,7 +1582,8 @@ hipError_t launch_attn_prefill_dma(const AttnPrefillArgs& a, hipStream_t s)
         if (r != hipSuccess) return r;
         attr_set.store(true, std::memory_order_release);
     }
-    DFK_LAUNCH((attn_prefill_dma_kernel<HD, G>), (pf_grid<HD, G>(a)), dim3(attn_pf_threads<G>()), lds, s, a);
+    DFK_LAUNCH((attn_prefill_dma_kernel<HD, G>), dim3((a.S + QB - 1) / QB, a.n_kv), dim3(attn_pf_threads<G>()), lds,
+               s, a);
     return hipGetLastError();
 }
 
