@@ -69,6 +69,12 @@ hipError_t launch_mv_w(const Weight& W, int mode, const float* x,
     case MV_SWIGLU:
         return norm ? launch_mv_t<WT, MV_SWIGLU, true>(W, x, nw, eps, n_out, up_rows, out, s, act)
                     : launch_mv_t<WT, MV_SWIGLU, false>(W, x, nw, eps, n_out, up_rows, out, s, act);
+    case MV_STORE2:
+        return norm ? launch_mv_t<WT, MV_STORE2, true>(W, x, nw, eps, n_out, up_rows, out, s, act)
+                    : launch_mv_t<WT, MV_STORE2, false>(W, x, nw, eps, n_out, up_rows, out, s, act);
+    case MV_RESID2:
+        return norm ? launch_mv_t<WT, MV_RESID2, true>(W, x, nw, eps, n_out, up_rows, out, s, act)
+                    : launch_mv_t<WT, MV_RESID2, false>(W, x, nw, eps, n_out, up_rows, out, s, act);
     }
     return hipErrorInvalidValue;
 }
@@ -421,7 +427,7 @@ MvLayout make_mv_layout(int wdtype, int64_t K, int64_t n_out, int64_t up_rows, i
 
 size_t mv_lds_bytes(const MvLayout& L, int mode)
 {
-    const int NR = mode == MV_SWIGLU ? 2 : 1;
+    const int NR = (mode == MV_SWIGLU || mode == MV_STORE2 || mode == MV_RESID2) ? 2 : 1;
     const int S = 1 << L.log_s;
     return size_t(dev::mv_staged_floats(L.wdtype, L.K)) * sizeof(float) +
            size_t(L.upb) * S * NR * sizeof(float);
@@ -432,6 +438,13 @@ hipError_t launch_matvec(const Weight& W, int mode, const float* x,
                          int64_t up_rows, float* out, hipStream_t s, int act)
 {
     if (n_out <= 0) return hipSuccess;
+    // An even number of rows runs as pairs (n, n + n_out / 2): one LDS read
+    // of the activation per two weights.
+    if ((mode == MV_STORE || mode == MV_RESID) && n_out % 2 == 0) {
+        mode = mode == MV_STORE ? MV_STORE2 : MV_RESID2;
+        up_rows = n_out / 2;
+        n_out /= 2;
+    }
     switch (W.dtype) {
     case W_F32: return launch_mv_w<W_F32>(W, mode, x, norm_w, eps, n_out, up_rows, out, s, act);
     case W_F16: return launch_mv_w<W_F16>(W, mode, x, norm_w, eps, n_out, up_rows, out, s, act);

@@ -303,7 +303,7 @@ __device__ inline void fetch(const void* W, const uint16_t* scales, const MvLayo
 
 template <int WT, int MODE>
 struct MvState {
-    static constexpr int NR = (MODE == MV_SWIGLU) ? 2 : 1;
+    static constexpr int NR = (MODE == MV_SWIGLU || MODE == MV_STORE2 || MODE == MV_RESID2) ? 2 : 1;
     static constexpr int U = (WT == W_F32) ? 8 : (NR == 1 ? 8 : 4);
     ChunkBatch<WT, NR, U> cur;
     Cursor fc, uc;
@@ -345,8 +345,9 @@ __device__ inline void mv_begin(const void* W, const uint16_t* scales, const MvL
 
 // Part 2: stage x (times the norm weight, if NORM) in LDS (hs: the staged
 // activation, then the slice sums), then consume the batches and write the
-// epilogue selected by MODE (MV_SWIGLU: gate and up rows together; the
-// others one row).
+// epilogue selected by MODE (MV_SWIGLU: gate and up rows together;
+// MV_STORE2 / MV_RESID2: rows n and n + up_rows together; the others one
+// row).
 template <int WT, int MODE, bool NORM>
 __device__ inline void mv_finish(const uint16_t* scales, const void* W, const MvLayout L,
                                  MvState<WT, MODE>& st, const float* __restrict__ x,
@@ -366,9 +367,12 @@ __device__ inline void mv_finish(const uint16_t* scales, const void* W, const Mv
     // The residual value of this thread's first output unit, loaded now so
     // that its latency passes while the activation is staged and the weights
     // stream.
-    float resid0 = 0.f;
-    if constexpr (MODE == MV_RESID) {
-        if (tid < L.upb && st.unit0 + tid < L.n_out) resid0 = *gmem(out + st.unit0 + tid);
+    float resid0 = 0.f, resid1 = 0.f;
+    if constexpr (MODE == MV_RESID || MODE == MV_RESID2) {
+        if (tid < L.upb && st.unit0 + tid < L.n_out) {
+            resid0 = *gmem(out + st.unit0 + tid);
+            if constexpr (MODE == MV_RESID2) resid1 = *gmem(out + st.unit0 + tid + L.up_rows);
+        }
     }
 
     float ss = 0.f;
@@ -404,6 +408,15 @@ __device__ inline void mv_finish(const uint16_t* scales, const void* W, const Mv
         } else if constexpr (MODE == MV_RESID) {
             const float old = unit == st.unit0 + tid ? resid0 : *gmem(out + unit);
             *gmem(out + unit) = old + acc[0] * r;
+        } else if constexpr (MODE == MV_RESID2) {
+            const bool own = unit == st.unit0 + tid;
+            const float old0 = own ? resid0 : *gmem(out + unit);
+            const float old1 = own ? resid1 : *gmem(out + unit + L.up_rows);
+            *gmem(out + unit) = old0 + acc[0] * r;
+            *gmem(out + unit + L.up_rows) = old1 + acc[1] * r;
+        } else if constexpr (MODE == MV_STORE2) {
+            *gmem(out + unit) = acc[0] * r;
+            *gmem(out + unit + L.up_rows) = acc[1] * r;
         } else {
             *gmem(out + unit) = acc[0] * r;
         }

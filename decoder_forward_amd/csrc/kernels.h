@@ -50,7 +50,11 @@ struct Weight {
 //   MV_SWIGLU: out[f]  = act(r (W (x . w))[f]) * r (W (x . w))[f + up_rows]
 // where (x . w) is x times the norm weight and r = 1/sqrt(mean(x^2) + eps)
 // when a norm weight is given, else x and r = 1; act is silu or gelu_tanh.
-enum MatvecMode { MV_STORE = 0, MV_RESID = 1, MV_SWIGLU = 2 };
+// MV_STORE2 / MV_RESID2 are MV_STORE / MV_RESID with two rows per unit, n
+// and n + up_rows (= half the rows), so that each activation value a lane
+// reads from LDS serves two weights of the same column, as in MV_SWIGLU;
+// launch_matvec picks them for an even number of rows.
+enum MatvecMode { MV_STORE = 0, MV_RESID = 1, MV_SWIGLU = 2, MV_STORE2 = 3, MV_RESID2 = 4 };
 // Gate activation of the gated FFN.
 enum GateAct { ACT_SILU = 0, ACT_GELU_TANH = 1 };
 // Gate activation of the gated FFN (GateAct): silu(g) = g / (1 + e^-g), or
