@@ -63,9 +63,6 @@ hipError_t launch_mv_w(const Weight& W, int mode, const float* x,
     case MV_STORE:
         return norm ? launch_mv_t<WT, MV_STORE, true>(W, x, nw, eps, n_out, up_rows, out, s, act)
                     : launch_mv_t<WT, MV_STORE, false>(W, x, nw, eps, n_out, up_rows, out, s, act);
-    case MV_RESID:
-        return norm ? launch_mv_t<WT, MV_RESID, true>(W, x, nw, eps, n_out, up_rows, out, s, act)
-                    : launch_mv_t<WT, MV_RESID, false>(W, x, nw, eps, n_out, up_rows, out, s, act);
     case MV_SWIGLU:
         return norm ? launch_mv_t<WT, MV_SWIGLU, true>(W, x, nw, eps, n_out, up_rows, out, s, act)
                     : launch_mv_t<WT, MV_SWIGLU, false>(W, x, nw, eps, n_out, up_rows, out, s, act);
@@ -439,7 +436,10 @@ hipError_t launch_matvec(const Weight& W, int mode, const float* x,
 {
     if (n_out <= 0) return hipSuccess;
     // An even number of rows runs as pairs (n, n + n_out / 2): one LDS read
-    // of the activation per two weights.
+    // of the activation per two weights. Residual outputs (d_model rows, a
+    // multiple of 32) are always even; an odd MV_STORE (a vocabulary) runs
+    // one row per unit.
+    if (mode == MV_RESID && n_out % 2 != 0) return hipErrorInvalidValue;
     if ((mode == MV_STORE || mode == MV_RESID) && n_out % 2 == 0) {
         mode = mode == MV_STORE ? MV_STORE2 : MV_RESID2;
         up_rows = n_out / 2;

@@ -368,10 +368,10 @@ __device__ inline void mv_finish(const uint16_t* scales, const void* W, const Mv
     // that its latency passes while the activation is staged and the weights
     // stream.
     float resid0 = 0.f, resid1 = 0.f;
-    if constexpr (MODE == MV_RESID || MODE == MV_RESID2) {
+    if constexpr (MODE == MV_RESID2) {
         if (tid < L.upb && st.unit0 + tid < L.n_out) {
             resid0 = *gmem(out + st.unit0 + tid);
-            if constexpr (MODE == MV_RESID2) resid1 = *gmem(out + st.unit0 + tid + L.up_rows);
+            resid1 = *gmem(out + st.unit0 + tid + L.up_rows);
         }
     }
 
@@ -405,9 +405,6 @@ __device__ inline void mv_finish(const uint16_t* scales, const void* W, const Mv
             const float g = acc[0] * r;
             const float u = acc[1] * r;
             *gmem(out + unit) = gate_act(g, L.act) * u;
-        } else if constexpr (MODE == MV_RESID) {
-            const float old = unit == st.unit0 + tid ? resid0 : *gmem(out + unit);
-            *gmem(out + unit) = old + acc[0] * r;
         } else if constexpr (MODE == MV_RESID2) {
             const bool own = unit == st.unit0 + tid;
             const float old0 = own ? resid0 : *gmem(out + unit);

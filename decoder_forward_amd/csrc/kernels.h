@@ -53,7 +53,8 @@ struct Weight {
 // MV_STORE2 / MV_RESID2 are MV_STORE / MV_RESID with two rows per unit, n
 // and n + up_rows (= half the rows), so that each activation value a lane
 // reads from LDS serves two weights of the same column, as in MV_SWIGLU;
-// launch_matvec picks them for an even number of rows.
+// launch_matvec picks them for an even number of rows (MV_RESID always runs
+// as MV_RESID2: its outputs, d_model rows, are a multiple of 32).
 enum MatvecMode { MV_STORE = 0, MV_RESID = 1, MV_SWIGLU = 2, MV_STORE2 = 3, MV_RESID2 = 4 };
 // Gate activation of the gated FFN.
 enum GateAct { ACT_SILU = 0, ACT_GELU_TANH = 1 };

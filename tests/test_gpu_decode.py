@@ -47,7 +47,10 @@ def gpu_teacher_forced(dfa, cfg, W, fed, max_ctx=None):
     ("qwen2", "f32", {}), ("qwen2", "f16", dict(rope_pairing="adjacent")),
     ("qwen2", "q8", dict(n_heads=6, n_kv_heads=2)),
     ("llama", "f32", dict(rope_pairing="adjacent", n_heads=14, n_kv_heads=2)),
-    ("qwen3", "f16", dict(rope_pairing="adjacent", n_heads=10, n_kv_heads=2))],
+    ("qwen3", "f16", dict(rope_pairing="adjacent", n_heads=10, n_kv_heads=2)),
+    # odd vocabularies: the logits matvec runs one row per unit instead of
+    # row pairs
+    ("llama", "f16", dict(vocab=257)), ("qwen3", "q8", dict(vocab=251))],
     ids=lambda v: "-".join(f"{k}{x}" for k, x in v.items()) if isinstance(v, dict) else str(v))
 def test_tiny_token_by_token_and_decode(dfa, arch, wdtype, over):
     say(f"[tiny {arch} {wdtype} {over}] 32-token prompt + 16 greedy steps")
