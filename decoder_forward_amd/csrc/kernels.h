@@ -237,8 +237,9 @@ hipError_t launch_dequant_q8(const void* values, const uint16_t* scales, int64_t
                              uint16_t* out, hipStream_t s);
 // Bulk prefill of at least this many rows dequantises each layer's 8-bit
 // matrices to f16 first and runs the f16 GEMMs: the conversion costs less
-// than the 8-bit GEMM's slower register-staged loads from about here on.
-constexpr int PF_DEQUANT_MIN_ROWS = 2048;
+// than the 8-bit GEMM's slower register-staged loads from about here on
+// (measured faster at 1024 rows, slower at 512).
+constexpr int PF_DEQUANT_MIN_ROWS = 1024;
 
 struct QkPostArgs {
     const float* qkv;     // [S][qd | kvd | kvd] f32

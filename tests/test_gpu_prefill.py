@@ -138,7 +138,7 @@ def test_tiny_q8_bulk_then_decode(dfa, arch):
 
 @pytest.mark.parametrize("arch", ["llama", "qwen2", "gemma3"])
 def test_tiny_q8_long_bulk_dequantised_first(dfa, arch):
-    """From 2048 rows on, each layer's 8-bit matrices are dequantised to f16
+    """From 1024 rows on, each layer's 8-bit matrices are dequantised to f16
     before the f16 GEMMs; the result must match the oracle as the in-GEMM
     dequantisation does."""
     S = 2100
@@ -166,7 +166,7 @@ def test_q8_dequantised_first_at_the_widest_ffn(dfa):
     """ffn 32768 (the widest the library takes): the gate/up matrix has 65536
     rows, more than one launch grid dimension holds, at exactly the row count
     from which the weights are dequantised before the GEMMs."""
-    S = 2048
+    S = 1024
     say(f"[tiny llama q8, ffn 32768] bulk {S} vs the oracle")
     cfg = synth.config("tiny", arch="llama", wdtype="q8", ffn_dim=32768, max_ctx=S + 4)
     W = synth.make_weights(cfg)
