@@ -164,7 +164,10 @@ dequant_q8_kernel(const int8_t* __restrict__ q, const uint16_t* __restrict__ sc,
 // in a grid of (BM/2) x (BN/WN) wave tiles. A wave reads BM/64 A and BN/(32 WN)
 // B fragments from LDS per 16-deep step and issues one MFMA per pair, so
 // larger wave tiles need less LDS bandwidth per flop; 8 waves (two per SIMD)
-// let one wave's LDS traffic and waits overlap the other's MFMAs.
+// let one wave's LDS traffic and waits overlap the other's MFMAs. A grid of
+// 128-row tiles that fills at most half of the compute units may split each
+// tile's K loop over 2-4 work-groups (split_reduce: the last adds the
+// partial sums in a fixed order).
 //
 // Lane layout of v_mfma_f32_32x32x16_f16 (checked on the device): lane l
 // supplies A[l%32][(l/32)*8 + i] and B[(l/32)*8 + i][l%32] for i < 8 and
@@ -578,8 +581,9 @@ gemm_kernel(GemmArgs g)
 
 // ---------------------------------------------------------------------------
 // The same GEMM for f16 weights with the operand tiles loaded straight into
-// LDS (global_load_lds_dwordx4: lane i of a wave writes 16 bytes at LDS base
-// + 16 i), no register staging. A stage holds A rows [BM][64] and B rows
+// LDS (buffer_load_dwordx4 ... lds: lane i of a wave writes 16 bytes at LDS
+// base + 16 i; a per-lane byte offset fixed for the whole K loop plus a
+// scalar per-stage offset), no register staging. A stage holds A rows [BM][64] and B rows
 // [BN][64] unpadded, each row's 16-byte K chunks permuted (gemm_swz), so a
 // load instruction fills 8 whole rows and the fragment reads (32 rows of one
 // chunk column per half-wave) fall in distinct banks.
