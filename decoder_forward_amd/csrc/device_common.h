@@ -239,8 +239,9 @@ __device__ inline float lane_dot(uint4 w, const float* hl, uint16_t scale_bits)
 // Decode matvec: out = epilogue(r * W (x . w)).
 //
 // Work layout (MvLayout, computed on the host by make_mv_layout). A block
-// owns `upb` consecutive output units (a row, or a gate row with its up row)
-// and splits each unit's K range into S equal slices of whole 64-lane chunks
+// owns `upb` consecutive output units (a row; a gate row with its up row; or
+// rows n and n + up_rows of an even row count, whose weights of one column
+// share the lane's activation value) and splits each unit's K range into S equal slices of whole 64-lane chunks
 // so that its 8 waves get equal numbers of (unit, slice) items: no straggler
 // waves. Each wave walks its items as one stream of chunks, U chunks per
 // batch, and issues the loads of batch i+1 before it consumes batch i. The
