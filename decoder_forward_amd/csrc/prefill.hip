@@ -1761,8 +1761,10 @@ hipError_t launch_gemm(const GemmArgs& g, int mode, hipStream_t s)
     // the split needs the caller's partial-sum space and tickets
     GemmArgs ga = g;
     ga.split = split > 1 && g.ws && g.tickets ? split : 1;
-    // the plan assumes contiguous operands; other strides are checked here
-    const bool fits = gemm_dma_fits(g.M, g.N, g.K, g.lda, g.ldb, g.up_rows, mode);
+    // the plan assumes contiguous f16 operands; other strides, and 8-bit
+    // weights (g.Bsc: an int8 plane half the size an f16 load would read),
+    // never take the direct-to-LDS kernels
+    const bool fits = g.Bsc == nullptr && gemm_dma_fits(g.M, g.N, g.K, g.lda, g.ldb, g.up_rows, mode);
     const bool dma = plan == GEMM_PLAN_256x256_LDS && fits;
     if (plan == GEMM_PLAN_256x192_LDS && mode != GEMM_SWIGLU_F16) {
         switch (mode) {
