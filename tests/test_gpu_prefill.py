@@ -64,7 +64,9 @@ def check_kv(m, om, cfg, n, tol=TOL):
 @pytest.mark.parametrize("arch,over", [
     ("qwen3", {}), ("llama", {}), ("qwen2", {}),
     ("qwen2", dict(rope_pairing="adjacent", n_heads=6, n_kv_heads=2)),
-    ("qwen3", dict(rope_pairing="adjacent", n_heads=14, n_kv_heads=2))],
+    ("qwen3", dict(rope_pairing="adjacent", n_heads=14, n_kv_heads=2)),
+    # an odd vocabulary: the last row's logits matvec runs one row per unit
+    ("llama", dict(vocab=257))],
     ids=lambda v: "-".join(f"{k}{x}" for k, x in v.items()) if isinstance(v, dict) else str(v))
 def test_tiny_f16_bulk_then_bulk_then_decode(dfa, arch, over):
     say(f"[tiny {arch} f16 {over}] bulk 40 + bulk 7 (on top) + 6 decode steps")
