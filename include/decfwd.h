@@ -1,7 +1,7 @@
 /*
  * decfwd.h — C ABI of the MI355X decoder forward pass (gfx950, HIP).
  *
- * One loaded decoder (llama or qwen3 step list) on one GPU: load(config,
+ * One loaded decoder (llama, qwen3, qwen2 or gemma3 step list) on one GPU: load(config,
  * weights) -> model; forward(model, tokens) -> logits of the last position;
  * reset_kv_cache; free. Plain pointers and sizes only; no C++ or PyTorch
  * types cross this boundary, and no call aborts, exits or throws.
@@ -84,12 +84,12 @@ typedef int32_t df_status;
  * pairing): DF_ROPE_HALVES rotates (t[i], t[i + head_dim/2]),
  * DF_ROPE_ADJACENT rotates (t[2i], t[2i+1]); pair i turns by
  * p * theta^(-2i/head_dim) either way. */
+#define DF_ROPE_HALVES 0
+#define DF_ROPE_ADJACENT 1
+
 /* Widest matmul input: a decode matvec keeps its whole f32 input vector in
  * LDS (128 KiB at this width, of the 160 KiB a gfx950 work-group may use). */
 #define DF_MAX_WIDTH 32768
-
-#define DF_ROPE_HALVES 0
-#define DF_ROPE_ADJACENT 1
 
 /* Weight dtypes. DF_Q8_32: blocks of 32 consecutive int8 values along a row
  * with one f16 scale each; the host layout of one block is the scale
@@ -201,8 +201,9 @@ df_status df_forward(df_model* m, const int32_t* tokens, int32_t n,
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same
  * result as n df_forward calls of one token each, with no allocation in the
  * call. The n tokens run through the decode kernels one position at a time
- * (never the bulk matrix-core path, whose buffers grow with n). The activations that pass between the step's kernels
- * live in one fixed device array of DF_NOALLOC_SCRATCH_BYTES bytes per GPU,
+ * (never the bulk matrix-core path, whose buffers grow with n). The
+ * activations that pass between the step's kernels live in one fixed device
+ * array of DF_NOALLOC_SCRATCH_BYTES bytes per GPU,
  * held by the library until the process ends and shared by every call on
  * that GPU: calls that overlap on one GPU (two models, or two sessions, on
  * different streams) race on it and must be ordered by the caller. Nothing
